@@ -1,0 +1,6 @@
+"""CPU oracle for Sliding Tile Attention -- test infrastructure only.
+
+Imported by the tests, the smoke check and the benchmark's CPU-baseline leg;
+the library under ``sparse_attention_video_tile_amd`` never imports it.
+"""
+from .sta_oracle import *  # noqa: F401,F403
