@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the Sliding Tile Attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole path over one batch of synthetic input
+already resident in HBM: sta_reorder_tiles on q, k and v, sta_forward (which
+derives each query tile's key tiles inline) and sta_restore_order on the
+output. The headline value is effective TFLOP/s over the step, counting only
+computed blocks: 4 * tau^2 * head_dim FLOPs per (query tile, key tile) pair.
+
+Printed as one JSON line. Besides the contract fields it carries
+  roofline      the attention kernel (dominant) against the bf16 MFMA peak,
+                timed with HIP events on the stream it runs on;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the workload;
+  dense         the dense comparator at the same shape and the speed-up;
+  reorder       the permutation kernels' achieved HBM bandwidth.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+F32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector, published
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "STA fwd effective TFLOP/s + MFMA util, 30x48x80 latent, w=(18,24,24), 1 GPU"
+
+
+def algorithmic_flops(w, windows) -> float:
+    """4 * tau^2 * d per computed (query tile, key tile) pair, times B."""
+    from sparse_attention_video_tile_amd import binding
+    pairs = binding.sta_kv_pair_count(w.heads, w.volume, w.tile, windows)
+    tau = w.tile[0] * w.tile[1] * w.tile[2]
+    return float(w.B) * pairs * 4.0 * tau * tau * w.head_dim
+
+
+def gpu_inputs(w, torch):
+    """Seeded N(0,1) tensors of the workload's shape drawn on the device."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed)
+    shape = (w.B, w.heads) + tuple(w.volume) + (w.head_dim,)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return [torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(dt) for _ in range(3)]
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the oracle on query tiles of one head until the budget is spent."""
+    import oracle
+    from sparse_attention_video_tile_amd import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = 1
+    one = w.with_(heads=1, windows=None if w.windows is None else w.windows[:1])
+    inp = workloads.make_inputs(one)
+    window = tuple(int(x) for x in inp.windows[0])
+    scale = 1.0 / math.sqrt(w.head_dim)
+    n = oracle.tile_grid(w.volume, w.tile)
+    n_tiles = n[0] * n[1] * n[2]
+    om = oracle.window_in_tiles(window, w.tile, w.volume)
+    tau = w.tile[0] * w.tile[1] * w.tile[2]
+    flops_per_tile = om[0] * om[1] * om[2] * 4.0 * tau * tau * w.head_dim
+    done, t0 = 0, time.perf_counter()
+    while done < n_tiles:
+        rows = oracle.tile_tokens(w.volume, w.tile, done)
+        oracle.sta_attention_rows(inp.q, inp.k, inp.v, w.tile, window, scale, 0, 0, rows)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s and done >= 2:
+            break
+    el = time.perf_counter() - t0
+    return {
+        "value": done * flops_per_tile / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done} query tiles of head 0 ({done * tau} query rows, window {window}) "
+                  f"of a 1-head draw of {w.name}, {el:.1f} s",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sta_30x48x80_w18x24x24")
+    ap.add_argument("--dense-reps", type=int, default=2, help="dense comparator launches to time (0: skip)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the STA path is built and timed on a single "
+              "MI355X; run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    from sparse_attention_video_tile_amd import binding, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    binding.load_library()
+    w = workloads.by_name(args.workload)
+    windows = workloads.head_windows(w)
+    flops = algorithmic_flops(w, windows)
+    S = w.seq_len
+    q, k, v = gpu_inputs(w, torch)
+    qt, kt, vt = (torch.empty((w.B, w.heads, S, w.head_dim), dtype=q.dtype, device="cuda") for _ in range(3))
+    ot = torch.empty_like(qt)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(timers=None):
+        if timers is not None:
+            timers[0].record(stream)
+        for src, dst in ((q, qt), (k, kt), (v, vt)):
+            binding.sta_reorder_tiles(src, w.tile, out=dst)
+        if timers is not None:
+            timers[1].record(stream)
+        binding.sta_forward(qt, kt, vt, w.volume, w.tile, windows, out=ot)
+        if timers is not None:
+            timers[2].record(stream)
+        binding.sta_restore_order(ot, w.volume, w.tile, out=out)
+        if timers is not None:
+            timers[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    timers = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    start, stop = ev(), ev()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(timers[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    attn_ms = float(np.mean([t[1].elapsed_time(t[2]) for t in timers]))
+    reorder_ms = float(np.mean([t[0].elapsed_time(t[1]) for t in timers]))
+    restore_ms = float(np.mean([t[2].elapsed_time(t[3]) for t in timers]))
+    elem = 2 if w.dtype == "bf16" else 4
+    tensor_bytes = w.B * w.heads * S * w.head_dim * elem
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+
+    dense = None
+    if args.dense_reps > 0:
+        qd, kd, vd = (x.view(w.B, w.heads, S, w.head_dim) for x in (q, k, v))
+        od = torch.empty_like(qd)
+        binding.sta_full_attention(qd, kd, vd, out=od)  # warm-up
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(args.dense_reps):
+            binding.sta_full_attention(qd, kd, vd, out=od)
+        b.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = a.elapsed_time(b) / args.dense_reps
+        dense_flops = float(w.B) * w.heads * 4.0 * S * S * w.head_dim
+        dense = {"ms": dense_ms, "tflops": dense_flops / (dense_ms * 1e-3) / 1e12,
+                 "speedup_sta_vs_dense": dense_ms / attn_ms}
+        del qd, kd, vd, od
+
+    cpu = cpu_baseline(w, args.cpu_budget) if args.cpu_budget > 0 else None
+
+    result = {
+        "metric": METRIC,
+        "value": flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "B": w.B, "heads": w.heads, "head_dim": w.head_dim,
+            "volume": list(w.volume), "tile": list(w.tile),
+            "windows": sorted({tuple(x) for x in windows.tolist()}),
+            "algorithmic_tflop_per_step": flops / 1e12,
+            "inputs": "seeded N(0,1) q, k, v drawn on the device, rounded to bf16",
+        },
+        "roofline": {
+            "kernel": "attn_bf16_kernel" if w.dtype == "bf16" else "attn_f32_kernel",
+            "bound": "mfma",
+            "achieved": attn_tflops,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": attn_tflops / peak,
+            "traffic": None,
+            "launch_ms": attn_ms,
+        },
+        "cpu_baseline": cpu,
+        "dense": dense,
+        "reorder": {
+            "qkv_ms": reorder_ms,
+            "qkv_gbs": 3 * 2 * tensor_bytes / (reorder_ms * 1e-3) / 1e9,
+            "restore_ms": restore_ms,
+            "restore_gbs": 2 * tensor_bytes / (restore_ms * 1e-3) / 1e9,
+            "peak_gbs": HBM_PEAK_GBS,
+        },
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

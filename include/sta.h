@@ -1,0 +1,148 @@
+/*
+ * libsta -- Sliding Tile Attention (STA) forward for AMD MI355X (gfx950).
+ *
+ * STA ("Fast Video Generation with Sliding Tile Attention") replaces full 3D
+ * attention over a (T, H, W) latent video. The token grid is cut into tiles of
+ * (c_t, c_h, c_w) tokens; the attention window slides tile by tile, so every
+ * query of one tile attends to exactly the keys of the tiles inside that
+ * tile's 3D window (podcast transcript on hotaipapers.com, the answers on what
+ * a tile is and on dense / empty / mixed blocks; dianyo ICML2025 blog, STA
+ * "Observation & Proposed Method"). Every (query tile, key tile) block is then
+ * either computed densely or skipped; no block is partly masked.
+ *
+ * Window rule (the pages do not spell it out; this is the reading the library
+ * implements): per head a window of w = (w_t, w_h, w_w) tokens, a whole number
+ * of tiles per axis, omega_a = w_a / c_a. For a query tile with tile
+ * coordinate q_a on an axis of n_a tiles,
+ *     start_a = min(max(q_a - omega_a / 2, 0), n_a - omega_a)      (integer /)
+ * and the window covers key tiles start_a .. start_a + omega_a - 1. The window
+ * keeps its full size at the volume's border (its centre is clamped inside the
+ * volume), so each query tile sees exactly omega_t * omega_h * omega_w tiles.
+ *
+ * Token orders.
+ *   raster:     s  = (t * H + y) * W + x
+ *   tile-major: s' = tile * tau + local, tau = c_t * c_h * c_w,
+ *               tile  = (floor(t/c_t) * n_h + floor(y/c_h)) * n_w + floor(x/c_w),
+ *               local = ((t % c_t) * c_h + (y % c_h)) * c_w + (x % c_w)
+ *   with n_a = extent_a / c_a. Tensors are [B][heads][S][head_dim], contiguous,
+ *   S = T * H * W, in one of these orders as each call states.
+ *
+ * Conventions for every call.
+ *   - Device pointers are caller-owned device memory (e.g. torch tensors). The
+ *     library allocates no device memory and keeps no state between calls
+ *     apart from a thread-local error message.
+ *   - Host arrays (tile, window) are read during the call only; the window
+ *     table is copied into the kernel arguments, so it may be freed on return.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     is asynchronous: inputs must stay alive and unmodified until the stream
+ *     has passed the work.
+ *   - Arguments are validated before anything is enqueued. On any error the
+ *     call returns a negative sta_status, enqueues nothing (except STA_ERR_HIP,
+ *     which reports a failed launch) and sta_last_error() describes it.
+ *   - Outputs must not overlap any input.
+ */
+#ifndef STA_H_
+#define STA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  STA_OK = 0,
+  STA_ERR_INVALID_ARG = -1, /* NULL pointer, bad size, tile/window mismatch, overlap */
+  STA_ERR_UNSUPPORTED = -2, /* a valid request this build has no kernel for */
+  STA_ERR_HIP = -3          /* the HIP runtime reported an error at launch */
+} sta_status;
+
+typedef enum {
+  STA_BF16 = 0, /* bfloat16 storage, float32 accumulation */
+  STA_F32 = 1   /* float32 storage and arithmetic */
+} sta_dtype;
+
+/* Largest head count whose window table fits the kernel arguments. */
+#define STA_MAX_HEADS 256
+
+/* Version of this interface; bumped on any incompatible change. */
+int sta_abi_version(void);
+
+/*
+ * Permute the token axis from raster to tile-major order (a bit-exact copy).
+ * The pages describe a tile as a contiguous cube of tokens (podcast
+ * transcript, the answer on what a tile is); this call makes each tile one
+ * contiguous run of tau rows so that attention can stream it.
+ *   x_raster: device, [B][heads][S][head_dim] raster order, read.
+ *   x_tiled:  device, same size, written in tile-major order. No overlap.
+ *   tile:     host int[3] (c_t, c_h, c_w), each dividing (T, H, W).
+ *   dtype:    sta_dtype; head_dim * element size must be a multiple of 16 bytes.
+ */
+int sta_reorder_tiles(const void* x_raster, void* x_tiled, int B, int heads, int head_dim,
+                      int T, int H, int W, const int* tile, int dtype, void* stream);
+
+/*
+ * Inverse of sta_reorder_tiles: tile-major back to raster order (bit-exact).
+ * Same arguments, with the roles of input and output swapped.
+ */
+int sta_restore_order(const void* x_tiled, void* x_raster, int B, int heads, int head_dim,
+                      int T, int H, int W, const int* tile, int dtype, void* stream);
+
+/*
+ * Enumerate, per head and query tile, the key tiles of its window: the
+ * implicit block-sparse mask of STA (podcast transcript, the answers on the
+ * producer warpgroups that hold the sparse mask and on the threadblock split).
+ *   kv_list:  device int32 [heads][N_t][max_kv]; entries 0..count-1 hold the
+ *             selected key tile indices in ascending order (raster order of
+ *             tile coordinates), the rest are -1.
+ *   kv_count: device int32 [heads][N_t]; omega_t * omega_h * omega_w.
+ *   window:   host int[heads][3], tokens, each a multiple of the tile and at
+ *             most the volume on its axis.
+ *   max_kv:   row length of kv_list; must be >= the largest count.
+ * N_t = (T/c_t) * (H/c_h) * (W/c_w).
+ */
+int sta_kv_tiles(int* kv_list, int* kv_count, int heads, int T, int H, int W, const int* tile,
+                 const int* window, int max_kv, void* stream);
+
+/*
+ * Number of computed (query tile, key tile) pairs summed over heads, for one
+ * batch entry: sum_h N_t * prod_a omega_a. Host only; enqueues nothing.
+ * Returns a negative sta_status on invalid arguments.
+ */
+long long sta_kv_pair_count(int heads, int T, int H, int W, const int* tile, const int* window);
+
+/*
+ * STA forward: for every batch entry b, head h and query tile i,
+ *     O_i = softmax(scale * Q_i K_J^T) V_J,
+ * with J the tokens of the key tiles in tile i's window (rule above) and the
+ * softmax taken over those keys only. Softmax base e; only dense blocks are
+ * computed (atlas.scime.ai summary, "Approach"; podcast transcript, the answer
+ * on how blocks are computed). The window's key tiles are found inside the
+ * kernel by the same integer rule as sta_kv_tiles.
+ *   q, k, v: device [B][heads][S][head_dim] in TILE-MAJOR order, read.
+ *   out:     device, same shape, tile-major, written. No overlap with inputs.
+ *   tile:    host int[3]; window: host int[heads][3] (tokens), as above.
+ *   scale:   finite, > 0 (1/sqrt(head_dim) is the usual choice).
+ *   dtype:   STA_BF16 (head_dim 64 or 128) or STA_F32 (head_dim 64 or 128).
+ * Accumulation is float32; for STA_BF16 the probabilities are rounded to
+ * bfloat16 before they multiply V, and the output is rounded to bfloat16.
+ */
+int sta_forward(const void* q, const void* k, const void* v, void* out, int B, int heads,
+                int head_dim, int T, int H, int W, const int* tile, const int* window,
+                float scale, int dtype, void* stream);
+
+/*
+ * Full softmax attention over all S keys (the computation STA replaces, used
+ * as the speed-up denominator: atlas.scime.ai summary, "Key results").
+ *   q, k, v, out: device [B][heads][S][head_dim], any common token order.
+ * Same dtype, head_dim and scale rules as sta_forward; S >= 1, any length.
+ */
+int sta_full_attention(const void* q, const void* k, const void* v, void* out, int B, int heads,
+                       int head_dim, int S, float scale, int dtype, void* stream);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* sta_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STA_H_ */

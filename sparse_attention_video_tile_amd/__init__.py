@@ -1,1 +1,19 @@
-"""Sliding Tile Attention forward for AMD MI355X (gfx950)."""
+"""Sliding Tile Attention forward for AMD MI355X (gfx950).
+
+The compute path is libsta.so (HIP kernels + C ABI, see include/sta.h); the
+functions re-exported here are its ctypes binding.
+"""
+
+from .binding import (  # noqa: F401
+    STA_MAX_HEADS,
+    StaError,
+    last_error,
+    load_library,
+    sliding_tile_attention,
+    sta_forward,
+    sta_full_attention,
+    sta_kv_pair_count,
+    sta_kv_tiles,
+    sta_reorder_tiles,
+    sta_restore_order,
+)

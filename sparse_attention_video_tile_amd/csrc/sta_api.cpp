@@ -1,0 +1,234 @@
+// C-ABI entry points of libsta: argument checks, then dispatch to the HIP
+// launchers. Nothing here touches the device before every check has passed.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "sta.h"
+#include "sta_geometry.h"
+#include "sta_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return STA_OK;
+}
+
+int elem_size(int dtype) {
+  switch (dtype) {
+    case STA_BF16: return 2;
+    case STA_F32: return 4;
+    default: return 0;
+  }
+}
+
+// Byte ranges [a, a+na) and [b, b+nb) overlap.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a);
+  const uintptr_t pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+// Checks the volume and tile, fills g. Returns STA_OK or an error status.
+int check_volume(int T, int H, int W, const int* tile, sta::Geometry* g) {
+  if (!tile) return fail(STA_ERR_INVALID_ARG, "tile is NULL");
+  if (T <= 0 || H <= 0 || W <= 0)
+    return fail(STA_ERR_INVALID_ARG, "volume (%d,%d,%d) must be positive", T, H, W);
+  if (tile[0] <= 0 || tile[1] <= 0 || tile[2] <= 0)
+    return fail(STA_ERR_INVALID_ARG, "tile (%d,%d,%d) must be positive", tile[0], tile[1], tile[2]);
+  if (T % tile[0] || H % tile[1] || W % tile[2])
+    return fail(STA_ERR_INVALID_ARG, "tile (%d,%d,%d) does not divide volume (%d,%d,%d)", tile[0],
+                tile[1], tile[2], T, H, W);
+  const long long S = (long long)T * H * W;
+  if (S > (1LL << 30)) return fail(STA_ERR_INVALID_ARG, "volume of %lld tokens is too large", S);
+  g->T = T; g->H = H; g->W = W;
+  g->ct = tile[0]; g->ch = tile[1]; g->cw = tile[2];
+  g->nt = T / tile[0]; g->nh = H / tile[1]; g->nw = W / tile[2];
+  g->n_tiles = g->nt * g->nh * g->nw;
+  g->tau = tile[0] * tile[1] * tile[2];
+  g->S = (int)S;
+  return STA_OK;
+}
+
+// Checks the per-head windows against the geometry; fills omega (tiles).
+int check_windows(const sta::Geometry& g, int heads, const int* window, uint16_t (*omega)[3]) {
+  if (!window) return fail(STA_ERR_INVALID_ARG, "window is NULL");
+  const int ext[3] = {g.T, g.H, g.W};
+  const int c[3] = {g.ct, g.ch, g.cw};
+  for (int h = 0; h < heads; ++h) {
+    for (int a = 0; a < 3; ++a) {
+      const int w = window[3 * h + a];
+      if (w <= 0 || w % c[a] || w > ext[a])
+        return fail(STA_ERR_INVALID_ARG,
+                    "window (%d,%d,%d) of head %d must be a positive multiple of the tile "
+                    "(%d,%d,%d) and at most the volume (%d,%d,%d)",
+                    window[3 * h], window[3 * h + 1], window[3 * h + 2], h, g.ct, g.ch, g.cw, g.T,
+                    g.H, g.W);
+      omega[h][a] = (uint16_t)(w / c[a]);
+    }
+  }
+  return STA_OK;
+}
+
+int check_heads(int B, int heads, int head_dim) {
+  if (B <= 0 || heads <= 0 || head_dim <= 0)
+    return fail(STA_ERR_INVALID_ARG, "B=%d, heads=%d, head_dim=%d must be positive", B, heads,
+                head_dim);
+  return STA_OK;
+}
+
+int launched(int rc) {
+  if (rc == 0) return ok();
+  if (rc < 0) return rc;  // message already set by the launcher's caller
+  return fail(STA_ERR_HIP, "HIP launch failed: %s", sta::hip_error_string(rc));
+}
+
+int reorder_common(const void* src, void* dst, int B, int heads, int head_dim, int T, int H,
+                   int W, const int* tile, int dtype, void* stream, bool to_tiles) {
+  if (!src || !dst) return fail(STA_ERR_INVALID_ARG, "input or output pointer is NULL");
+  int rc = check_heads(B, heads, head_dim);
+  if (rc) return rc;
+  const int es = elem_size(dtype);
+  if (!es) return fail(STA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  sta::Geometry g;
+  if ((rc = check_volume(T, H, W, tile, &g))) return rc;
+  const long long row_bytes = (long long)head_dim * es;
+  if (row_bytes % 16)
+    return fail(STA_ERR_UNSUPPORTED, "head_dim * element size (%lld bytes) must be a multiple of 16",
+                row_bytes);
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16)
+    return fail(STA_ERR_UNSUPPORTED, "input and output must be 16-byte aligned");
+  const long long BH = (long long)B * heads;
+  if (BH > (1LL << 24)) return fail(STA_ERR_INVALID_ARG, "B*heads=%lld is too large", BH);
+  const size_t bytes = (size_t)BH * g.S * row_bytes;
+  if (overlaps(src, bytes, dst, bytes)) return fail(STA_ERR_INVALID_ARG, "input and output overlap");
+  return launched(sta::launch_reorder(src, dst, (int)BH, (int)row_bytes, g, to_tiles, stream));
+}
+
+int attention_common(sta::AttnProblem& p, void* stream) {
+  if (!p.q || !p.k || !p.v || !p.out) return fail(STA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  int rc = check_heads(p.B, p.heads, p.head_dim);
+  if (rc) return rc;
+  const int es = elem_size(p.dtype);
+  if (!es) return fail(STA_ERR_INVALID_ARG, "unknown dtype %d", p.dtype);
+  if (!(p.scale > 0.0f) || !isfinite(p.scale))
+    return fail(STA_ERR_INVALID_ARG, "scale %g must be finite and positive", (double)p.scale);
+  if (p.head_dim != 64 && p.head_dim != 128)
+    return fail(STA_ERR_UNSUPPORTED, "head_dim %d: kernels exist for 64 and 128", p.head_dim);
+  const uintptr_t any = reinterpret_cast<uintptr_t>(p.q) | reinterpret_cast<uintptr_t>(p.k) |
+                        reinterpret_cast<uintptr_t>(p.v) | reinterpret_cast<uintptr_t>(p.out);
+  if (any % 16) return fail(STA_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
+  const long long BH = (long long)p.B * p.heads;
+  if (BH > (1LL << 24)) return fail(STA_ERR_INVALID_ARG, "B*heads=%lld is too large", BH);
+  const size_t bytes = (size_t)BH * p.g.S * p.head_dim * es;
+  if (overlaps(p.out, bytes, p.q, bytes) || overlaps(p.out, bytes, p.k, bytes) ||
+      overlaps(p.out, bytes, p.v, bytes))
+    return fail(STA_ERR_INVALID_ARG, "output overlaps an input");
+  rc = sta::launch_attention(p, stream);
+  if (rc < 0) return fail(rc, "no kernel for dtype %d with head_dim %d", p.dtype, p.head_dim);
+  return launched(rc);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sta_abi_version(void) { return 1; }
+
+const char* sta_last_error(void) { return g_last_error.c_str(); }
+
+int sta_reorder_tiles(const void* x_raster, void* x_tiled, int B, int heads, int head_dim, int T,
+                      int H, int W, const int* tile, int dtype, void* stream) {
+  return reorder_common(x_raster, x_tiled, B, heads, head_dim, T, H, W, tile, dtype, stream, true);
+}
+
+int sta_restore_order(const void* x_tiled, void* x_raster, int B, int heads, int head_dim, int T,
+                      int H, int W, const int* tile, int dtype, void* stream) {
+  return reorder_common(x_tiled, x_raster, B, heads, head_dim, T, H, W, tile, dtype, stream, false);
+}
+
+long long sta_kv_pair_count(int heads, int T, int H, int W, const int* tile, const int* window) {
+  if (heads <= 0 || heads > STA_MAX_HEADS)
+    return fail(STA_ERR_INVALID_ARG, "heads=%d must be in [1, %d]", heads, STA_MAX_HEADS);
+  sta::Geometry g;
+  int rc = check_volume(T, H, W, tile, &g);
+  if (rc) return rc;
+  static thread_local uint16_t omega[STA_MAX_HEADS][3];
+  if ((rc = check_windows(g, heads, window, omega))) return rc;
+  long long pairs = 0;
+  for (int h = 0; h < heads; ++h)
+    pairs += (long long)g.n_tiles * omega[h][0] * omega[h][1] * omega[h][2];
+  ok();
+  return pairs;
+}
+
+int sta_kv_tiles(int* kv_list, int* kv_count, int heads, int T, int H, int W, const int* tile,
+                 const int* window, int max_kv, void* stream) {
+  if (!kv_list || !kv_count) return fail(STA_ERR_INVALID_ARG, "kv_list or kv_count is NULL");
+  if (heads <= 0 || heads > STA_MAX_HEADS)
+    return fail(STA_ERR_INVALID_ARG, "heads=%d must be in [1, %d]", heads, STA_MAX_HEADS);
+  sta::Geometry g;
+  int rc = check_volume(T, H, W, tile, &g);
+  if (rc) return rc;
+  uint16_t omega[STA_MAX_HEADS][3];
+  if ((rc = check_windows(g, heads, window, omega))) return rc;
+  int need = 0;
+  for (int h = 0; h < heads; ++h) {
+    const int c = omega[h][0] * omega[h][1] * omega[h][2];
+    need = c > need ? c : need;
+  }
+  if (max_kv < need) return fail(STA_ERR_INVALID_ARG, "max_kv=%d is below the largest count %d", max_kv, need);
+  const size_t list_bytes = (size_t)heads * g.n_tiles * max_kv * sizeof(int);
+  const size_t count_bytes = (size_t)heads * g.n_tiles * sizeof(int);
+  if (overlaps(kv_list, list_bytes, kv_count, count_bytes))
+    return fail(STA_ERR_INVALID_ARG, "kv_list and kv_count overlap");
+  if ((long long)heads * g.n_tiles * max_kv > (1LL << 31) - 1)
+    return fail(STA_ERR_INVALID_ARG, "kv_list is too large");
+  return launched(sta::launch_kv_tiles(kv_list, kv_count, heads, g, omega, max_kv, stream));
+}
+
+int sta_forward(const void* q, const void* k, const void* v, void* out, int B, int heads,
+                int head_dim, int T, int H, int W, const int* tile, const int* window, float scale,
+                int dtype, void* stream) {
+  if (heads <= 0 || heads > STA_MAX_HEADS)
+    return fail(STA_ERR_INVALID_ARG, "heads=%d must be in [1, %d]", heads, STA_MAX_HEADS);
+  static thread_local sta::AttnProblem p;
+  p.q = q; p.k = k; p.v = v; p.out = out;
+  p.B = B; p.heads = heads; p.head_dim = head_dim; p.dtype = dtype; p.scale = scale;
+  p.dense = false;
+  int rc = check_volume(T, H, W, tile, &p.g);
+  if (rc) return rc;
+  if ((rc = check_windows(p.g, heads, window, p.omega))) return rc;
+  return attention_common(p, stream);
+}
+
+int sta_full_attention(const void* q, const void* k, const void* v, void* out, int B, int heads,
+                       int head_dim, int S, float scale, int dtype, void* stream) {
+  if (S <= 0 || S > (1 << 30)) return fail(STA_ERR_INVALID_ARG, "S=%d must be in [1, 2^30]", S);
+  static thread_local sta::AttnProblem p;
+  memset(&p.g, 0, sizeof(p.g));
+  p.q = q; p.k = k; p.v = v; p.out = out;
+  p.B = B; p.heads = heads; p.head_dim = head_dim; p.dtype = dtype; p.scale = scale;
+  p.dense = true;
+  p.g.S = S;
+  return attention_common(p, stream);
+}
+
+}  // extern "C"

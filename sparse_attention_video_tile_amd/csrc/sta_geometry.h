@@ -1,0 +1,38 @@
+// Integer geometry of Sliding Tile Attention, shared by the host checks and
+// the HIP kernels of libsta.
+//
+// A (T, H, W) token volume is cut into (c_t, c_h, c_w) tiles; a head's window
+// is a whole number of tiles per axis. The window keeps its size at the border
+// of the volume: its start along an axis is the query tile minus half the
+// window (rounded down), clamped into [0, n - omega].
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define STA_HD __host__ __device__ __forceinline__
+#else
+#define STA_HD inline
+#endif
+
+namespace sta {
+
+// First key tile of the window along one axis of n tiles, for query tile q
+// and a window of omega tiles (1 <= omega <= n).
+STA_HD int window_start(int q, int n, int omega) {
+  int s = q - omega / 2;
+  s = s < 0 ? 0 : s;
+  const int hi = n - omega;
+  return s > hi ? hi : s;
+}
+
+struct Geometry {
+  int T, H, W;     // tokens per axis
+  int ct, ch, cw;  // tile size in tokens
+  int nt, nh, nw;  // tiles per axis
+  int n_tiles;     // nt * nh * nw
+  int tau;         // tokens per tile
+  int S;           // tokens in the volume
+};
+
+}  // namespace sta

@@ -1,0 +1,40 @@
+// Launch interface between the C-ABI layer (sta_api.cpp) and the HIP kernels.
+// Every launcher enqueues on the given stream and returns 0 on success or the
+// hipError_t value reported by the runtime right after the launch.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sta.h"
+#include "sta_geometry.h"
+
+namespace sta {
+
+struct AttnProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int B, heads, head_dim;
+  int dtype;       // sta_dtype
+  float scale;
+  bool dense;      // true: every query attends to all S keys
+  Geometry g;      // for dense problems only g.S is used
+  // Window per head in tiles (sparse problems only).
+  uint16_t omega[STA_MAX_HEADS][3];
+};
+
+int launch_reorder(const void* src, void* dst, int BH, int row_bytes, const Geometry& g,
+                   bool to_tiles, void* stream);
+
+int launch_kv_tiles(int* kv_list, int* kv_count, int heads, const Geometry& g,
+                    const uint16_t (*omega)[3], int max_kv, void* stream);
+
+// Returns STA_ERR_UNSUPPORTED (as a negative value) when no kernel exists for
+// the (dtype, head_dim) pair, 0 on success, or a positive hipError_t.
+int launch_attention(const AttnProblem& p, void* stream);
+
+const char* hip_error_string(int code);
+
+}  // namespace sta

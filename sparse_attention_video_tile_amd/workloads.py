@@ -13,13 +13,17 @@ for them: a 30x48x80 latent volume, 24 heads of dimension 128, tile (6,8,8).
 The window triples in tokens, (18,24,24), (30,40,40) and the whole volume, are
 the ones the same summary lists in its measured-effects table.
 
-Draw order (NumPy PCG64, ``default_rng(seed)``):
-  1. q, k, v, each ``standard_normal((B, heads, T, H, W, d), float32)``;
-  2. if the windows are drawn: one index per head, ``integers(0, n_options)``;
-  3. if a sinusoid is added: integer frequencies ``integers(0, 3, (d, 3))``
-     (cycles per extent along t, y, x) and phases ``uniform(0, 2*pi, d)``; the
-     field ``amp * sin(2*pi*(f_t t/T + f_y y/H + f_x x/W) + phase)`` is added to
-     q, k and v for every batch entry and head.
+Random streams (NumPy PCG64):
+  * ``default_rng(seed)``: q, k, v in that order, each
+    ``standard_normal((B, heads, T, H, W, d), float32)``;
+  * ``default_rng((seed, 1))``: if the windows are drawn, one option index per
+    head, ``integers(0, n_options, heads)`` (independent of the tensor sizes, so
+    the windows are known without drawing the tensors);
+  * ``default_rng((seed, 2))``: if a sinusoid is added, integer frequencies
+    ``integers(0, 3, (d, 3))`` (cycles per extent along t, y, x) and phases
+    ``uniform(0, 2*pi, d)``; the field
+    ``amp * sin(2*pi*(f_t t/T + f_y y/H + f_x x/W) + phase)`` is added to q, k
+    and v for every batch entry and head.
 Then bf16 workloads are rounded once, round-to-nearest-even, with torch's cast.
 """
 
@@ -141,6 +145,18 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).to(torch.float32).numpy()
 
 
+def head_windows(w: Workload) -> np.ndarray:
+    """Token windows per head as an int32 (heads, 3) array (drawn if need be)."""
+    if w.windows is None:
+        if not w.window_options:
+            raise ValueError("workload has neither windows nor window options")
+        idx = np.random.default_rng((w.seed, 1)).integers(0, len(w.window_options), w.heads)
+        return np.asarray([w.window_options[i] for i in idx], dtype=np.int32)
+    if len(w.windows) != w.heads:
+        raise ValueError("one window triple per head is required")
+    return np.asarray(w.windows, dtype=np.int32).reshape(w.heads, 3)
+
+
 def make_inputs(w: Workload) -> Inputs:
     """Draw q, k, v (and, if asked, windows and a shared sinusoid) for ``w``."""
     rng = np.random.default_rng(w.seed)
@@ -149,21 +165,13 @@ def make_inputs(w: Workload) -> Inputs:
     q = rng.standard_normal(shape, dtype=np.float32)
     k = rng.standard_normal(shape, dtype=np.float32)
     v = rng.standard_normal(shape, dtype=np.float32)
-
-    if w.windows is None:
-        if not w.window_options:
-            raise ValueError("workload has neither windows nor window options")
-        idx = rng.integers(0, len(w.window_options), w.heads)
-        windows = np.asarray([w.window_options[i] for i in idx], dtype=np.int32)
-    else:
-        if len(w.windows) != w.heads:
-            raise ValueError("one window triple per head is required")
-        windows = np.asarray(w.windows, dtype=np.int32).reshape(w.heads, 3)
+    windows = head_windows(w)
 
     if w.sinusoid_amp:
         d = w.head_dim
-        freq = rng.integers(0, 3, (d, 3))
-        phase = rng.uniform(0.0, 2.0 * math.pi, d)
+        srng = np.random.default_rng((w.seed, 2))
+        freq = srng.integers(0, 3, (d, 3))
+        phase = srng.uniform(0.0, 2.0 * math.pi, d)
         t = np.arange(T, dtype=np.float64)[:, None, None, None] / T
         y = np.arange(H, dtype=np.float64)[None, :, None, None] / H
         x = np.arange(W, dtype=np.float64)[None, None, :, None] / W

@@ -1,0 +1,121 @@
+"""The C-ABI library loads and exports what include/sta.h declares; host-side
+argument checks reject bad calls before anything reaches a device. No test
+here launches a kernel."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_attention_video_tile_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sta.h")
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z ]+\*?\s*(sta_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_header_declares_expected_functions():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.sta_abi_version() == binding.ABI_VERSION
+
+
+def i3(*v):
+    return binding._int_array(v)
+
+
+def test_reorder_rejects_bad_arguments(lib):
+    t = i3(6, 8, 8)
+    assert lib.sta_reorder_tiles(None, FAKE, 1, 1, 128, 30, 48, 80, t, 0, None) == -1
+    assert lib.sta_reorder_tiles(FAKE, FAKE * 4, 1, 1, 128, 31, 48, 80, t, 0, None) == -1
+    assert "does not divide" in binding.last_error()
+    assert lib.sta_reorder_tiles(FAKE, FAKE * 4, 0, 1, 128, 30, 48, 80, t, 0, None) == -1
+    assert lib.sta_reorder_tiles(FAKE, FAKE * 4, 1, 1, 128, 30, 48, 80, t, 7, None) == -1
+    assert lib.sta_reorder_tiles(FAKE, FAKE * 4, 1, 1, 4, 30, 48, 80, t, 0, None) == -2
+    # in-place / overlapping buffers
+    assert lib.sta_reorder_tiles(FAKE, FAKE + 16, 1, 1, 128, 30, 48, 80, t, 0, None) == -1
+    assert "overlap" in binding.last_error()
+    assert lib.sta_restore_order(FAKE, FAKE, 1, 1, 128, 30, 48, 80, t, 0, None) == -1
+
+
+def test_forward_rejects_bad_arguments(lib):
+    t = i3(6, 8, 8)
+    w = i3(18, 24, 24)
+    args = lambda **kw: dict(dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, o=FAKE * 1000, B=1, heads=1, d=128,
+                                  T=30, H=48, W=80, tile=t, win=w, scale=0.1, dt=0), **kw)
+
+    def call(a):
+        return lib.sta_forward(a["q"], a["k"], a["v"], a["o"], a["B"], a["heads"], a["d"], a["T"], a["H"],
+                               a["W"], a["tile"], a["win"], a["scale"], a["dt"], None)
+
+    assert call(args(q=None)) == -1
+    assert call(args(o=None)) == -1
+    assert call(args(win=None)) == -1
+    assert call(args(heads=0)) == -1
+    assert call(args(heads=binding.STA_MAX_HEADS + 1)) == -1
+    assert call(args(win=i3(20, 24, 24))) == -1      # not whole tiles
+    assert call(args(win=i3(36, 24, 24))) == -1      # larger than the volume
+    assert "window" in binding.last_error()
+    assert call(args(win=i3(0, 24, 24))) == -1
+    assert call(args(tile=i3(7, 8, 8))) == -1
+    assert call(args(scale=0.0)) == -1
+    assert call(args(scale=float("nan"))) == -1
+    assert call(args(scale=float("inf"))) == -1
+    assert call(args(dt=5)) == -1
+    assert call(args(d=96)) == -2
+    assert call(args(q=FAKE + 8)) == -2              # misaligned
+    assert call(args(o=FAKE * 2)) == -1              # out aliases k
+    assert "overlap" in binding.last_error()
+
+
+def test_full_attention_rejects_bad_arguments(lib):
+    f = lib.sta_full_attention
+    assert f(FAKE, FAKE * 2, FAKE * 3, None, 1, 1, 128, 1024, 0.1, 0, None) == -1
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 1000, 1, 1, 128, 0, 0.1, 0, None) == -1
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 1000, 1, 1, 128, 1024, -1.0, 0, None) == -1
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 1000, 1, 1, 48, 1024, 0.1, 0, None) == -2
+
+
+def test_kv_tiles_rejects_bad_arguments(lib):
+    t = i3(6, 8, 8)
+    w = i3(18, 24, 24)
+    assert lib.sta_kv_tiles(None, FAKE, 1, 30, 48, 80, t, w, 27, None) == -1
+    assert lib.sta_kv_tiles(FAKE, FAKE * 1000, 1, 30, 48, 80, t, w, 26, None) == -1  # max_kv too small
+    assert lib.sta_kv_tiles(FAKE, FAKE + 4, 1, 30, 48, 80, t, w, 27, None) == -1  # overlap
+
+
+@pytest.mark.parametrize(
+    "heads,volume,tile,windows",
+    [
+        (1, (30, 48, 80), (6, 8, 8), [(18, 24, 24)]),
+        (3, (30, 48, 80), (6, 8, 8), [(18, 24, 24), (30, 40, 40), (30, 48, 80)]),
+        (2, (12, 16, 16), (4, 4, 4), [(12, 12, 12), (4, 8, 16)]),
+        (1, (6, 9, 10), (3, 3, 2), [(3, 6, 4)]),
+    ],
+)
+def test_kv_pair_count_matches_oracle(heads, volume, tile, windows):
+    got = binding.sta_kv_pair_count(heads, volume, tile, windows)
+    assert got == oracle.kv_pair_count(volume, tile, np.array(windows))
+
+
+def test_kv_pair_count_rejects_bad_window(lib):
+    assert lib.sta_kv_pair_count(1, 30, 48, 80, i3(6, 8, 8), i3(18, 24, 25)) == -1

@@ -1,0 +1,148 @@
+"""GPU: STA forward and the dense comparator against the float64 oracle,
+element by element, on small seeded workloads that span several tiles."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_video_tile_amd import binding, workloads
+from tests.parity_util import assert_close, default_scale, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def run_sta(inp: workloads.Inputs, scale=None):
+    """The whole path: raster inputs -> reorder -> forward -> restore -> numpy."""
+    w = inp.workload
+    q, k, v = (to_gpu(x, w.dtype) for x in (inp.q, inp.k, inp.v))
+    out = binding.sliding_tile_attention(q, k, v, w.tile, inp.windows, scale)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+SMALL_CASES = [
+    # name, volume, tile, windows per head, head_dim, dtype
+    ("hunyuan_tiles_2x2x3", (12, 16, 24), (6, 8, 8), [(6, 8, 8), (12, 16, 24), (6, 16, 8)], 128, "bf16"),
+    ("tile64_3x4x4_w333", (12, 16, 16), (4, 4, 4), [(12, 12, 12), (4, 4, 4)], 128, "bf16"),
+    ("tile64_d64", (12, 16, 16), (4, 4, 4), [(12, 12, 12), (8, 8, 8)], 64, "bf16"),  # even windows
+    ("tile48_ragged_runs", (9, 8, 12), (3, 4, 4), [(6, 4, 8), (9, 8, 12)], 128, "bf16"),
+    ("tile128", (8, 8, 16), (4, 4, 8), [(4, 8, 8), (8, 4, 16)], 128, "bf16"),
+    ("tile8_tiny", (4, 4, 6), (2, 2, 2), [(2, 2, 2), (4, 4, 6), (4, 2, 4)], 128, "bf16"),
+    ("one_tile_volume", (6, 8, 8), (6, 8, 8), [(6, 8, 8)], 128, "bf16"),
+    ("f32_tiny_like", (12, 16, 16), (4, 4, 4), [(12, 12, 12), (4, 8, 12)], 64, "f32"),
+    ("f32_d128", (6, 8, 8), (2, 4, 4), [(4, 8, 4), (6, 8, 8)], 128, "f32"),
+    ("f32_ragged", (9, 8, 12), (3, 4, 4), [(6, 4, 8)], 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: c[0])
+def test_forward_matches_oracle(case):
+    name, volume, tile, windows, d, dtype = case
+    w = workloads.small_case(volume, tile, windows, head_dim=d, dtype=dtype, seed=11, name=name)
+    print(f"[case] forward {w}", flush=True)
+    inp = workloads.make_inputs(w)
+    got = run_sta(inp)
+    ref = oracle.sta_attention(inp.q, inp.k, inp.v, tile, inp.windows, default_scale(d))
+    assert_close(got, ref, dtype, name)
+
+
+def test_forward_batch_and_sinusoid():
+    w = workloads.small_case((12, 16, 24), (6, 8, 8), [(6, 16, 8), (12, 8, 24)], B=2, seed=5,
+                             sinusoid_amp=0.5, name="batch2_sinusoid")
+    print(f"[case] forward {w}", flush=True)
+    inp = workloads.make_inputs(w)
+    got = run_sta(inp, scale=0.2)
+    ref = oracle.sta_attention(inp.q, inp.k, inp.v, w.tile, inp.windows, 0.2)
+    assert_close(got, ref, "bf16", w.name)
+
+
+def test_tiny_named_config():
+    w = workloads.TINY_F32
+    print(f"[case] forward {w.name}", flush=True)
+    inp = workloads.make_inputs(w)
+    got = run_sta(inp)
+    ref = oracle.sta_attention(inp.q, inp.k, inp.v, w.tile, inp.windows, default_scale(w.head_dim))
+    assert_close(got, ref, "f32", w.name)
+
+
+def test_zero_query_gives_window_mean():
+    w = workloads.small_case((12, 16, 24), (6, 8, 8), [(6, 8, 24)], seed=3, name="zero_q")
+    print(f"[case] forward {w.name}", flush=True)
+    inp = workloads.make_inputs(w)
+    inp.q[...] = 0.0
+    got = run_sta(inp)
+    ref = oracle.sta_attention(inp.q, inp.k, inp.v, w.tile, inp.windows, 1.0)
+    assert_close(got, ref, "bf16", w.name)
+
+
+def test_constant_values_pass_through():
+    w = workloads.small_case((12, 16, 16), (4, 4, 4), [(8, 8, 8)], seed=4, name="const_v")
+    print(f"[case] forward {w.name}", flush=True)
+    inp = workloads.make_inputs(w)
+    const = workloads.round_to_bf16(np.linspace(-2, 2, w.head_dim, dtype=np.float32))
+    inp.v[...] = const
+    got = run_sta(inp)
+    np.testing.assert_allclose(got, np.broadcast_to(const, got.shape), rtol=0, atol=2e-2)
+
+
+def test_forward_is_deterministic():
+    w = workloads.small_case((12, 16, 24), (6, 8, 8), [(6, 16, 8)], seed=8, name="det")
+    print(f"[case] forward determinism {w.name}", flush=True)
+    inp = workloads.make_inputs(w)
+    a, b = run_sta(inp), run_sta(inp)
+    assert np.array_equal(a, b)
+
+
+def test_whole_volume_window_equals_dense_kernel():
+    w = workloads.small_case((12, 16, 24), (6, 8, 8), [(12, 16, 24), (12, 16, 24)], seed=9, name="whole")
+    print(f"[case] whole-volume STA vs dense kernel", flush=True)
+    inp = workloads.make_inputs(w)
+    sta = run_sta(inp)
+    q, k, v = (to_gpu(x.reshape(w.B, w.heads, -1, w.head_dim), "bf16") for x in (inp.q, inp.k, inp.v))
+    dense = binding.sta_full_attention(q, k, v).float().cpu().numpy().reshape(sta.shape)
+    ref = oracle.full_attention(inp.q, inp.k, inp.v, default_scale(w.head_dim))
+    assert_close(sta, ref, "bf16", "whole-volume STA")
+    assert_close(dense, ref, "bf16", "dense kernel")
+    assert np.abs(sta - dense).max() <= 2e-2
+
+
+@pytest.mark.parametrize("S,d,dtype", [(1, 128, "bf16"), (100, 128, "bf16"), (1000, 64, "bf16"),
+                                       (4608, 128, "bf16"), (777, 64, "f32"), (300, 128, "f32")])
+def test_dense_kernel_matches_oracle(S, d, dtype):
+    print(f"[case] dense S={S} d={d} {dtype}", flush=True)
+    rng = np.random.default_rng(S + d)
+    shape = (1, 2, S, d)
+    xs = [rng.standard_normal(shape, dtype=np.float32) for _ in range(3)]
+    if dtype == "bf16":
+        xs = [workloads.round_to_bf16(x) for x in xs]
+    q, k, v = (to_gpu(x, dtype) for x in xs)
+    got = binding.sta_full_attention(q, k, v).float().cpu().numpy()
+    ref = oracle.full_attention(*xs, default_scale(d))
+    assert_close(got, ref, dtype, f"dense S={S}")
+
+
+def test_large_logits_are_stable():
+    w = workloads.small_case((12, 16, 16), (4, 4, 4), [(8, 8, 8)], seed=6, name="large_logits")
+    print(f"[case] forward {w.name}", flush=True)
+    inp = workloads.make_inputs(w)
+    inp.q *= 8.0
+    inp.q = workloads.round_to_bf16(inp.q)
+    got = run_sta(inp)
+    ref = oracle.sta_attention(inp.q, inp.k, inp.v, w.tile, inp.windows, default_scale(w.head_dim))
+    assert np.isfinite(got).all()
+    assert_close(got, ref, "bf16", w.name)
+
+
+def test_invalid_inputs_raise_before_launch():
+    q = torch.zeros((1, 1, 384, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        binding.sta_forward(q, q.clone(), q.clone(), (6, 8, 8), (6, 8, 8), [(7, 8, 8)])
+    with pytest.raises(NotImplementedError):
+        x = torch.zeros((1, 1, 384, 96), dtype=torch.bfloat16, device="cuda")
+        binding.sta_forward(x, x.clone(), x.clone(), (6, 8, 8), (6, 8, 8), [(6, 8, 8)])
+    with pytest.raises(TypeError):
+        x = torch.zeros((1, 1, 384, 128), dtype=torch.float16, device="cuda")
+        binding.sta_forward(x, x.clone(), x.clone(), (6, 8, 8), (6, 8, 8), [(6, 8, 8)])
