@@ -132,26 +132,73 @@ struct Bf16Cfg {
   static constexpr int kThreads = WAVES * 64;
   static constexpr int kRowsWave = 16 * RB;
   static constexpr int kRows = WAVES * kRowsWave;
-  static constexpr int kDK = D / 32;     // k-steps of S^T = K Q^T
-  static constexpr int kDB = D / 16;     // 16-row blocks of O^T
-  static constexpr int kKT = BN / 16;    // 16-key score tiles per chunk
-  static constexpr int kKP = BN / 32;    // 32-key steps of O^T += V^T P^T
-  static constexpr int kKPitch = D + 8;  // LDS row pitch of K (elements)
-  static constexpr int kVPitch = BN + 8; // LDS row pitch of V^T (elements)
-  static constexpr int kPieces = BN * D / 8;  // 16-byte pieces per chunk of K (or V)
+  static constexpr int kDK = D / 32;            // k-steps of S^T = K Q^T
+  static constexpr int kDB = D / 16;            // 16-row blocks of O^T
+  static constexpr int kKT = BN / 16;           // 16-key score tiles per chunk
+  static constexpr int kKP = BN / 32;           // 32-key steps of O^T += V^T P^T
+  static constexpr int kRowBytes = D * 2;       // one key row of K or V
+  static constexpr int kCPR = kRowBytes / 16;   // 16-byte chunks per row
+  static constexpr int kChunkBytes = BN * kRowBytes;       // K (or V) of one chunk
+  static constexpr int kBlocks = kChunkBytes / 1024;       // 1 KB LDS-DMA blocks per chunk
+  static constexpr int kBlocksPerWave = kBlocks / WAVES;
+  static constexpr int kRowsPerBlock = 1024 / kRowBytes;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert(kBlocks % WAVES == 0, "each wave loads whole 1 KB blocks");
 };
 
-template <int D, int WAVES, int RB, int BN>
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Physical byte offset of 16-byte chunk `c` of key row `row` in a K/V buffer.
+// Chunks are XOR-swizzled by the row so that the 16 rows read by one MFMA
+// operand fetch hit distinct LDS banks.
+template <int CPR>
+__device__ __forceinline__ int swz(int row, int c) {
+  return row * (CPR * 16) + ((c ^ (row % CPR)) << 4);
+}
+
+// Issue this wave's direct-to-LDS loads of one K/V chunk: key rows
+// kv_row0 .. kv_row0 + BN - 1 of the head (rows past `nvalid` repeat the last
+// valid row; their scores are masked). Each instruction fills one 1 KB block.
+template <class C>
+__device__ __forceinline__ void load_chunk(const bf16_t* kg, const bf16_t* vg, int kv_row0,
+                                           int nvalid, char* kbuf, char* vbuf, int wave, int lane) {
+#pragma unroll
+  for (int b = 0; b < C::kBlocksPerWave; ++b) {
+    const int blk = wave * C::kBlocksPerWave + b;
+    const int row = blk * C::kRowsPerBlock + lane / C::kCPR;
+    const int pos = lane % C::kCPR;
+    const int c = pos ^ (row % C::kCPR);
+    const int src_row = kv_row0 + min(row, nvalid - 1);
+    const long long off = (long long)src_row * (C::kRowBytes / 2) + c * 8;
+    __builtin_amdgcn_global_load_lds(kg + off, (lds_void*)(kbuf + blk * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vg + off, (lds_void*)(vbuf + blk * 1024), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vm_all() {
+  // vmcnt(0); expcnt and lgkmcnt left at their maxima (not waited on).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+template <int D, int WAVES, int RB, int BN, bool DENSE>
 __global__ void __launch_bounds__(WAVES * 64)
 attn_bf16_kernel(const AttnParams p) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
-  __shared__ bf16_t ks[BN * C::kKPitch];
-  __shared__ bf16_t vt[D * C::kVPitch];
+  // Two buffers, each K then V of one chunk. They are separate objects and the
+  // loop below selects them statically, so the compiler can tell the chunk
+  // being read apart from the one the LDS DMA is filling and does not wait
+  // for the prefetch before reading.
+  __shared__ __attribute__((aligned(1024))) char smem0[2 * C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char smem1[2 * C::kChunkBytes];
 
   const int task = logical_task(p);
   if (task >= p.n_tasks) return;
-  const Task t = decode_task<C::kRows>(p, task, D);
+  Task t = decode_task<C::kRows>(p, task, D);
+  if (DENSE) {
+    t.kv.runs = 1;
+    t.kv.run_len = p.S;
+  }
   const bf16_t* qg = static_cast<const bf16_t*>(p.q) + t.head_base;
   const bf16_t* kg = static_cast<const bf16_t*>(p.k) + t.head_base;
   const bf16_t* vg = static_cast<const bf16_t*>(p.v) + t.head_base;
@@ -159,9 +206,26 @@ attn_bf16_kernel(const AttnParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int g = lane >> 4;
+
+  const int chunks_per_run = (t.kv.run_len + BN - 1) / BN;
+  const int n_chunks = t.kv.runs * chunks_per_run;
+
+  // Chunk `it` covers keys run_start(run) + c0 .. + BN of the head.
+  auto chunk_rows = [&](int it, int* row0, int* nvalid) {
+    const int run = it / chunks_per_run;
+    const int c0 = (it - run * chunks_per_run) * BN;
+    *row0 = (DENSE ? 0 : t.kv.run_start(run)) + c0;
+    *nvalid = min(BN, t.kv.run_len - c0);
+  };
+
+  {
+    int row0, nv;
+    chunk_rows(0, &row0, &nv);
+    load_chunk<C>(kg, vg, row0, nv, smem0, smem0 + C::kChunkBytes, wave, lane);
+  }
 
   // Q rows of this lane: row (within the work item) wave*kRowsWave + 16*rb + l16.
   bf16x8 qf[RB][C::kDK];
@@ -188,108 +252,135 @@ attn_bf16_kernel(const AttnParams p) {
     for (int db = 0; db < C::kDB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int run = 0; run < t.kv.runs; ++run) {
-    const int kv0 = t.kv.run_start(run);
-    for (int c0 = 0; c0 < t.kv.run_len; c0 += BN) {
-      const int nvalid = min(BN, t.kv.run_len - c0);
-      __syncthreads();  // the previous chunk is no longer read
-      // Stage K (row-major) and V (transposed) for keys kv0+c0 .. +BN.
-#pragma unroll
-      for (int i = tid; i < C::kPieces; i += C::kThreads) {
-        const int key = i / (D / 8);
-        const int col = (i % (D / 8)) * 8;
-        bf16x8 kx = bf16x8{}, vx = bf16x8{};
-        if (key < nvalid) {
-          const long long off = (long long)(kv0 + c0 + key) * D + col;
-          kx = *reinterpret_cast<const bf16x8*>(kg + off);
-          vx = *reinterpret_cast<const bf16x8*>(vg + off);
-        }
-        *reinterpret_cast<bf16x8*>(&ks[key * C::kKPitch + col]) = kx;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vt[(col + e) * C::kVPitch + key] = vx[e];
-      }
-      __syncthreads();
+  // One chunk: wait for its K/V, start the next chunk's loads into the other
+  // buffer, then compute.
+  auto chunk_step = [&](const char* cur, char* nxt, int it) __attribute__((always_inline)) {
+    int nvalid;
+    {
+      int row0;
+      chunk_rows(it, &row0, &nvalid);
+    }
+    wait_vm_all();     // this wave's loads of chunk `it` have landed in LDS
+    __syncthreads();   // ... and every wave's; chunk it-1's buffer is free
+    if (it + 1 < n_chunks) {
+      int row0, nv;
+      chunk_rows(it + 1, &row0, &nv);
+      load_chunk<C>(kg, vg, row0, nv, nxt, nxt + C::kChunkBytes, wave, lane);
+    }
+    const char* kbuf = cur;
+    const char* vbuf = cur + C::kChunkBytes;
 
-      // Scores S^T[key][row] for the wave's rows; lane holds keys 16*kt+4g+r of row l16.
-      f32x4 s[RB][C::kKT];
+    // Scores S^T[key][row] for the wave's rows; lane holds keys 16*kt+4g+r of row l16.
+    f32x4 s[RB][C::kKT];
+#pragma unroll
+    for (int kt = 0; kt < C::kKT; ++kt) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) s[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int krow = 16 * kt + l16;
+#pragma unroll
+      for (int dk = 0; dk < C::kDK; ++dk) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(kbuf + swz<C::kCPR>(krow, 4 * dk + g));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          s[rb][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][dk], s[rb][kt], 0, 0, 0);
+      }
+    }
+    if (nvalid < BN) {
+#pragma unroll
+      for (int kt = 0; kt < C::kKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * kt + 4 * g + r >= nvalid)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) s[rb][kt][r] = -INFINITY;
+    }
+
+    // Online softmax, base 2. The reference max m only moves when a row's
+    // chunk max exceeds it by more than 8 (then O and l are rescaled); in
+    // between, probabilities stay below 2^8, which fp32 sums and bf16 P hold
+    // exactly as well as values below 1.
+    float mx[RB];
+    bool grow = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float a = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < C::kKT; ++kt)
+        a = fmaxf(a, fmaxf(fmaxf(s[rb][kt][0], s[rb][kt][1]), fmaxf(s[rb][kt][2], s[rb][kt][3])));
+      a = wave_xor_max(a, 16);
+      a = wave_xor_max(a, 32);
+      mx[rb] = a * p.scale_log2;
+      grow |= mx[rb] > m[rb] + 8.0f;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float m_new = fmaxf(m[rb], mx[rb]);
+        const float alpha = __builtin_amdgcn_exp2f(m[rb] - m_new);
+        m[rb] = m_new;
+        lsum[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db) o[rb][db] *= alpha;
+      }
+    }
+    bf16x8 pf[RB][C::kKP];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float ls = 0.f;
 #pragma unroll
       for (int kt = 0; kt < C::kKT; ++kt) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int dk = 0; dk < C::kDK; ++dk) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(&ks[(16 * kt + l16) * C::kKPitch + 32 * dk + 8 * g]);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            s[rb][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][dk], s[rb][kt], 0, 0, 0);
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -m[rb]));
+          ls += e;
+          s[rb][kt][r] = e;
         }
       }
-      if (nvalid < BN) {
-#pragma unroll
-        for (int kt = 0; kt < C::kKT; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (16 * kt + 4 * g + r >= nvalid)
-#pragma unroll
-              for (int rb = 0; rb < RB; ++rb) s[rb][kt][r] = -INFINITY;
-      }
-
-      // Online softmax (base 2) and P in bf16 as the B operand of O^T += V^T P^T.
-      bf16x8 pf[RB][C::kKP];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < C::kKT; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[rb][kt][r]);
-        mx = wave_xor_max(mx, 16);
-        mx = wave_xor_max(mx, 32);
-        const float m_new = fmaxf(m[rb], mx * p.scale_log2);
-        const float alpha = __builtin_amdgcn_exp2f(m[rb] - m_new);
-        m[rb] = m_new;
-        float ls = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < C::kKT; ++kt) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = __builtin_amdgcn_exp2f(s[rb][kt][r] * p.scale_log2 - m_new);
-            ls += e;
-            s[rb][kt][r] = e;
-          }
-        }
-        lsum[rb] = lsum[rb] * alpha + ls;
-#pragma unroll
-        for (int db = 0; db < C::kDB; ++db) o[rb][db] *= alpha;
-#pragma unroll
-        for (int kp = 0; kp < C::kKP; ++kp) {
-          bf16x8 x;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            x[r] = static_cast<bf16_t>(s[rb][2 * kp][r]);
-            x[4 + r] = static_cast<bf16_t>(s[rb][2 * kp + 1][r]);
-          }
-          pf[rb][kp] = x;
-        }
-      }
-
-      // O^T[d][row] += V^T[d][key] P^T[key][row]. Slot j of lane group g maps
-      // to key 32*kp + 4g + j (j < 4) or 32*kp + 16 + 4g + (j - 4).
+      lsum[rb] += ls;
 #pragma unroll
       for (int kp = 0; kp < C::kKP; ++kp) {
+        bf16x8 x;
 #pragma unroll
-        for (int db = 0; db < C::kDB; ++db) {
-          const bf16_t* vrow = &vt[(16 * db + l16) * C::kVPitch + 32 * kp + 4 * g];
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 16);
-          const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb][kp], o[rb][db], 0, 0, 0);
+        for (int r = 0; r < 4; ++r) {
+          x[r] = static_cast<bf16_t>(s[rb][2 * kp][r]);
+          x[4 + r] = static_cast<bf16_t>(s[rb][2 * kp + 1][r]);
         }
+        pf[rb][kp] = x;
       }
     }
+
+    // O^T[d][row] += V^T[d][key] P^T[key][row]. Slot j of lane group g maps
+    // to key 32*kp + 4g + j (j < 4) or 32*kp + 16 + 4g + (j - 4). The
+    // transposing LDS read gives lane i of a 16-lane group element (i % 4) of
+    // the 4-element piece addressed by lane 4r + i/4, for r = 0..3: lane s of
+    // group g addresses key 32*kp + 4g + s/4, columns 16*db + 4*(s%4) .. +4,
+    // so lane i receives V[32*kp + 4g + r][16*db + i], r = 0..3.
+    const int s4 = l16 >> 2, sq = l16 & 3;
+#pragma unroll
+    for (int kp = 0; kp < C::kKP; ++kp) {
+      const int vrow_lo = 32 * kp + 4 * g + s4;
+      const int vrow_hi = vrow_lo + 16;
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) {
+        const int col = 16 * db + 4 * sq;  // element column of this lane's piece
+        const int c = col >> 3, half = (col & 7) * 2;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vbuf + swz<C::kCPR>(vrow_lo, c) + half));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vbuf + swz<C::kCPR>(vrow_hi, c) + half));
+        const i16x4 both[2] = {lo, hi};
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(both);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb][kp], o[rb][db], 0, 0, 0);
+      }
+    }
+  };
+
+  for (int it = 0; it < n_chunks; it += 2) {
+    chunk_step(smem0, smem1, it);
+    if (it + 1 < n_chunks) chunk_step(smem1, smem0, it + 1);
   }
 
   // Normalise and store: lane holds O[row l16][16*db + 4g + r].
@@ -440,8 +531,12 @@ int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
   AttnParams p;
   fill_params(pr, C::kRows, &p);
   const unsigned grid = (unsigned)p.per_xcd * kXcds;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN>), dim3(grid), dim3(C::kThreads), 0,
-                     stream, p);
+  if (pr.dense)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true>), dim3(grid), dim3(C::kThreads),
+                       0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false>), dim3(grid), dim3(C::kThreads),
+                       0, stream, p);
   return (int)hipGetLastError();
 }
 
