@@ -99,6 +99,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="sta_30x48x80_w18x24x24")
     ap.add_argument("--dense-reps", type=int, default=2, help="dense comparator launches to time (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="run one plain device copy of a q-sized tensor first (counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -138,6 +140,9 @@ def main(argv=None):
         if timers is not None:
             timers[3].record(stream)
 
+    if args.copy_reference:
+        out.copy_(q)  # a plain copy kernel: reads and writes exactly one tensor
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

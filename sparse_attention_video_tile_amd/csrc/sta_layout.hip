@@ -1,11 +1,11 @@
 // Token-order and tile-list kernels of libsta (gfx950).
 //
 // reorder_kernel: raster <-> tile-major permutation of the token axis. A
-// wavefront moves one tile of one (batch, head). The tile is c_t * c_h runs;
-// a run is the c_w tokens that share (t, y), contiguous in both orders
-// (c_w * row_bytes bytes), so each is copied with 16-byte loads and stores that
-// are coalesced on both sides. Loads of several runs are issued before their
-// stores to keep enough bytes in flight for HBM.
+// wavefront moves one tile of one (batch, head): it walks the tile's
+// contiguous tile-major range in 1 KB steps (16 bytes per lane). Each 16-byte
+// chunk lies in one run, the c_w tokens that share (t, y), which is also
+// contiguous in raster order, so both sides are coalesced. Eight chunks per
+// lane are loaded before any is stored, to keep enough bytes in flight.
 //
 // kv_tiles_kernel: one thread per (head, query tile, list slot) writes the
 // slot's key tile, walking the window box in (t, h, w) lexicographic order,
@@ -17,22 +17,47 @@
 namespace sta {
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kReorderThreads = 256;
-constexpr int kRunsInFlight = 4;   // runs whose loads are issued before their stores
-constexpr int kChunksPerLane = 2;  // 16-byte chunks per lane per run and pass
+constexpr int kUnroll = 8;  // 16-byte chunks per lane whose loads are in flight together
+
+// Unsigned division by a divisor fixed for the whole launch, as a multiply
+// and shift (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): for n < 2^31, n / d = (umulhi(n, m) + n) >> s with
+// s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1.
+struct FastDiv {
+  uint32_t d, m, s;
+  static FastDiv make(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    f.s = 0;
+    while ((1ull << f.s) < d) ++f.s;
+    f.m = (uint32_t)(((1ull << 32) * ((1ull << f.s) - d)) / d + 1);
+    return f;
+  }
+  __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    return (__umulhi(n, m) + n) >> s;
+  }
+};
 
 struct ReorderParams {
-  const uint4* __restrict__ src;
-  uint4* __restrict__ dst;
-  long long tasks;  // BH * n_tiles: one (head, tile) per wavefront
-  int row_chunks;   // 16-byte chunks per token row
-  int run_chunks;   // row_chunks * cw: one contiguous run
+  const u32x4* src;
+  u32x4* dst;
+  long long tasks;   // BH * n_tiles: one (head, tile) per wavefront
+  int tile_chunks;   // tau * row_chunks: 16-byte chunks in one tile
+  int row_chunks;    // 16-byte chunks per token row
   int S, H, W;
   int ct, ch, cw, nh, nw, n_tiles, tau;
+  FastDiv run_div;   // by row_chunks * cw: chunk -> run
+  FastDiv ch_div;    // by ch: run -> (lt, lh)
+  int run_chunks;
   int to_tiles;
 };
 
-// One wavefront moves one tile of one (batch, head): ct * ch runs of cw rows.
+// One wavefront moves one tile of one (batch, head). Chunk e of the tile in
+// tile-major order (contiguous) belongs to run e / run_chunks; a run is the
+// cw tokens that share (t, y), contiguous in raster order too.
 __global__ void __launch_bounds__(kReorderThreads) reorder_kernel(const ReorderParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -43,37 +68,45 @@ __global__ void __launch_bounds__(kReorderThreads) reorder_kernel(const ReorderP
   const int iw = tile % p.nw;
   const int ih = (tile / p.nw) % p.nh;
   const int it = tile / (p.nw * p.nh);
-  const long long head_row = bh * p.S;
-  const long long raster0 = head_row + ((long long)it * p.ct * p.H + ih * p.ch) * p.W + iw * p.cw;
-  const long long tiled0 = head_row + (long long)tile * p.tau;
-  const int runs = p.ct * p.ch;
-  for (int c0 = 0; c0 < p.run_chunks; c0 += 64 * kChunksPerLane) {
-    for (int r0 = 0; r0 < runs; r0 += kRunsInFlight) {
-      uint4 buf[kRunsInFlight][kChunksPerLane];
-      long long dst_off[kRunsInFlight];
+  const long long head_chunk = bh * p.S * (long long)p.row_chunks;
+  // Raster chunk offset of the tile's first run, and per-(lt, lh) strides.
+  const long long raster0 =
+      head_chunk + (((long long)it * p.ct * p.H + ih * p.ch) * p.W + iw * p.cw) * p.row_chunks;
+  const long long tiled0 = head_chunk + (long long)tile * p.tile_chunks;
+  const long long lt_stride = (long long)p.H * p.W * p.row_chunks;
+  const long long lh_stride = (long long)p.W * p.row_chunks;
+
+  auto raster_of = [&](int e) -> long long {
+    const uint32_t run = p.run_div.div((uint32_t)e);
+    const int c = e - (int)run * p.run_chunks;
+    const uint32_t lt = p.ch_div.div(run);
+    const int lh = (int)run - (int)lt * p.ch;
+    return raster0 + lt * lt_stride + lh * lh_stride + c;
+  };
+
+  const u32x4* __restrict__ src = p.src;
+  u32x4* __restrict__ dst = p.dst;
+  int e0 = 0;
+  for (; e0 + 64 * kUnroll <= p.tile_chunks; e0 += 64 * kUnroll) {
+    u32x4 buf[kUnroll];
+    long long soff[kUnroll], doff[kUnroll];
 #pragma unroll
-      for (int i = 0; i < kRunsInFlight; ++i) {
-        const int run = r0 + i;
-        const int lt = run / p.ch, lh = run % p.ch;
-        const long long raster_row = raster0 + ((long long)lt * p.H + lh) * p.W;
-        const long long tiled_row = tiled0 + (long long)run * p.cw;
-        const long long src_row = p.to_tiles ? raster_row : tiled_row;
-        dst_off[i] = (p.to_tiles ? tiled_row : raster_row) * p.row_chunks;
-#pragma unroll
-        for (int j = 0; j < kChunksPerLane; ++j) {
-          const int c = c0 + lane + 64 * j;
-          if (run < runs && c < p.run_chunks) buf[i][j] = p.src[src_row * p.row_chunks + c];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kRunsInFlight; ++i) {
-#pragma unroll
-        for (int j = 0; j < kChunksPerLane; ++j) {
-          const int c = c0 + lane + 64 * j;
-          if (r0 + i < runs && c < p.run_chunks) p.dst[dst_off[i] + c] = buf[i][j];
-        }
-      }
+    for (int u = 0; u < kUnroll; ++u) {
+      const int e = e0 + 64 * u + lane;
+      const long long r = raster_of(e);
+      soff[u] = p.to_tiles ? r : tiled0 + e;
+      doff[u] = p.to_tiles ? tiled0 + e : r;
     }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) buf[u] = src[soff[u]];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) dst[doff[u]] = buf[u];
+  }
+  for (int e = e0 + lane; e < p.tile_chunks; e += 64) {
+    const long long r = raster_of(e);
+    const long long so = p.to_tiles ? r : tiled0 + e;
+    const long long d = p.to_tiles ? tiled0 + e : r;
+    dst[d] = src[so];
   }
 }
 
@@ -116,17 +149,22 @@ __global__ void __launch_bounds__(256) kv_tiles_kernel(const KvTilesParams p) {
 int launch_reorder(const void* src, void* dst, int BH, int row_bytes, const Geometry& g,
                    bool to_tiles, void* stream) {
   ReorderParams p;
-  p.src = static_cast<const uint4*>(src);
-  p.dst = static_cast<uint4*>(dst);
+  p.src = static_cast<const u32x4*>(src);
+  p.dst = static_cast<u32x4*>(dst);
   p.tasks = (long long)BH * g.n_tiles;
   p.row_chunks = row_bytes / 16;
+  p.tile_chunks = g.tau * p.row_chunks;
   p.run_chunks = p.row_chunks * g.cw;
   p.S = g.S; p.H = g.H; p.W = g.W;
   p.ct = g.ct; p.ch = g.ch; p.cw = g.cw; p.nh = g.nh; p.nw = g.nw;
   p.n_tiles = g.n_tiles; p.tau = g.tau;
+  p.run_div = FastDiv::make((uint32_t)p.run_chunks);
+  p.ch_div = FastDiv::make((uint32_t)g.ch);
   p.to_tiles = to_tiles ? 1 : 0;
+  if ((long long)p.tile_chunks >= (1LL << 31)) return (int)hipErrorInvalidValue;
   const long long waves_per_block = kReorderThreads / 64;
   const long long blocks = (p.tasks + waves_per_block - 1) / waves_per_block;
+  if (blocks > 0x7fffffffLL) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(reorder_kernel, dim3((unsigned)blocks), dim3(kReorderThreads), 0,
                      static_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
