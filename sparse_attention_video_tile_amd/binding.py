@@ -41,11 +41,17 @@ class StaError(RuntimeError):
     """A HIP runtime error reported by libsta."""
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libsta.so once and declare the C signatures."""
+def load_library(path: str = None) -> ctypes.CDLL:
+    """Load libsta.so once and declare the C signatures.
+
+    The default is the in-tree build; the STA_LIBRARY environment variable
+    may name another build of the same library (e.g. a variant under test).
+    """
     global _lib
     if _lib is not None:
         return _lib
+    if path is None:
+        path = os.environ.get("STA_LIBRARY", LIB_PATH)
     if not os.path.exists(path):
         raise RuntimeError(
             f"libsta.so not found at {path}; build it with "

@@ -30,6 +30,7 @@ namespace {
 typedef __bf16 bf16_t;
 typedef bf16_t bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16_t bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16_t bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -116,9 +117,22 @@ __device__ __forceinline__ Task decode_task(const AttnParams& p, int task, int D
   return t;
 }
 
-__device__ __forceinline__ float wave_xor_max(float x, int mask) {
-  return fmaxf(x, __shfl_xor(x, mask, 64));
+// Max / sum of x over the four lanes l, l^16, l^32, l^48 (the lanes that
+// hold one query row in the MFMA output layouts). A permlane swap of x with
+// itself yields, in its two results, x of this lane and of its partner lane
+// (l^16 for the 16-lane swap, l^32 for the 32-lane swap), in some order.
+__device__ __forceinline__ float pair16(float x, bool is_max) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return is_max ? fmaxf(a, b) : a + b;
 }
+__device__ __forceinline__ float pair32(float x, bool is_max) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return is_max ? fmaxf(a, b) : a + b;
+}
+__device__ __forceinline__ float row_max4(float x) { return pair32(pair16(x, true), true); }
+__device__ __forceinline__ float row_sum4(float x) { return pair32(pair16(x, false), false); }
 __device__ __forceinline__ float wave_xor_sum(float x, int mask) {
   return x + __shfl_xor(x, mask, 64);
 }
@@ -129,6 +143,8 @@ __device__ __forceinline__ float wave_xor_sum(float x, int mask) {
 
 template <int D, int WAVES, int RB, int BN>
 struct Bf16Cfg {
+  static constexpr int kD = D;
+  static constexpr int kBN = BN;
   static constexpr int kThreads = WAVES * 64;
   static constexpr int kRowsWave = 16 * RB;
   static constexpr int kRows = WAVES * kRowsWave;
@@ -140,39 +156,50 @@ struct Bf16Cfg {
   static constexpr int kCPR = kRowBytes / 16;   // 16-byte chunks per row
   static constexpr int kChunkBytes = BN * kRowBytes;       // K (or V) of one chunk
   static constexpr int kBlocks = kChunkBytes / 1024;       // 1 KB LDS-DMA blocks per chunk
-  static constexpr int kBlocksPerWave = kBlocks / WAVES;
   static constexpr int kRowsPerBlock = 1024 / kRowBytes;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert(kBlocks % WAVES == 0, "each wave loads whole 1 KB blocks");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // Physical byte offset of 16-byte chunk `c` of key row `row` in a K/V buffer.
-// Chunks are XOR-swizzled by the row so that the 16 rows read by one MFMA
-// operand fetch hit distinct LDS banks.
+// Chunks are XOR-swizzled by the row so that the operand fetches of the MFMA
+// loops hit distinct LDS banks: with 256-byte rows every row starts at bank 0
+// and the chunk slot is c ^ rotl4(row % 16). The K fetch reads one chunk of
+// 16 consecutive rows (rotl4 is a bijection on 0..15); the transposing V
+// fetch reads chunks 2m and 2m+1 of 8 consecutive rows, which rotl4 also
+// spreads over 16 distinct slots. With 128-byte rows the slot is c ^ (row % 8).
 template <int CPR>
 __device__ __forceinline__ int swz(int row, int c) {
-  return row * (CPR * 16) + ((c ^ (row % CPR)) << 4);
+  int key;
+  if (CPR == 16) {
+    const int r = row & 15;
+    key = ((r << 1) | (r >> 3)) & 15;
+  } else {
+    key = row % CPR;
+  }
+  return row * (CPR * 16) + ((c ^ key) << 4);
 }
 
-// Issue this wave's direct-to-LDS loads of one K/V chunk: key rows
-// kv_row0 .. kv_row0 + BN - 1 of the head (rows past `nvalid` repeat the last
-// valid row; their scores are masked). Each instruction fills one 1 KB block.
-template <class C>
-__device__ __forceinline__ void load_chunk(const bf16_t* kg, const bf16_t* vg, int kv_row0,
-                                           int nvalid, char* kbuf, char* vbuf, int wave, int lane) {
+// Issue this wave's share of the direct-to-LDS loads of one K (or V) chunk:
+// key rows kv_row0 .. kv_row0 + BN - 1 of the head (rows past `nvalid` repeat
+// the last valid row; their scores are masked). Each instruction fills one
+// 1 KB block; WAVES wavefronts share the chunk.
+template <class C, int WAVES>
+__device__ __forceinline__ void load_rows(const bf16_t* src, int kv_row0, int nvalid, char* buf,
+                                          int wave, int lane) {
+  constexpr int kIter = (C::kBlocks + WAVES - 1) / WAVES;
 #pragma unroll
-  for (int b = 0; b < C::kBlocksPerWave; ++b) {
-    const int blk = wave * C::kBlocksPerWave + b;
+  for (int b = 0; b < kIter; ++b) {
+    const int blk = wave + WAVES * b;
+    if (kIter * WAVES != C::kBlocks && blk >= C::kBlocks) break;  // wave-uniform
     const int row = blk * C::kRowsPerBlock + lane / C::kCPR;
-    const int pos = lane % C::kCPR;
-    const int c = pos ^ (row % C::kCPR);
+    const int pos = lane % C::kCPR;                      // slot this lane fills
+    const int c = pos ^ ((swz<C::kCPR>(row, 0) >> 4) & (C::kCPR - 1));  // chunk it holds
     const int src_row = kv_row0 + min(row, nvalid - 1);
     const long long off = (long long)src_row * (C::kRowBytes / 2) + c * 8;
-    __builtin_amdgcn_global_load_lds(kg + off, (lds_void*)(kbuf + blk * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vg + off, (lds_void*)(vbuf + blk * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src + off, (lds_void*)(buf + blk * 1024), 16, 0, 0);
   }
 }
 
@@ -181,227 +208,378 @@ __device__ __forceinline__ void wait_vm_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// Rare branches (a ragged last chunk, a growing row max) hold code the
+// compiler would otherwise turn into unconditional selects and multiplies on
+// every chunk; an empty volatile asm statement keeps them real branches.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
+// Per-wave state of the flash loop: Q fragments, O^T accumulators, running
+// max m (log2 units) and partial row sums, the current scores and the bf16
+// probabilities, and the lane's byte offsets into a K/V buffer.
+template <class C, int RB>
+struct WaveState {
+  bf16x8 qf[RB][C::kDK];
+  f32x4 o[RB][C::kDB];
+  float m[RB], lsum[RB];
+  f32x4 s[RB][C::kKT];
+  bf16x8 pf[RB][C::kKP];
+  // K operand: row 16*kt + l16, chunk 4*dk + g; the swizzled offset is
+  // koff[dk] + 16*kt*row_bytes because the row's low 4 bits are l16.
+  int koff[C::kDK];
+  // V operand (transposing read): row 32*kp + 4g + l16/4 (+16 for the upper
+  // half), element column 16*db + 4*(l16 % 4); offset voff[db] + rows*row_bytes.
+  int voff[C::kDB];
+};
+
+template <class C, int RB>
+__device__ __forceinline__ void lane_offsets(WaveState<C, RB>& w, int l16, int g) {
+#pragma unroll
+  for (int dk = 0; dk < C::kDK; ++dk) w.koff[dk] = swz<C::kCPR>(l16, 4 * dk + g);
+  const int s4 = l16 >> 2, sq = l16 & 3;
+  const int vrow = 4 * g + s4;  // row within its 16-row group (< 16)
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db) {
+    const int col = 16 * db + 4 * sq;
+    w.voff[db] = swz<C::kCPR>(vrow, col >> 3) + (col & 7) * 2;
+  }
+}
+
+// Scores S^T[key][row] = K Q^T for one chunk; lane (l16, g) ends up with keys
+// 16*kt + 4g + r of query row l16 of each 16-row block.
+template <class C, int RB>
+__device__ __forceinline__ void qk_chunk(WaveState<C, RB>& w, const char* kbuf, int l16, int g) {
+#pragma unroll
+  for (int kt = 0; kt < C::kKT; ++kt) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) w.s[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dk = 0; dk < C::kDK; ++dk) {
+      const bf16x8 kf =
+          *reinterpret_cast<const bf16x8*>(kbuf + w.koff[dk] + 16 * kt * C::kRowBytes);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        w.s[rb][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, w.qf[rb][dk], w.s[rb][kt], 0, 0, 0);
+    }
+  }
+}
+
+// Online softmax (base 2) of one chunk's scores into bf16 probabilities. The
+// reference max m only moves when a row's chunk max exceeds it by more than 8
+// (then O and the row sum are rescaled); in between, probabilities stay below
+// 2^8, which fp32 sums and bf16 P hold as well as values below 1.
+template <class C, int RB>
+__device__ __forceinline__ void softmax_chunk(WaveState<C, RB>& w, int nvalid, float scale_log2,
+                                              int g) {
+  if (nvalid < C::kBN) {
+    keep_branch();
+#pragma unroll
+    for (int kt = 0; kt < C::kKT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (16 * kt + 4 * g + r >= nvalid)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) w.s[rb][kt][r] = -INFINITY;
+  }
+  float mx[RB];
+  bool grow = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float a = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < C::kKT; ++kt)
+      a = fmaxf(a, fmaxf(fmaxf(w.s[rb][kt][0], w.s[rb][kt][1]), fmaxf(w.s[rb][kt][2], w.s[rb][kt][3])));
+    mx[rb] = row_max4(a) * scale_log2;
+    grow |= mx[rb] > w.m[rb] + 8.0f;
+  }
+  if (__any(grow)) {
+    keep_branch();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float m_new = fmaxf(w.m[rb], mx[rb]);
+      const float alpha = __builtin_amdgcn_exp2f(w.m[rb] - m_new);
+      w.m[rb] = m_new;
+      w.lsum[rb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) w.o[rb][db] *= alpha;
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int kt = 0; kt < C::kKT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        w.s[rb][kt][r] = __builtin_amdgcn_exp2f(fmaf(w.s[rb][kt][r], scale_log2, -w.m[rb]));
+    // The row sum adds the bf16-rounded probabilities, the same values that
+    // multiply V, two per dot instruction.
+    float ls = w.lsum[rb];
+    const bf16x2 ones = {static_cast<bf16_t>(1.0f), static_cast<bf16_t>(1.0f)};
+#pragma unroll
+    for (int kp = 0; kp < C::kKP; ++kp) {
+      bf16x8 x;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[r] = static_cast<bf16_t>(w.s[rb][2 * kp][r]);
+        x[4 + r] = static_cast<bf16_t>(w.s[rb][2 * kp + 1][r]);
+      }
+      w.pf[rb][kp] = x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {x[2 * e], x[2 * e + 1]};
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);
+      }
+    }
+    w.lsum[rb] = ls;
+  }
+}
+
+// O^T[d][row] += V^T[d][key] P^T[key][row] for one chunk. Slot j of lane group
+// g maps to key 32*kp + 4g + j (j < 4) or 32*kp + 16 + 4g + (j - 4). The
+// transposing LDS read gives lane i of a 16-lane group element (i % 4) of the
+// 4-element piece addressed by lane 4r + i/4, for r = 0..3: lane s of group g
+// addresses key 32*kp + 4g + s/4, columns 16*db + 4*(s%4) .. +4, so lane i
+// receives V[32*kp + 4g + r][16*db + i], r = 0..3.
+template <class C, int RB>
+__device__ __forceinline__ void pv_chunk(WaveState<C, RB>& w, const char* vbuf, int l16, int g) {
+#pragma unroll
+  for (int kp = 0; kp < C::kKP; ++kp) {
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) {
+      const char* lo_addr = vbuf + w.voff[db] + 32 * kp * C::kRowBytes;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(lo_addr));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(lo_addr + 16 * C::kRowBytes));
+      const i16x4 both[2] = {lo, hi};
+      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(both);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        w.o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, w.pf[rb][kp], w.o[rb][db], 0, 0, 0);
+    }
+  }
+}
+
+template <class C, int RB>
+__device__ __forceinline__ void load_q_init(WaveState<C, RB>& w, const bf16_t* qg, const Task& t,
+                                            int wave, int l16, int g) {
+  lane_offsets<C, RB>(w, l16, g);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = wave * C::kRowsWave + 16 * rb + l16;
+    const bool ok = r < t.valid_rows;
+    const bf16_t* src = qg + (long long)(t.row0 + (ok ? r : 0)) * C::kD + 8 * g;
+#pragma unroll
+    for (int dk = 0; dk < C::kDK; ++dk) {
+      bf16x8 x = *reinterpret_cast<const bf16x8*>(src + 32 * dk);
+      if (!ok) x = bf16x8{};
+      w.qf[rb][dk] = x;
+    }
+    w.m[rb] = -INFINITY;
+    w.lsum[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) w.o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Normalise and store: lane holds O[row l16][16*db + 4g + r].
+template <class C, int RB>
+__device__ __forceinline__ void store_out(WaveState<C, RB>& w, bf16_t* og, const Task& t, int wave,
+                                          int l16, int g) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float inv = 1.0f / row_sum4(w.lsum[rb]);
+    const int r = wave * C::kRowsWave + 16 * rb + l16;
+    if (r < t.valid_rows) {
+      bf16_t* dst = og + (long long)(t.row0 + r) * C::kD + 4 * g;
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) {
+        bf16x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = static_cast<bf16_t>(w.o[rb][db][e] * inv);
+        *reinterpret_cast<bf16x4*>(dst + 16 * db) = y;
+      }
+    }
+  }
+}
+
+// Walks the key chunks of a work item: chunk `it` covers keys
+// row0(it) .. + BN of the head, of which nvalid(it) are inside the run.
+struct ChunkWalk {
+  int chunks_per_run, n_chunks, run_len, bn;
+  KvRuns kv;
+  bool dense;
+  __device__ __forceinline__ void at(int it, int* row0, int* nvalid) const {
+    const int run = it / chunks_per_run;
+    const int c0 = (it - run * chunks_per_run) * bn;
+    *row0 = (dense ? 0 : kv.run_start(run)) + c0;
+    *nvalid = min(bn, run_len - c0);
+  }
+};
+
+template <int BN, bool DENSE>
+__device__ __forceinline__ ChunkWalk make_walk(const Task& t, int S) {
+  ChunkWalk cw;
+  cw.kv = t.kv;
+  cw.dense = DENSE;
+  cw.run_len = DENSE ? S : t.kv.run_len;
+  cw.bn = BN;
+  cw.chunks_per_run = (cw.run_len + BN - 1) / BN;
+  cw.n_chunks = (DENSE ? 1 : t.kv.runs) * cw.chunks_per_run;
+  return cw;
+}
+
+// Plain flash loop: every wave runs QK^T, softmax and PV of a chunk in turn;
+// the next chunk's K and V stream into the other LDS buffer meanwhile.
 template <int D, int WAVES, int RB, int BN, bool DENSE>
-__global__ void __launch_bounds__(WAVES * 64)
+__global__ void __launch_bounds__(WAVES * 64, (WAVES <= 4 ? 2 : 1))
 attn_bf16_kernel(const AttnParams p) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
-  // Two buffers, each K then V of one chunk. They are separate objects and the
-  // loop below selects them statically, so the compiler can tell the chunk
-  // being read apart from the one the LDS DMA is filling and does not wait
-  // for the prefetch before reading.
-  __shared__ __attribute__((aligned(1024))) char smem0[2 * C::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char smem1[2 * C::kChunkBytes];
+  // K and V buffers of two chunks. They are separate objects and the loop
+  // selects them statically, so the compiler can tell the chunk being read
+  // apart from the one the LDS DMA is filling and does not wait for the
+  // prefetch before reading.
+  __shared__ __attribute__((aligned(1024))) char kb0[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char vb0[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char kb1[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char vb1[C::kChunkBytes];
 
   const int task = logical_task(p);
   if (task >= p.n_tasks) return;
-  Task t = decode_task<C::kRows>(p, task, D);
-  if (DENSE) {
-    t.kv.runs = 1;
-    t.kv.run_len = p.S;
-  }
+  const Task t = decode_task<C::kRows>(p, task, D);
   const bf16_t* qg = static_cast<const bf16_t*>(p.q) + t.head_base;
   const bf16_t* kg = static_cast<const bf16_t*>(p.k) + t.head_base;
   const bf16_t* vg = static_cast<const bf16_t*>(p.v) + t.head_base;
   bf16_t* og = static_cast<bf16_t*>(p.out) + t.head_base;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15;
   const int g = lane >> 4;
+  const ChunkWalk walk = make_walk<BN, DENSE>(t, p.S);
+  {
+    int row0, nv;
+    walk.at(0, &row0, &nv);
+    load_rows<C, WAVES>(kg, row0, nv, kb0, wave, lane);
+    load_rows<C, WAVES>(vg, row0, nv, vb0, wave, lane);
+  }
+  WaveState<C, RB> w;
+  load_q_init<C, RB>(w, qg, t, wave, l16, g);
 
-  const int chunks_per_run = (t.kv.run_len + BN - 1) / BN;
-  const int n_chunks = t.kv.runs * chunks_per_run;
-
-  // Chunk `it` covers keys run_start(run) + c0 .. + BN of the head.
-  auto chunk_rows = [&](int it, int* row0, int* nvalid) {
-    const int run = it / chunks_per_run;
-    const int c0 = (it - run * chunks_per_run) * BN;
-    *row0 = (DENSE ? 0 : t.kv.run_start(run)) + c0;
-    *nvalid = min(BN, t.kv.run_len - c0);
+  auto chunk_step = [&](const char* kcur, const char* vcur, char* knxt, char* vnxt, int it)
+                        __attribute__((always_inline)) {
+    int row0, nvalid;
+    walk.at(it, &row0, &nvalid);
+    wait_vm_all();     // this wave's loads of chunk `it` have landed in LDS
+    __syncthreads();   // ... and every wave's; chunk it-1's buffers are free
+    if (it + 1 < walk.n_chunks) {
+      int r1, nv1;
+      walk.at(it + 1, &r1, &nv1);
+      load_rows<C, WAVES>(kg, r1, nv1, knxt, wave, lane);
+      load_rows<C, WAVES>(vg, r1, nv1, vnxt, wave, lane);
+    }
+    qk_chunk<C, RB>(w, kcur, l16, g);
+    softmax_chunk<C, RB>(w, nvalid, p.scale_log2, g);
+    pv_chunk<C, RB>(w, vcur, l16, g);
   };
+  for (int it = 0; it < walk.n_chunks; it += 2) {
+    chunk_step(kb0, vb0, kb1, vb1, it);
+    if (it + 1 < walk.n_chunks) chunk_step(kb1, vb1, kb0, vb0, it + 1);
+  }
+  store_out<C, RB>(w, og, t, wave, l16, g);
+}
+
+// Ping-pong flash loop (8 waves). The waves form two groups with one wave of
+// each on every SIMD. All waves run the same sequence per chunk j: an MFMA
+// phase M_j (PV of chunk j-1, then QK^T of chunk j), a barrier, a softmax
+// phase S_j (VALU), a barrier. Group 1 starts one barrier later than group 0,
+// so while one wave of a SIMD is in an MFMA phase its partner is in a softmax
+// phase: the matrix core and the VALU work at the same time.
+//
+// Barrier intervals are numbered 1, 2, ...; group 0 runs M_j in interval
+// 2j+1 and S_j in 2j+2, group 1 one interval later. K_j and V_{j-1} are read
+// in intervals 2j+1 and 2j+2. At the start of M_j, group 0 issues the DMA of
+// K_{j+1} and V_j (their buffers' previous chunks were last read in interval
+// 2j) and waits for it at the end of S_j, before the workgroup barrier that
+// precedes the first reads in interval 2j+3.
+template <int D, int RB, int BN, bool DENSE, int GROUPING>
+__global__ void __launch_bounds__(512)
+attn_bf16_pp_kernel(const AttnParams p) {
+  using C = Bf16Cfg<D, 8, RB, BN>;
+  __shared__ __attribute__((aligned(1024))) char kb0[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char kb1[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char vb0[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char vb1[C::kChunkBytes];
+
+  const int task = logical_task(p);
+  if (task >= p.n_tasks) return;
+  const Task t = decode_task<C::kRows>(p, task, D);
+  const bf16_t* qg = static_cast<const bf16_t*>(p.q) + t.head_base;
+  const bf16_t* kg = static_cast<const bf16_t*>(p.k) + t.head_base;
+  const bf16_t* vg = static_cast<const bf16_t*>(p.v) + t.head_base;
+  bf16_t* og = static_cast<bf16_t*>(p.out) + t.head_base;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  // Group 0 or 1; the two waves sharing a SIMD belong to different groups.
+  const int group = GROUPING == 0 ? (wave >> 2) : (wave & 1);
+  const int gwave = GROUPING == 0 ? (wave & 3) : (wave >> 1);  // index within the group
+  const ChunkWalk walk = make_walk<BN, DENSE>(t, p.S);
+  const int n = walk.n_chunks;
 
   {
     int row0, nv;
-    chunk_rows(0, &row0, &nv);
-    load_chunk<C>(kg, vg, row0, nv, smem0, smem0 + C::kChunkBytes, wave, lane);
+    walk.at(0, &row0, &nv);
+    load_rows<C, 8>(kg, row0, nv, kb0, wave, lane);
   }
+  WaveState<C, RB> w;
+  load_q_init<C, RB>(w, qg, t, wave, l16, g);
+  wait_vm_all();
+  __syncthreads();
+  if (group == 1) __builtin_amdgcn_s_barrier();  // interval 1 is group 0's M_0
 
-  // Q rows of this lane: row (within the work item) wave*kRowsWave + 16*rb + l16.
-  bf16x8 qf[RB][C::kDK];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = wave * C::kRowsWave + 16 * rb + l16;
-    const bool ok = r < t.valid_rows;
-    const bf16_t* src = qg + (long long)(t.row0 + (ok ? r : 0)) * D + 8 * g;
-#pragma unroll
-    for (int dk = 0; dk < C::kDK; ++dk) {
-      bf16x8 x = *reinterpret_cast<const bf16x8*>(src + 32 * dk);
-      if (!ok) x = bf16x8{};
-      qf[rb][dk] = x;
-    }
-  }
-
-  f32x4 o[RB][C::kDB];
-  float m[RB], lsum[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m[rb] = -INFINITY;
-    lsum[rb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < C::kDB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // One chunk: wait for its K/V, start the next chunk's loads into the other
-  // buffer, then compute.
-  auto chunk_step = [&](const char* cur, char* nxt, int it) __attribute__((always_inline)) {
-    int nvalid;
-    {
-      int row0;
-      chunk_rows(it, &row0, &nvalid);
-    }
-    wait_vm_all();     // this wave's loads of chunk `it` have landed in LDS
-    __syncthreads();   // ... and every wave's; chunk it-1's buffer is free
-    if (it + 1 < n_chunks) {
-      int row0, nv;
-      chunk_rows(it + 1, &row0, &nv);
-      load_chunk<C>(kg, vg, row0, nv, nxt, nxt + C::kChunkBytes, wave, lane);
-    }
-    const char* kbuf = cur;
-    const char* vbuf = cur + C::kChunkBytes;
-
-    // Scores S^T[key][row] for the wave's rows; lane holds keys 16*kt+4g+r of row l16.
-    f32x4 s[RB][C::kKT];
-#pragma unroll
-    for (int kt = 0; kt < C::kKT; ++kt) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) s[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int krow = 16 * kt + l16;
-#pragma unroll
-      for (int dk = 0; dk < C::kDK; ++dk) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(kbuf + swz<C::kCPR>(krow, 4 * dk + g));
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          s[rb][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rb][dk], s[rb][kt], 0, 0, 0);
+  // Chunk step j: kcur holds K_j, vprv holds V_{j-1}; group 0 loads K_{j+1}
+  // into knxt and V_j into vnew.
+  auto step = [&](int j, const char* kcur, const char* vprv, char* knxt, char* vnew)
+                  __attribute__((always_inline)) {
+    if (group == 0) {
+      if (j + 1 < n) {
+        int r, nv;
+        walk.at(j + 1, &r, &nv);
+        load_rows<C, 4>(kg, r, nv, knxt, gwave, lane);
+      }
+      if (j < n) {
+        int r, nv;
+        walk.at(j, &r, &nv);
+        load_rows<C, 4>(vg, r, nv, vnew, gwave, lane);
       }
     }
-    if (nvalid < BN) {
-#pragma unroll
-      for (int kt = 0; kt < C::kKT; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (16 * kt + 4 * g + r >= nvalid)
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) s[rb][kt][r] = -INFINITY;
+    if (j > 0) pv_chunk<C, RB>(w, vprv, l16, g);
+    if (j < n) qk_chunk<C, RB>(w, kcur, l16, g);
+    if (group == 0)
+      __builtin_amdgcn_s_barrier();
+    else
+      __syncthreads();
+    if (j < n) {
+      int r, nv;
+      walk.at(j, &r, &nv);
+      softmax_chunk<C, RB>(w, nv, p.scale_log2, g);
     }
-
-    // Online softmax, base 2. The reference max m only moves when a row's
-    // chunk max exceeds it by more than 8 (then O and l are rescaled); in
-    // between, probabilities stay below 2^8, which fp32 sums and bf16 P hold
-    // exactly as well as values below 1.
-    float mx[RB];
-    bool grow = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float a = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < C::kKT; ++kt)
-        a = fmaxf(a, fmaxf(fmaxf(s[rb][kt][0], s[rb][kt][1]), fmaxf(s[rb][kt][2], s[rb][kt][3])));
-      a = wave_xor_max(a, 16);
-      a = wave_xor_max(a, 32);
-      mx[rb] = a * p.scale_log2;
-      grow |= mx[rb] > m[rb] + 8.0f;
+    if (group == 0) {
+      wait_vm_all();  // this step's DMA has landed
+      __syncthreads();
+    } else {
+      __builtin_amdgcn_s_barrier();
     }
-    if (__any(grow)) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float m_new = fmaxf(m[rb], mx[rb]);
-        const float alpha = __builtin_amdgcn_exp2f(m[rb] - m_new);
-        m[rb] = m_new;
-        lsum[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::kDB; ++db) o[rb][db] *= alpha;
-      }
-    }
-    bf16x8 pf[RB][C::kKP];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float ls = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < C::kKT; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -m[rb]));
-          ls += e;
-          s[rb][kt][r] = e;
-        }
-      }
-      lsum[rb] += ls;
-#pragma unroll
-      for (int kp = 0; kp < C::kKP; ++kp) {
-        bf16x8 x;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[r] = static_cast<bf16_t>(s[rb][2 * kp][r]);
-          x[4 + r] = static_cast<bf16_t>(s[rb][2 * kp + 1][r]);
-        }
-        pf[rb][kp] = x;
-      }
-    }
-
-    // O^T[d][row] += V^T[d][key] P^T[key][row]. Slot j of lane group g maps
-    // to key 32*kp + 4g + j (j < 4) or 32*kp + 16 + 4g + (j - 4). The
-    // transposing LDS read gives lane i of a 16-lane group element (i % 4) of
-    // the 4-element piece addressed by lane 4r + i/4, for r = 0..3: lane s of
-    // group g addresses key 32*kp + 4g + s/4, columns 16*db + 4*(s%4) .. +4,
-    // so lane i receives V[32*kp + 4g + r][16*db + i], r = 0..3.
-    const int s4 = l16 >> 2, sq = l16 & 3;
-#pragma unroll
-    for (int kp = 0; kp < C::kKP; ++kp) {
-      const int vrow_lo = 32 * kp + 4 * g + s4;
-      const int vrow_hi = vrow_lo + 16;
-#pragma unroll
-      for (int db = 0; db < C::kDB; ++db) {
-        const int col = 16 * db + 4 * sq;  // element column of this lane's piece
-        const int c = col >> 3, half = (col & 7) * 2;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vbuf + swz<C::kCPR>(vrow_lo, c) + half));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vbuf + swz<C::kCPR>(vrow_hi, c) + half));
-        const i16x4 both[2] = {lo, hi};
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(both);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb][kp], o[rb][db], 0, 0, 0);
-      }
-    }
+    wait_vm_all();  // nothing is outstanding here; tells the compiler so
   };
-
-  for (int it = 0; it < n_chunks; it += 2) {
-    chunk_step(smem0, smem1, it);
-    if (it + 1 < n_chunks) chunk_step(smem1, smem0, it + 1);
+  for (int j = 0; j <= n; j += 2) {
+    step(j, kb0, vb1, kb1, vb0);
+    if (j + 1 <= n) step(j + 1, kb1, vb0, kb0, vb1);
   }
-
-  // Normalise and store: lane holds O[row l16][16*db + 4g + r].
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    float l = lsum[rb];
-    l = wave_xor_sum(l, 16);
-    l = wave_xor_sum(l, 32);
-    const float inv = 1.0f / l;
-    const int r = wave * C::kRowsWave + 16 * rb + l16;
-    if (r < t.valid_rows) {
-      bf16_t* dst = og + (long long)(t.row0 + r) * D + 4 * g;
-#pragma unroll
-      for (int db = 0; db < C::kDB; ++db) {
-        bf16x4 y;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = static_cast<bf16_t>(o[rb][db][e] * inv);
-        *reinterpret_cast<bf16x4*>(dst + 16 * db) = y;
-      }
-    }
-  }
+  if (group == 0) __builtin_amdgcn_s_barrier();
+  store_out<C, RB>(w, og, t, wave, l16, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -540,6 +718,25 @@ int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
   return (int)hipGetLastError();
 }
 
+// Ping-pong kernel for 384-row work items.
+#ifndef STA_PP_GROUPING
+#define STA_PP_GROUPING 0
+#endif
+template <int D, int RB, int BN>
+int launch_bf16_pp(const AttnProblem& pr, hipStream_t stream) {
+  using C = Bf16Cfg<D, 8, RB, BN>;
+  AttnParams p;
+  fill_params(pr, C::kRows, &p);
+  const unsigned grid = (unsigned)p.per_xcd * kXcds;
+  if (pr.dense)
+    hipLaunchKernelGGL((attn_bf16_pp_kernel<D, RB, BN, true, STA_PP_GROUPING>), dim3(grid),
+                       dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_bf16_pp_kernel<D, RB, BN, false, STA_PP_GROUPING>), dim3(grid),
+                       dim3(512), 0, stream, p);
+  return (int)hipGetLastError();
+}
+
 template <int D>
 int launch_f32(const AttnProblem& pr, hipStream_t stream) {
   AttnParams p;
@@ -553,7 +750,23 @@ int launch_f32(const AttnProblem& pr, hipStream_t stream) {
 template <int D>
 int dispatch_bf16(const AttnProblem& pr, hipStream_t stream) {
   const int unit_rows = pr.dense ? pr.g.S : pr.g.tau;
-  if (unit_rows % 384 == 0) return launch_bf16<D, 8, 3, 64>(pr, stream);
+#ifndef STA_ATTN_VARIANT
+#define STA_ATTN_VARIANT 0
+#endif
+#ifndef STA_CFG_WAVES
+#define STA_CFG_WAVES 8
+#endif
+#ifndef STA_CFG_RB
+#define STA_CFG_RB 3
+#endif
+#ifndef STA_CFG_BN
+#define STA_CFG_BN 64
+#endif
+  constexpr int kBigRows = STA_CFG_WAVES * 16 * STA_CFG_RB;
+  if (unit_rows % kBigRows == 0) {
+    if (STA_ATTN_VARIANT == 1) return launch_bf16_pp<D, 3, 64>(pr, stream);
+    return launch_bf16<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN>(pr, stream);
+  }
   if (unit_rows <= 64) return launch_bf16<D, 4, 1, 64>(pr, stream);
   return launch_bf16<D, 4, 2, 64>(pr, stream);
 }
