@@ -55,6 +55,30 @@ def gpu_inputs(w, torch):
     return [torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(dt) for _ in range(3)]
 
 
+KERNEL_SOURCES = (
+    "sparse_attention_video_tile_amd/csrc/sta_attention.hip",
+    "sparse_attention_video_tile_amd/csrc/sta_geometry.h",
+    "sparse_attention_video_tile_amd/csrc/sta_kernels.h",
+)
+
+
+def recorded_traffic(workload: str):
+    """HBM-side bytes per attention launch from the committed counter record
+    (profiles/), or None when there is none for this workload or the kernel
+    sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attn_bf16_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return float(rec["bytes_per_launch"])
+
+
 def cpu_baseline(w, budget_s: float):
     """Time the oracle on query tiles of one head until the budget is spent."""
     import oracle
@@ -213,7 +237,7 @@ def main(argv=None):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": attn_tflops / peak,
-            "traffic": None,
+            "traffic": recorded_traffic(w.name) if w.dtype == "bf16" else None,
             "launch_ms": attn_ms,
         },
         "cpu_baseline": cpu,

@@ -222,6 +222,7 @@ struct WaveState {
   f32x4 o[RB][C::kDB];
   float m[RB], lsum[RB];
   f32x4 s[RB][C::kKT];
+  f32x4 s2[RB][C::kKT];  // second score buffer of the software-pipelined loop
   bf16x8 pf[RB][C::kKP];
   // K operand: row 16*kt + l16, chunk 4*dk + g; the swizzled offset is
   // koff[dk] + 16*kt*row_bytes because the row's low 4 bits are l16.
@@ -247,29 +248,31 @@ __device__ __forceinline__ void lane_offsets(WaveState<C, RB>& w, int l16, int g
 // Scores S^T[key][row] = K Q^T for one chunk; lane (l16, g) ends up with keys
 // 16*kt + 4g + r of query row l16 of each 16-row block.
 template <class C, int RB>
-__device__ __forceinline__ void qk_chunk(WaveState<C, RB>& w, const char* kbuf, int l16, int g) {
+__device__ __forceinline__ void qk_into(WaveState<C, RB>& w, f32x4 (&sc)[RB][C::kKT],
+                                        const char* kbuf, int l16, int g) {
 #pragma unroll
   for (int kt = 0; kt < C::kKT; ++kt) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) w.s[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) sc[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dk = 0; dk < C::kDK; ++dk) {
       const bf16x8 kf =
           *reinterpret_cast<const bf16x8*>(kbuf + w.koff[dk] + 16 * kt * C::kRowBytes);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        w.s[rb][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, w.qf[rb][dk], w.s[rb][kt], 0, 0, 0);
+        sc[rb][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, w.qf[rb][dk], sc[rb][kt], 0, 0, 0);
     }
   }
 }
 
-// Online softmax (base 2) of one chunk's scores into bf16 probabilities. The
-// reference max m only moves when a row's chunk max exceeds it by more than 8
-// (then O and the row sum are rescaled); in between, probabilities stay below
-// 2^8, which fp32 sums and bf16 P hold as well as values below 1.
 template <class C, int RB>
-__device__ __forceinline__ void softmax_chunk(WaveState<C, RB>& w, int nvalid, float scale_log2,
-                                              int g) {
+__device__ __forceinline__ void qk_chunk(WaveState<C, RB>& w, const char* kbuf, int l16, int g) {
+  qk_into<C, RB>(w, w.s, kbuf, l16, g);
+}
+
+template <class C, int RB>
+__device__ __forceinline__ void softmax_max(WaveState<C, RB>& w, f32x4 (&sc)[RB][C::kKT],
+                                            int nvalid, float scale_log2, int g) {
   if (nvalid < C::kBN) {
     keep_branch();
 #pragma unroll
@@ -278,7 +281,7 @@ __device__ __forceinline__ void softmax_chunk(WaveState<C, RB>& w, int nvalid, f
       for (int r = 0; r < 4; ++r)
         if (16 * kt + 4 * g + r >= nvalid)
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) w.s[rb][kt][r] = -INFINITY;
+          for (int rb = 0; rb < RB; ++rb) sc[rb][kt][r] = -INFINITY;
   }
   float mx[RB];
   bool grow = false;
@@ -287,7 +290,7 @@ __device__ __forceinline__ void softmax_chunk(WaveState<C, RB>& w, int nvalid, f
     float a = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < C::kKT; ++kt)
-      a = fmaxf(a, fmaxf(fmaxf(w.s[rb][kt][0], w.s[rb][kt][1]), fmaxf(w.s[rb][kt][2], w.s[rb][kt][3])));
+      a = fmaxf(a, fmaxf(fmaxf(sc[rb][kt][0], sc[rb][kt][1]), fmaxf(sc[rb][kt][2], sc[rb][kt][3])));
     mx[rb] = row_max4(a) * scale_log2;
     grow |= mx[rb] > w.m[rb] + 8.0f;
   }
@@ -303,13 +306,18 @@ __device__ __forceinline__ void softmax_chunk(WaveState<C, RB>& w, int nvalid, f
       for (int db = 0; db < C::kDB; ++db) w.o[rb][db] *= alpha;
     }
   }
+}
+
+template <class C, int RB>
+__device__ __forceinline__ void softmax_exp(WaveState<C, RB>& w, f32x4 (&sc)[RB][C::kKT],
+                                            float scale_log2) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int kt = 0; kt < C::kKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        w.s[rb][kt][r] = __builtin_amdgcn_exp2f(fmaf(w.s[rb][kt][r], scale_log2, -w.m[rb]));
+        sc[rb][kt][r] = __builtin_amdgcn_exp2f(fmaf(sc[rb][kt][r], scale_log2, -w.m[rb]));
     // The row sum adds the bf16-rounded probabilities, the same values that
     // multiply V, two per dot instruction.
     float ls = w.lsum[rb];
@@ -319,8 +327,8 @@ __device__ __forceinline__ void softmax_chunk(WaveState<C, RB>& w, int nvalid, f
       bf16x8 x;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        x[r] = static_cast<bf16_t>(w.s[rb][2 * kp][r]);
-        x[4 + r] = static_cast<bf16_t>(w.s[rb][2 * kp + 1][r]);
+        x[r] = static_cast<bf16_t>(sc[rb][2 * kp][r]);
+        x[4 + r] = static_cast<bf16_t>(sc[rb][2 * kp + 1][r]);
       }
       w.pf[rb][kp] = x;
 #pragma unroll
@@ -331,6 +339,17 @@ __device__ __forceinline__ void softmax_chunk(WaveState<C, RB>& w, int nvalid, f
     }
     w.lsum[rb] = ls;
   }
+}
+
+// Online softmax (base 2) of one chunk's scores into bf16 probabilities. The
+// reference max m only moves when a row's chunk max exceeds it by more than 8
+// (then O and the row sum are rescaled); in between, probabilities stay below
+// 2^8, which fp32 sums and bf16 P hold as well as values below 1.
+template <class C, int RB>
+__device__ __forceinline__ void softmax_chunk(WaveState<C, RB>& w, int nvalid, float scale_log2,
+                                              int g) {
+  softmax_max<C, RB>(w, w.s, nvalid, scale_log2, g);
+  softmax_exp<C, RB>(w, w.s, scale_log2);
 }
 
 // O^T[d][row] += V^T[d][key] P^T[key][row] for one chunk. Slot j of lane group
@@ -484,6 +503,87 @@ attn_bf16_kernel(const AttnParams p) {
   for (int it = 0; it < walk.n_chunks; it += 2) {
     chunk_step(kb0, vb0, kb1, vb1, it);
     if (it + 1 < walk.n_chunks) chunk_step(kb1, vb1, kb0, vb0, it + 1);
+  }
+  store_out<C, RB>(w, og, t, wave, l16, g);
+}
+
+// Software-pipelined flash loop. Each wave keeps two score buffers: while
+// the softmax of chunk j turns one into probabilities, QK^T of chunk j+1
+// fills the other, in the same basic block, so the compiler can interleave
+// the matrix instructions with the exponentials; PV of chunk j follows. K/V
+// chunks rotate through three LDS buffers, filled by DMA two chunks ahead.
+// The loop is unrolled six times so that every buffer and score-buffer
+// choice is static.
+template <int D, int WAVES, int RB, int BN, bool DENSE>
+__global__ void __launch_bounds__(WAVES * 64, (WAVES <= 4 ? 2 : 1))
+attn_bf16_sp_kernel(const AttnParams p) {
+  using C = Bf16Cfg<D, WAVES, RB, BN>;
+  __shared__ __attribute__((aligned(1024))) char kb0[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char kb1[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char kb2[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char vb0[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char vb1[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char vb2[C::kChunkBytes];
+
+  const int task = logical_task(p);
+  if (task >= p.n_tasks) return;
+  const Task t = decode_task<C::kRows>(p, task, D);
+  const bf16_t* qg = static_cast<const bf16_t*>(p.q) + t.head_base;
+  const bf16_t* kg = static_cast<const bf16_t*>(p.k) + t.head_base;
+  const bf16_t* vg = static_cast<const bf16_t*>(p.v) + t.head_base;
+  bf16_t* og = static_cast<bf16_t*>(p.out) + t.head_base;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const ChunkWalk walk = make_walk<BN, DENSE>(t, p.S);
+  const int n = walk.n_chunks;
+
+  auto dma = [&](int j, char* kdst, char* vdst) __attribute__((always_inline)) {
+    int r, nv;
+    walk.at(j, &r, &nv);
+    load_rows<C, WAVES>(kg, r, nv, kdst, wave, lane);
+    load_rows<C, WAVES>(vg, r, nv, vdst, wave, lane);
+  };
+  dma(0, kb0, vb0);
+  if (n > 1) dma(1, kb1, vb1);
+  WaveState<C, RB> w;
+  load_q_init<C, RB>(w, qg, t, wave, l16, g);
+  wait_vm_all();
+  __syncthreads();
+  qk_into<C, RB>(w, w.s, kb0, l16, g);
+
+  // Step j: chunk j's scores are in `cur`; chunk j+1's K is in kn; chunk j's
+  // V is in vc; DMA of chunk j+2 goes to kd / vd.
+  auto step = [&](int j, f32x4 (&cur)[RB][C::kKT], f32x4 (&nxt)[RB][C::kKT], const char* kn,
+                  const char* vc, char* kd, char* vd) __attribute__((always_inline)) {
+    wait_vm_all();   // chunk j+1 has landed (this wave's part)
+    __syncthreads(); // everyone's part; chunk j-1's buffers are free
+    if (j + 2 < n) dma(j + 2, kd, vd);
+    int r, nv;
+    walk.at(j, &r, &nv);
+    softmax_max<C, RB>(w, cur, nv, p.scale_log2, g);
+    // Unconditional so that it shares a basic block with the exponentials; on
+    // the last chunk it reads a stale (in-bounds) buffer and the scores are
+    // never used.
+    qk_into<C, RB>(w, nxt, kn, l16, g);
+    softmax_exp<C, RB>(w, cur, p.scale_log2);
+    pv_chunk<C, RB>(w, vc, l16, g);
+  };
+  // j % 3 selects the buffers, j % 2 the score buffer.
+  for (int j = 0; j < n; j += 6) {
+    step(j, w.s, w.s2, kb1, vb0, kb2, vb2);
+    if (j + 1 >= n) break;
+    step(j + 1, w.s2, w.s, kb2, vb1, kb0, vb0);
+    if (j + 2 >= n) break;
+    step(j + 2, w.s, w.s2, kb0, vb2, kb1, vb1);
+    if (j + 3 >= n) break;
+    step(j + 3, w.s2, w.s, kb1, vb0, kb2, vb2);
+    if (j + 4 >= n) break;
+    step(j + 4, w.s, w.s2, kb2, vb1, kb0, vb0);
+    if (j + 5 >= n) break;
+    step(j + 5, w.s2, w.s, kb0, vb2, kb1, vb1);
   }
   store_out<C, RB>(w, og, t, wave, l16, g);
 }
@@ -718,6 +818,21 @@ int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
   return (int)hipGetLastError();
 }
 
+template <int D, int WAVES, int RB, int BN>
+int launch_bf16_sp(const AttnProblem& pr, hipStream_t stream) {
+  using C = Bf16Cfg<D, WAVES, RB, BN>;
+  AttnParams p;
+  fill_params(pr, C::kRows, &p);
+  const unsigned grid = (unsigned)p.per_xcd * kXcds;
+  if (pr.dense)
+    hipLaunchKernelGGL((attn_bf16_sp_kernel<D, WAVES, RB, BN, true>), dim3(grid),
+                       dim3(C::kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_bf16_sp_kernel<D, WAVES, RB, BN, false>), dim3(grid),
+                       dim3(C::kThreads), 0, stream, p);
+  return (int)hipGetLastError();
+}
+
 // Ping-pong kernel for 384-row work items.
 #ifndef STA_PP_GROUPING
 #define STA_PP_GROUPING 0
@@ -765,6 +880,8 @@ int dispatch_bf16(const AttnProblem& pr, hipStream_t stream) {
   constexpr int kBigRows = STA_CFG_WAVES * 16 * STA_CFG_RB;
   if (unit_rows % kBigRows == 0) {
     if (STA_ATTN_VARIANT == 1) return launch_bf16_pp<D, 3, 64>(pr, stream);
+    if (STA_ATTN_VARIANT == 2)
+      return launch_bf16_sp<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN>(pr, stream);
     return launch_bf16<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN>(pr, stream);
   }
   if (unit_rows <= 64) return launch_bf16<D, 4, 1, 64>(pr, stream);
