@@ -3,18 +3,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step is one pass of the whole path over one batch of synthetic input
-already resident in HBM: sta_reorder_tiles on q, k and v, sta_forward (which
-derives each query tile's key tiles inline) and sta_restore_order on the
-output. The headline value is effective TFLOP/s over the step, counting only
-computed blocks: 4 * tau^2 * head_dim FLOPs per (query tile, key tile) pair.
+One step is one pass of the whole path over one batch of synthetic raster-
+order input already resident in HBM. By default (--path fused) that is one
+sta_forward_raster launch: the tile grouping of queries and keys, the window
+enumeration and the flash loop in one kernel. --path three_call times
+sta_reorder_tiles on q, k and v, sta_forward and sta_restore_order instead.
+The headline value is effective TFLOP/s over the step, counting only computed
+blocks: 4 * tau^2 * head_dim FLOPs per (query tile, key tile) pair.
 
 Printed as one JSON line. Besides the contract fields it carries
   roofline      the attention kernel (dominant) against the bf16 MFMA peak,
                 timed with HIP events on the stream it runs on;
   cpu_baseline  the CPU oracle timed on a bounded sample of the workload;
   dense         the dense comparator at the same shape and the speed-up;
-  reorder       the permutation kernels' achieved HBM bandwidth.
+  three_call    the reorder -> tile-major forward -> restore path, with the
+                permutation kernels' achieved HBM bandwidth.
 """
 
 from __future__ import annotations
@@ -55,26 +58,16 @@ def gpu_inputs(w, torch):
     return [torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(dt) for _ in range(3)]
 
 
-KERNEL_SOURCES = (
-    "sparse_attention_video_tile_amd/csrc/sta_attention.hip",
-    "sparse_attention_video_tile_amd/csrc/sta_geometry.h",
-    "sparse_attention_video_tile_amd/csrc/sta_kernels.h",
-)
-
-
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, path_name: str):
     """HBM-side bytes per attention launch from the committed counter record
-    (profiles/), or None when there is none for this workload or the kernel
-    sources have changed since the counters were taken."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"attn_bf16_{workload}_traffic.json")
+    (profiles/), or None when there is none for this workload and path or the
+    kernel sources have changed since the counters were taken."""
+    from sparse_attention_video_tile_amd.profile_summary import source_sha256
+    path = os.path.join(ROOT, "profiles", f"attn_bf16_{path_name}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if rec.get("source_sha256") != h.hexdigest():
+    if rec.get("source_sha256") != source_sha256(ROOT):
         return None
     return float(rec["bytes_per_launch"])
 
@@ -121,6 +114,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="sta_30x48x80_w18x24x24")
+    ap.add_argument("--path", choices=("fused", "three_call"), default="fused",
+                    help="fused: one raster-order kernel; three_call: reorder, forward, restore")
+    ap.add_argument("--compare-reps", type=int, default=3,
+                    help="steps of the other path to time for comparison (0: skip)")
     ap.add_argument("--dense-reps", type=int, default=2, help="dense comparator launches to time (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--copy-reference", action="store_true",
@@ -150,7 +147,20 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    def step(timers=None):
+    fused = args.path == "fused"
+    if fused and not binding.raster_run_fits(w.tile, windows, w.heads):
+        print(f"{w.name}: window run too long for the raster kernel; use --path three_call",
+              file=sys.stderr)
+        return 2
+
+    def step_fused(timers=None):
+        if timers is not None:
+            timers[0].record(stream)
+        binding.sta_forward_raster(q, k, v, w.tile, windows, out=out)
+        if timers is not None:
+            timers[1].record(stream)
+
+    def step_three(timers=None):
         if timers is not None:
             timers[0].record(stream)
         for src, dst in ((q, qt), (k, kt), (v, vt)):
@@ -164,30 +174,51 @@ def main(argv=None):
         if timers is not None:
             timers[3].record(stream)
 
+    def timed(step, n_steps, n_events):
+        timers = [[ev() for _ in range(n_events)] for _ in range(n_steps)]
+        start, stop = ev(), ev()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(n_steps):
+            step(timers[i])
+        stop.record(stream)
+        torch.cuda.synchronize()
+        spans = [float(np.mean([t[j].elapsed_time(t[j + 1]) for t in timers]))
+                 for j in range(n_events - 1)]
+        return start.elapsed_time(stop) / n_steps, spans
+
+    step = step_fused if fused else step_three
     if args.copy_reference:
         out.copy_(q)  # a plain copy kernel: reads and writes exactly one tensor
         torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    timers = [[ev() for _ in range(4)] for _ in range(args.steps)]
-    start, stop = ev(), ev()
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        step(timers[i])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
-    attn_ms = float(np.mean([t[1].elapsed_time(t[2]) for t in timers]))
-    reorder_ms = float(np.mean([t[0].elapsed_time(t[1]) for t in timers]))
-    restore_ms = float(np.mean([t[2].elapsed_time(t[3]) for t in timers]))
+    ms_per_step, spans = timed(step, args.steps, 2 if fused else 4)
+    attn_ms = spans[0] if fused else spans[1]
     elem = 2 if w.dtype == "bf16" else 4
     tensor_bytes = w.B * w.heads * S * w.head_dim * elem
     peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+
+    three = None
+    if not fused or args.compare_reps > 0:
+        if fused:
+            step_three()
+            three_ms, tspans = timed(step_three, args.compare_reps, 4)
+        else:
+            three_ms, tspans = ms_per_step, spans
+        reorder_ms, fwd_ms, restore_ms = tspans
+        three = {
+            "ms": three_ms,
+            "tflops": flops / (three_ms * 1e-3) / 1e12,
+            "forward_ms": fwd_ms,
+            "reorder_qkv_ms": reorder_ms,
+            "reorder_qkv_gbs": 3 * 2 * tensor_bytes / (reorder_ms * 1e-3) / 1e9,
+            "restore_ms": restore_ms,
+            "restore_gbs": 2 * tensor_bytes / (restore_ms * 1e-3) / 1e9,
+            "hbm_peak_gbs": HBM_PEAK_GBS,
+        }
 
     dense = None
     if args.dense_reps > 0:
@@ -227,28 +258,24 @@ def main(argv=None):
             "B": w.B, "heads": w.heads, "head_dim": w.head_dim,
             "volume": list(w.volume), "tile": list(w.tile),
             "windows": sorted({tuple(x) for x in windows.tolist()}),
+            "path": args.path,
             "algorithmic_tflop_per_step": flops / 1e12,
             "inputs": "seeded N(0,1) q, k, v drawn on the device, rounded to bf16",
         },
         "roofline": {
-            "kernel": "attn_bf16_kernel" if w.dtype == "bf16" else "attn_f32_kernel",
+            "kernel": ("attn_bf16_kernel" if w.dtype == "bf16" else "attn_f32_kernel")
+                      + (" (raster order)" if fused else " (tile-major order)"),
             "bound": "mfma",
             "achieved": attn_tflops,
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": attn_tflops / peak,
-            "traffic": recorded_traffic(w.name) if w.dtype == "bf16" else None,
+            "traffic": recorded_traffic(w.name, args.path) if w.dtype == "bf16" else None,
             "launch_ms": attn_ms,
         },
         "cpu_baseline": cpu,
         "dense": dense,
-        "reorder": {
-            "qkv_ms": reorder_ms,
-            "qkv_gbs": 3 * 2 * tensor_bytes / (reorder_ms * 1e-3) / 1e9,
-            "restore_ms": restore_ms,
-            "restore_gbs": 2 * tensor_bytes / (restore_ms * 1e-3) / 1e9,
-            "peak_gbs": HBM_PEAK_GBS,
-        },
+        "three_call": three,
     }
     print(json.dumps(result), flush=True)
     return 0

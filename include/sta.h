@@ -130,6 +130,22 @@ int sta_forward(const void* q, const void* k, const void* v, void* out, int B, i
                 float scale, int dtype, void* stream);
 
 /*
+ * STA forward on raster-order tensors: the same result as sta_reorder_tiles of
+ * q, k, v, then sta_forward, then sta_restore_order of the output, bit for bit,
+ * in one kernel and without the intermediate tile-major copies. The grouping
+ * of queries and keys into tiles (podcast transcript, the answer on what a tile
+ * is) is folded into the kernel's addressing instead of a separate permutation.
+ *   q, k, v: device [B][heads][S][head_dim] in RASTER order, read.
+ *   out:     device, same shape, raster order, written. No overlap with inputs.
+ * Other arguments and rules as sta_forward. Additionally each head's window run
+ * omega_w * tau (keys that are consecutive in tile-major order) must be at most
+ * 8192 keys, else STA_ERR_UNSUPPORTED (reorder and call sta_forward instead).
+ */
+int sta_forward_raster(const void* q, const void* k, const void* v, void* out, int B, int heads,
+                       int head_dim, int T, int H, int W, const int* tile, const int* window,
+                       float scale, int dtype, void* stream);
+
+/*
  * Full softmax attention over all S keys (the computation STA replaces, used
  * as the speed-up denominator: atlas.scime.ai summary, "Key results").
  *   q, k, v, out: device [B][heads][S][head_dim], any common token order.

@@ -9,8 +9,10 @@ from .binding import (  # noqa: F401
     StaError,
     last_error,
     load_library,
+    raster_run_fits,
     sliding_tile_attention,
     sta_forward,
+    sta_forward_raster,
     sta_full_attention,
     sta_kv_pair_count,
     sta_kv_tiles,

@@ -21,7 +21,9 @@ LIB_PATH = os.path.join(_PKG, "libsta.so")
 STA_OK, STA_ERR_INVALID_ARG, STA_ERR_UNSUPPORTED, STA_ERR_HIP = 0, -1, -2, -3
 STA_BF16, STA_F32 = 0, 1
 STA_MAX_HEADS = 256
-ABI_VERSION = 1
+ABI_VERSION = 2
+# Longest window run (omega_w * tau keys) sta_forward_raster accepts.
+STA_MAX_RASTER_RUN = 8192
 
 EXPORTS = (
     "sta_abi_version",
@@ -30,6 +32,7 @@ EXPORTS = (
     "sta_kv_tiles",
     "sta_kv_pair_count",
     "sta_forward",
+    "sta_forward_raster",
     "sta_full_attention",
     "sta_last_error",
 )
@@ -71,9 +74,11 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.sta_kv_tiles.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, int3, int3, c_int, c_void_p]
     lib.sta_kv_pair_count.restype = ctypes.c_longlong
     lib.sta_kv_pair_count.argtypes = [c_int, c_int, c_int, c_int, int3, int3]
-    lib.sta_forward.restype = c_int
-    lib.sta_forward.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
-                                c_int, c_int, c_int, int3, int3, c_float, c_int, c_void_p]
+    for name in ("sta_forward", "sta_forward_raster"):
+        f = getattr(lib, name)
+        f.restype = c_int
+        f.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
+                      c_int, c_int, c_int, int3, int3, c_float, c_int, c_void_p]
     lib.sta_full_attention.restype = c_int
     lib.sta_full_attention.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int,
                                        c_int, c_int, c_float, c_int, c_void_p]
@@ -263,12 +268,52 @@ def sta_full_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out
 
 
+def sta_forward_raster(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tile: Sequence[int],
+                       window, scale: Optional[float] = None,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """STA forward on raster (B, heads, T, H, W, d) tensors in one kernel;
+    returns the raster-order output (same values as reorder, sta_forward,
+    restore)."""
+    lib = load_library()
+    if q.dim() != 6 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must all be (B, heads, T, H, W, d)")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    B, heads, T, H, W, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    dev = _require_gpu(q, k, v, out)
+    with torch.cuda.device(dev):
+        rc = lib.sta_forward_raster(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B,
+                                    heads, d, T, H, W, _int_array(tile),
+                                    _int_array(_windows_per_head(window, heads)), float(scale),
+                                    _dtype_code(q), _stream(dev))
+    _check(rc, "sta_forward_raster")
+    return out
+
+
+def raster_run_fits(tile: Sequence[int], window, heads: int) -> bool:
+    """Whether every head's window run (omega_w * tau keys) is within what
+    sta_forward_raster accepts."""
+    ws = _windows_per_head(window, heads)
+    tau = int(tile[0]) * int(tile[1]) * int(tile[2])
+    return all((ws[3 * h + 2] // int(tile[2])) * tau <= STA_MAX_RASTER_RUN for h in range(heads))
+
+
 def sliding_tile_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tile: Sequence[int],
-                           window, scale: Optional[float] = None) -> torch.Tensor:
-    """The whole path on raster (B, heads, T, H, W, d) tensors: reorder q, k, v
-    to tile-major, STA forward, restore the output to raster order."""
+                           window, scale: Optional[float] = None, fused: bool = True) -> torch.Tensor:
+    """The whole path on raster (B, heads, T, H, W, d) tensors. fused=True runs
+    the single raster-order kernel when the windows allow it; otherwise q, k, v
+    are reordered to tile-major, STA forward runs, and the output is restored
+    to raster order. Both give the same values."""
     if q.dim() != 6:
         raise ValueError("q, k, v must be (B, heads, T, H, W, d)")
+    if fused and raster_run_fits(tile, window, q.shape[1]):
+        return sta_forward_raster(q, k, v, tile, window, scale)
     volume = tuple(q.shape[2:5])
     qt, kt, vt = (sta_reorder_tiles(x, tile) for x in (q, k, v))
     ot = sta_forward(qt, kt, vt, volume, tile, window, scale)

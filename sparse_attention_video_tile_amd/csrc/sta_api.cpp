@@ -146,11 +146,15 @@ int attention_common(sta::AttnProblem& p, void* stream) {
   return launched(rc);
 }
 
+int forward_common(const void* q, const void* k, const void* v, void* out, int B, int heads,
+                   int head_dim, int T, int H, int W, const int* tile, const int* window,
+                   float scale, int dtype, void* stream, bool raster);
+
 }  // namespace
 
 extern "C" {
 
-int sta_abi_version(void) { return 1; }
+int sta_abi_version(void) { return 2; }
 
 const char* sta_last_error(void) { return g_last_error.c_str(); }
 
@@ -204,19 +208,52 @@ int sta_kv_tiles(int* kv_list, int* kv_count, int heads, int T, int H, int W, co
   return launched(sta::launch_kv_tiles(kv_list, kv_count, heads, g, omega, max_kv, stream));
 }
 
-int sta_forward(const void* q, const void* k, const void* v, void* out, int B, int heads,
-                int head_dim, int T, int H, int W, const int* tile, const int* window, float scale,
-                int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int forward_common(const void* q, const void* k, const void* v, void* out, int B, int heads,
+                   int head_dim, int T, int H, int W, const int* tile, const int* window,
+                   float scale, int dtype, void* stream, bool raster) {
   if (heads <= 0 || heads > STA_MAX_HEADS)
     return fail(STA_ERR_INVALID_ARG, "heads=%d must be in [1, %d]", heads, STA_MAX_HEADS);
   static thread_local sta::AttnProblem p;
   p.q = q; p.k = k; p.v = v; p.out = out;
   p.B = B; p.heads = heads; p.head_dim = head_dim; p.dtype = dtype; p.scale = scale;
   p.dense = false;
+  p.raster = raster;
   int rc = check_volume(T, H, W, tile, &p.g);
   if (rc) return rc;
   if ((rc = check_windows(p.g, heads, window, p.omega))) return rc;
+  if (raster) {
+    for (int h = 0; h < heads; ++h) {
+      const long long run = (long long)p.omega[h][2] * p.g.tau;
+      if (run > sta::kMaxRasterRun)
+        return fail(STA_ERR_UNSUPPORTED,
+                    "raster order: window run of head %d has %lld keys (limit %d); reorder to "
+                    "tile-major order and use sta_forward",
+                    h, run, sta::kMaxRasterRun);
+    }
+  }
   return attention_common(p, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sta_forward(const void* q, const void* k, const void* v, void* out, int B, int heads,
+                int head_dim, int T, int H, int W, const int* tile, const int* window, float scale,
+                int dtype, void* stream) {
+  return forward_common(q, k, v, out, B, heads, head_dim, T, H, W, tile, window, scale, dtype,
+                        stream, false);
+}
+
+int sta_forward_raster(const void* q, const void* k, const void* v, void* out, int B, int heads,
+                       int head_dim, int T, int H, int W, const int* tile, const int* window,
+                       float scale, int dtype, void* stream) {
+  return forward_common(q, k, v, out, B, heads, head_dim, T, H, W, tile, window, scale, dtype,
+                        stream, true);
 }
 
 int sta_full_attention(const void* q, const void* k, const void* v, void* out, int B, int heads,
@@ -224,6 +261,7 @@ int sta_full_attention(const void* q, const void* k, const void* v, void* out, i
   if (S <= 0 || S > (1 << 30)) return fail(STA_ERR_INVALID_ARG, "S=%d must be in [1, 2^30]", S);
   static thread_local sta::AttnProblem p;
   memset(&p.g, 0, sizeof(p.g));
+  p.raster = false;
   p.q = q; p.k = k; p.v = v; p.out = out;
   p.B = B; p.heads = heads; p.head_dim = head_dim; p.dtype = dtype; p.scale = scale;
   p.dense = true;

@@ -52,8 +52,10 @@ struct AttnParams {
   float scale_log2; // scale * log2(e)
   int dense;
   int nt, nh, nw, tau;
+  int H, W, ct, ch, cw;  // volume and tile, for raster-order addressing
   uint16_t omega[STA_MAX_HEADS][3];
 };
+
 
 // Maps the hardware workgroup id to a logical task so that consecutive
 // logical tasks (the row blocks of one query tile, then neighbouring tiles
@@ -71,10 +73,17 @@ struct KvRuns {
   int st, sh, sw;     // window start in tiles
   int nh, nw, tau;
   int dense;
+  // Token index (tile-major order) of run r's first key.
   __device__ __forceinline__ int run_start(int r) const {
     if (dense) return 0;
     const int it = r / oh, ih = r - (r / oh) * oh;
     return (((st + it) * nh + (sh + ih)) * nw + sw) * tau;
+  }
+  // Raster token index of run r's first key (the run's tile-major key e sits
+  // at this plus the run offset table entry e).
+  __device__ __forceinline__ int run_start_raster(int r, int H, int W, int ct, int ch, int cw) const {
+    const int it = r / oh, ih = r - (r / oh) * oh;
+    return (((st + it) * ct) * H + (sh + ih) * ch) * W + sw * cw;
   }
 };
 
@@ -82,8 +91,34 @@ struct Task {
   long long head_base;  // element offset of this (batch, head)
   int row0;             // first query row (token index) of the work item
   int valid_rows;       // rows of the work item inside its unit
+  int local0;           // first row of the work item within its unit
+  int qt, qh, qw;       // query tile coordinates (STA)
   KvRuns kv;
 };
+
+// Raster token index of row `local` (tile-major order inside the tile) of
+// query tile (qt, qh, qw).
+__device__ __forceinline__ int tile_row_raster(const AttnParams& p, int qt, int qh, int qw, int local) {
+  const int plane = p.ch * p.cw;
+  const int lt = local / plane;
+  const int rem = local - lt * plane;
+  const int lh = rem / p.cw;
+  const int lw = rem - lh * p.cw;
+  return ((qt * p.ct + lt) * p.H + qh * p.ch + lh) * p.W + qw * p.cw + lw;
+}
+
+// Raster offset, relative to the run's first key, of key e of a window run
+// (tile-major order within the run: tile along w, then the tile's tokens).
+__device__ __forceinline__ int run_offset_raster(const AttnParams& p, int e) {
+  const int tw = e / p.tau;
+  const int local = e - tw * p.tau;
+  const int plane = p.ch * p.cw;
+  const int lt = local / plane;
+  const int rem = local - lt * plane;
+  const int lh = rem / p.cw;
+  const int lw = rem - lh * p.cw;
+  return (lt * p.H + lh) * p.W + tw * p.cw + lw;
+}
 
 template <int ROWS>
 __device__ __forceinline__ Task decode_task(const AttnParams& p, int task, int D) {
@@ -96,7 +131,9 @@ __device__ __forceinline__ Task decode_task(const AttnParams& p, int task, int D
   t.head_base = (long long)bh * p.S * D;
   const int unit_row0 = unit * p.unit_rows;
   t.row0 = unit_row0 + rb * ROWS;
+  t.local0 = rb * ROWS;
   t.valid_rows = min(ROWS, p.unit_rows - rb * ROWS);
+  t.qt = t.qh = t.qw = 0;
   KvRuns& kv = t.kv;
   kv.dense = p.dense;
   kv.nh = p.nh; kv.nw = p.nw; kv.tau = p.tau;
@@ -107,6 +144,7 @@ __device__ __forceinline__ Task decode_task(const AttnParams& p, int task, int D
     const int qw = unit % p.nw;
     const int qh = (unit / p.nw) % p.nh;
     const int qt = unit / (p.nw * p.nh);
+    t.qt = qt; t.qh = qh; t.qw = qw;
     kv.st = window_start(qt, p.nt, ot);
     kv.sh = window_start(qh, p.nh, oh);
     kv.sw = window_start(qw, p.nw, ow);
@@ -188,7 +226,7 @@ __device__ __forceinline__ int swz(int row, int c) {
 // 1 KB block; WAVES wavefronts share the chunk.
 template <class C, int WAVES>
 __device__ __forceinline__ void load_rows(const bf16_t* src, int kv_row0, int nvalid, char* buf,
-                                          int wave, int lane) {
+                                          int wave, int lane, const int* rtab = nullptr) {
   constexpr int kIter = (C::kBlocks + WAVES - 1) / WAVES;
 #pragma unroll
   for (int b = 0; b < kIter; ++b) {
@@ -197,7 +235,11 @@ __device__ __forceinline__ void load_rows(const bf16_t* src, int kv_row0, int nv
     const int row = blk * C::kRowsPerBlock + lane / C::kCPR;
     const int pos = lane % C::kCPR;                      // slot this lane fills
     const int c = pos ^ ((swz<C::kCPR>(row, 0) >> 4) & (C::kCPR - 1));  // chunk it holds
-    const int src_row = kv_row0 + min(row, nvalid - 1);
+    // Tile-major order: the chunk's keys are consecutive token rows from
+    // kv_row0. Raster order: kv_row0 is the run's first raster token and
+    // rtab (already offset to the chunk) gives each key's raster offset.
+    const int key = min(row, nvalid - 1);
+    const int src_row = rtab ? kv_row0 + rtab[key] : kv_row0 + key;
     const long long off = (long long)src_row * (C::kRowBytes / 2) + c * 8;
     __builtin_amdgcn_global_load_lds(src + off, (lds_void*)(buf + blk * 1024), 16, 0, 0);
   }
@@ -222,7 +264,6 @@ struct WaveState {
   f32x4 o[RB][C::kDB];
   float m[RB], lsum[RB];
   f32x4 s[RB][C::kKT];
-  f32x4 s2[RB][C::kKT];  // second score buffer of the software-pipelined loop
   bf16x8 pf[RB][C::kKP];
   // K operand: row 16*kt + l16, chunk 4*dk + g; the swizzled offset is
   // koff[dk] + 16*kt*row_bytes because the row's low 4 bits are l16.
@@ -378,19 +419,39 @@ __device__ __forceinline__ void pv_chunk(WaveState<C, RB>& w, const char* vbuf, 
   }
 }
 
+// Token index (in the tensor's own order) of each of this lane's query rows,
+// and whether the row exists (work items may be ragged).
 template <class C, int RB>
-__device__ __forceinline__ void load_q_init(WaveState<C, RB>& w, const bf16_t* qg, const Task& t,
-                                            int wave, int l16, int g) {
-  lane_offsets<C, RB>(w, l16, g);
+struct RowMap {
+  int tok[RB];
+  bool ok[RB];
+};
+
+template <class C, int RB, bool RASTER>
+__device__ __forceinline__ RowMap<C, RB> map_rows(const AttnParams& p, const Task& t, int wave,
+                                                  int l16) {
+  RowMap<C, RB> rm;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int r = wave * C::kRowsWave + 16 * rb + l16;
-    const bool ok = r < t.valid_rows;
-    const bf16_t* src = qg + (long long)(t.row0 + (ok ? r : 0)) * C::kD + 8 * g;
+    rm.ok[rb] = r < t.valid_rows;
+    const int rr = rm.ok[rb] ? r : 0;
+    rm.tok[rb] = RASTER ? tile_row_raster(p, t.qt, t.qh, t.qw, t.local0 + rr) : t.row0 + rr;
+  }
+  return rm;
+}
+
+template <class C, int RB>
+__device__ __forceinline__ void load_q_init(WaveState<C, RB>& w, const bf16_t* qg,
+                                            const RowMap<C, RB>& rm, int l16, int g) {
+  lane_offsets<C, RB>(w, l16, g);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const bf16_t* src = qg + (long long)rm.tok[rb] * C::kD + 8 * g;
 #pragma unroll
     for (int dk = 0; dk < C::kDK; ++dk) {
       bf16x8 x = *reinterpret_cast<const bf16x8*>(src + 32 * dk);
-      if (!ok) x = bf16x8{};
+      if (!rm.ok[rb]) x = bf16x8{};
       w.qf[rb][dk] = x;
     }
     w.m[rb] = -INFINITY;
@@ -402,14 +463,13 @@ __device__ __forceinline__ void load_q_init(WaveState<C, RB>& w, const bf16_t* q
 
 // Normalise and store: lane holds O[row l16][16*db + 4g + r].
 template <class C, int RB>
-__device__ __forceinline__ void store_out(WaveState<C, RB>& w, bf16_t* og, const Task& t, int wave,
-                                          int l16, int g) {
+__device__ __forceinline__ void store_out(WaveState<C, RB>& w, bf16_t* og, const RowMap<C, RB>& rm,
+                                          int g) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float inv = 1.0f / row_sum4(w.lsum[rb]);
-    const int r = wave * C::kRowsWave + 16 * rb + l16;
-    if (r < t.valid_rows) {
-      bf16_t* dst = og + (long long)(t.row0 + r) * C::kD + 4 * g;
+    if (rm.ok[rb]) {
+      bf16_t* dst = og + (long long)rm.tok[rb] * C::kD + 4 * g;
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db) {
         bf16x4 y;
@@ -433,6 +493,15 @@ struct ChunkWalk {
     *row0 = (dense ? 0 : kv.run_start(run)) + c0;
     *nvalid = min(bn, run_len - c0);
   }
+  // Raster order: the run's first raster token, the chunk's first key within
+  // the run, and the number of valid keys.
+  __device__ __forceinline__ void at_raster(const AttnParams& p, int it, int* base, int* c0,
+                                            int* nvalid) const {
+    const int run = it / chunks_per_run;
+    *c0 = (it - run * chunks_per_run) * bn;
+    *base = kv.run_start_raster(run, p.H, p.W, p.ct, p.ch, p.cw);
+    *nvalid = min(bn, run_len - *c0);
+  }
 };
 
 template <int BN, bool DENSE>
@@ -447,9 +516,13 @@ __device__ __forceinline__ ChunkWalk make_walk(const Task& t, int S) {
   return cw;
 }
 
-// Plain flash loop: every wave runs QK^T, softmax and PV of a chunk in turn;
-// the next chunk's K and V stream into the other LDS buffer meanwhile.
-template <int D, int WAVES, int RB, int BN, bool DENSE>
+// Flash loop: every wave runs QK^T, softmax and PV of a chunk in turn; the
+// next chunk's K and V stream into the other LDS buffer meanwhile.
+// RASTER: q, k, v, out are in raster token order (the permutation to and from
+// tile-major order is folded into the addressing): query rows map through
+// tile_row_raster, and every key of a window run through a table of raster
+// offsets built in dynamic LDS at the start (all runs of a work item share it).
+template <int D, int WAVES, int RB, int BN, bool DENSE, bool RASTER>
 __global__ void __launch_bounds__(WAVES * 64, (WAVES <= 4 ? 2 : 1))
 attn_bf16_kernel(const AttnParams p) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
@@ -461,6 +534,8 @@ attn_bf16_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) char vb0[C::kChunkBytes];
   __shared__ __attribute__((aligned(1024))) char kb1[C::kChunkBytes];
   __shared__ __attribute__((aligned(1024))) char vb1[C::kChunkBytes];
+  // Raster offsets of one window run (RASTER only), sized at launch.
+  extern __shared__ int rtab[];
 
   const int task = logical_task(p);
   if (task >= p.n_tasks) return;
@@ -475,14 +550,27 @@ attn_bf16_kernel(const AttnParams p) {
   const int l16 = lane & 15;
   const int g = lane >> 4;
   const ChunkWalk walk = make_walk<BN, DENSE>(t, p.S);
-  {
-    int row0, nv;
-    walk.at(0, &row0, &nv);
-    load_rows<C, WAVES>(kg, row0, nv, kb0, wave, lane);
-    load_rows<C, WAVES>(vg, row0, nv, vb0, wave, lane);
+  if (RASTER) {
+    for (int e = threadIdx.x; e < walk.run_len; e += C::kThreads) rtab[e] = run_offset_raster(p, e);
+    __syncthreads();
   }
+  auto dma = [&](int it, char* kdst, char* vdst) __attribute__((always_inline)) {
+    if (RASTER) {
+      int base, c0, nv;
+      walk.at_raster(p, it, &base, &c0, &nv);
+      load_rows<C, WAVES>(kg, base, nv, kdst, wave, lane, rtab + c0);
+      load_rows<C, WAVES>(vg, base, nv, vdst, wave, lane, rtab + c0);
+    } else {
+      int row0, nv;
+      walk.at(it, &row0, &nv);
+      load_rows<C, WAVES>(kg, row0, nv, kdst, wave, lane);
+      load_rows<C, WAVES>(vg, row0, nv, vdst, wave, lane);
+    }
+  };
+  dma(0, kb0, vb0);
+  const RowMap<C, RB> rm = map_rows<C, RB, RASTER>(p, t, wave, l16);
   WaveState<C, RB> w;
-  load_q_init<C, RB>(w, qg, t, wave, l16, g);
+  load_q_init<C, RB>(w, qg, rm, l16, g);
 
   auto chunk_step = [&](const char* kcur, const char* vcur, char* knxt, char* vnxt, int it)
                         __attribute__((always_inline)) {
@@ -490,12 +578,7 @@ attn_bf16_kernel(const AttnParams p) {
     walk.at(it, &row0, &nvalid);
     wait_vm_all();     // this wave's loads of chunk `it` have landed in LDS
     __syncthreads();   // ... and every wave's; chunk it-1's buffers are free
-    if (it + 1 < walk.n_chunks) {
-      int r1, nv1;
-      walk.at(it + 1, &r1, &nv1);
-      load_rows<C, WAVES>(kg, r1, nv1, knxt, wave, lane);
-      load_rows<C, WAVES>(vg, r1, nv1, vnxt, wave, lane);
-    }
+    if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
     qk_chunk<C, RB>(w, kcur, l16, g);
     softmax_chunk<C, RB>(w, nvalid, p.scale_log2, g);
     pv_chunk<C, RB>(w, vcur, l16, g);
@@ -504,182 +587,7 @@ attn_bf16_kernel(const AttnParams p) {
     chunk_step(kb0, vb0, kb1, vb1, it);
     if (it + 1 < walk.n_chunks) chunk_step(kb1, vb1, kb0, vb0, it + 1);
   }
-  store_out<C, RB>(w, og, t, wave, l16, g);
-}
-
-// Software-pipelined flash loop. Each wave keeps two score buffers: while
-// the softmax of chunk j turns one into probabilities, QK^T of chunk j+1
-// fills the other, in the same basic block, so the compiler can interleave
-// the matrix instructions with the exponentials; PV of chunk j follows. K/V
-// chunks rotate through three LDS buffers, filled by DMA two chunks ahead.
-// The loop is unrolled six times so that every buffer and score-buffer
-// choice is static.
-template <int D, int WAVES, int RB, int BN, bool DENSE>
-__global__ void __launch_bounds__(WAVES * 64, (WAVES <= 4 ? 2 : 1))
-attn_bf16_sp_kernel(const AttnParams p) {
-  using C = Bf16Cfg<D, WAVES, RB, BN>;
-  __shared__ __attribute__((aligned(1024))) char kb0[C::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char kb1[C::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char kb2[C::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char vb0[C::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char vb1[C::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char vb2[C::kChunkBytes];
-
-  const int task = logical_task(p);
-  if (task >= p.n_tasks) return;
-  const Task t = decode_task<C::kRows>(p, task, D);
-  const bf16_t* qg = static_cast<const bf16_t*>(p.q) + t.head_base;
-  const bf16_t* kg = static_cast<const bf16_t*>(p.k) + t.head_base;
-  const bf16_t* vg = static_cast<const bf16_t*>(p.v) + t.head_base;
-  bf16_t* og = static_cast<bf16_t*>(p.out) + t.head_base;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l16 = lane & 15;
-  const int g = lane >> 4;
-  const ChunkWalk walk = make_walk<BN, DENSE>(t, p.S);
-  const int n = walk.n_chunks;
-
-  auto dma = [&](int j, char* kdst, char* vdst) __attribute__((always_inline)) {
-    int r, nv;
-    walk.at(j, &r, &nv);
-    load_rows<C, WAVES>(kg, r, nv, kdst, wave, lane);
-    load_rows<C, WAVES>(vg, r, nv, vdst, wave, lane);
-  };
-  dma(0, kb0, vb0);
-  if (n > 1) dma(1, kb1, vb1);
-  WaveState<C, RB> w;
-  load_q_init<C, RB>(w, qg, t, wave, l16, g);
-  wait_vm_all();
-  __syncthreads();
-  qk_into<C, RB>(w, w.s, kb0, l16, g);
-
-  // Step j: chunk j's scores are in `cur`; chunk j+1's K is in kn; chunk j's
-  // V is in vc; DMA of chunk j+2 goes to kd / vd.
-  auto step = [&](int j, f32x4 (&cur)[RB][C::kKT], f32x4 (&nxt)[RB][C::kKT], const char* kn,
-                  const char* vc, char* kd, char* vd) __attribute__((always_inline)) {
-    wait_vm_all();   // chunk j+1 has landed (this wave's part)
-    __syncthreads(); // everyone's part; chunk j-1's buffers are free
-    if (j + 2 < n) dma(j + 2, kd, vd);
-    int r, nv;
-    walk.at(j, &r, &nv);
-    softmax_max<C, RB>(w, cur, nv, p.scale_log2, g);
-    // Unconditional so that it shares a basic block with the exponentials; on
-    // the last chunk it reads a stale (in-bounds) buffer and the scores are
-    // never used.
-    qk_into<C, RB>(w, nxt, kn, l16, g);
-    softmax_exp<C, RB>(w, cur, p.scale_log2);
-    pv_chunk<C, RB>(w, vc, l16, g);
-  };
-  // j % 3 selects the buffers, j % 2 the score buffer.
-  for (int j = 0; j < n; j += 6) {
-    step(j, w.s, w.s2, kb1, vb0, kb2, vb2);
-    if (j + 1 >= n) break;
-    step(j + 1, w.s2, w.s, kb2, vb1, kb0, vb0);
-    if (j + 2 >= n) break;
-    step(j + 2, w.s, w.s2, kb0, vb2, kb1, vb1);
-    if (j + 3 >= n) break;
-    step(j + 3, w.s2, w.s, kb1, vb0, kb2, vb2);
-    if (j + 4 >= n) break;
-    step(j + 4, w.s, w.s2, kb2, vb1, kb0, vb0);
-    if (j + 5 >= n) break;
-    step(j + 5, w.s2, w.s, kb0, vb2, kb1, vb1);
-  }
-  store_out<C, RB>(w, og, t, wave, l16, g);
-}
-
-// Ping-pong flash loop (8 waves). The waves form two groups with one wave of
-// each on every SIMD. All waves run the same sequence per chunk j: an MFMA
-// phase M_j (PV of chunk j-1, then QK^T of chunk j), a barrier, a softmax
-// phase S_j (VALU), a barrier. Group 1 starts one barrier later than group 0,
-// so while one wave of a SIMD is in an MFMA phase its partner is in a softmax
-// phase: the matrix core and the VALU work at the same time.
-//
-// Barrier intervals are numbered 1, 2, ...; group 0 runs M_j in interval
-// 2j+1 and S_j in 2j+2, group 1 one interval later. K_j and V_{j-1} are read
-// in intervals 2j+1 and 2j+2. At the start of M_j, group 0 issues the DMA of
-// K_{j+1} and V_j (their buffers' previous chunks were last read in interval
-// 2j) and waits for it at the end of S_j, before the workgroup barrier that
-// precedes the first reads in interval 2j+3.
-template <int D, int RB, int BN, bool DENSE, int GROUPING>
-__global__ void __launch_bounds__(512)
-attn_bf16_pp_kernel(const AttnParams p) {
-  using C = Bf16Cfg<D, 8, RB, BN>;
-  __shared__ __attribute__((aligned(1024))) char kb0[C::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char kb1[C::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char vb0[C::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char vb1[C::kChunkBytes];
-
-  const int task = logical_task(p);
-  if (task >= p.n_tasks) return;
-  const Task t = decode_task<C::kRows>(p, task, D);
-  const bf16_t* qg = static_cast<const bf16_t*>(p.q) + t.head_base;
-  const bf16_t* kg = static_cast<const bf16_t*>(p.k) + t.head_base;
-  const bf16_t* vg = static_cast<const bf16_t*>(p.v) + t.head_base;
-  bf16_t* og = static_cast<bf16_t*>(p.out) + t.head_base;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l16 = lane & 15;
-  const int g = lane >> 4;
-  // Group 0 or 1; the two waves sharing a SIMD belong to different groups.
-  const int group = GROUPING == 0 ? (wave >> 2) : (wave & 1);
-  const int gwave = GROUPING == 0 ? (wave & 3) : (wave >> 1);  // index within the group
-  const ChunkWalk walk = make_walk<BN, DENSE>(t, p.S);
-  const int n = walk.n_chunks;
-
-  {
-    int row0, nv;
-    walk.at(0, &row0, &nv);
-    load_rows<C, 8>(kg, row0, nv, kb0, wave, lane);
-  }
-  WaveState<C, RB> w;
-  load_q_init<C, RB>(w, qg, t, wave, l16, g);
-  wait_vm_all();
-  __syncthreads();
-  if (group == 1) __builtin_amdgcn_s_barrier();  // interval 1 is group 0's M_0
-
-  // Chunk step j: kcur holds K_j, vprv holds V_{j-1}; group 0 loads K_{j+1}
-  // into knxt and V_j into vnew.
-  auto step = [&](int j, const char* kcur, const char* vprv, char* knxt, char* vnew)
-                  __attribute__((always_inline)) {
-    if (group == 0) {
-      if (j + 1 < n) {
-        int r, nv;
-        walk.at(j + 1, &r, &nv);
-        load_rows<C, 4>(kg, r, nv, knxt, gwave, lane);
-      }
-      if (j < n) {
-        int r, nv;
-        walk.at(j, &r, &nv);
-        load_rows<C, 4>(vg, r, nv, vnew, gwave, lane);
-      }
-    }
-    if (j > 0) pv_chunk<C, RB>(w, vprv, l16, g);
-    if (j < n) qk_chunk<C, RB>(w, kcur, l16, g);
-    if (group == 0)
-      __builtin_amdgcn_s_barrier();
-    else
-      __syncthreads();
-    if (j < n) {
-      int r, nv;
-      walk.at(j, &r, &nv);
-      softmax_chunk<C, RB>(w, nv, p.scale_log2, g);
-    }
-    if (group == 0) {
-      wait_vm_all();  // this step's DMA has landed
-      __syncthreads();
-    } else {
-      __builtin_amdgcn_s_barrier();
-    }
-    wait_vm_all();  // nothing is outstanding here; tells the compiler so
-  };
-  for (int j = 0; j <= n; j += 2) {
-    step(j, kb0, vb1, kb1, vb0);
-    if (j + 1 <= n) step(j + 1, kb1, vb0, kb0, vb1);
-  }
-  if (group == 0) __builtin_amdgcn_s_barrier();
-  store_out<C, RB>(w, og, t, wave, l16, g);
+  store_out<C, RB>(w, og, rm, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -689,7 +597,7 @@ attn_bf16_pp_kernel(const AttnParams p) {
 constexpr int kF32Threads = 128;
 constexpr int kF32BN = 32;
 
-template <int D>
+template <int D, bool RASTER>
 __global__ void __launch_bounds__(kF32Threads) attn_f32_kernel(const AttnParams p) {
   __shared__ float4 ks[kF32BN * D / 4];
   __shared__ float4 vs[kF32BN * D / 4];
@@ -704,7 +612,9 @@ __global__ void __launch_bounds__(kF32Threads) attn_f32_kernel(const AttnParams 
   const int tid = threadIdx.x;
   const bool row_ok = tid < t.valid_rows;
   float q[D], o[D];
-  const float* qrow = qg + (long long)(t.row0 + (row_ok ? tid : 0)) * D;
+  const int my_row = row_ok ? tid : 0;
+  const int q_tok = RASTER ? tile_row_raster(p, t.qt, t.qh, t.qw, t.local0 + my_row) : t.row0 + my_row;
+  const float* qrow = qg + (long long)q_tok * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     q[d] = row_ok ? qrow[d] : 0.f;
@@ -714,6 +624,7 @@ __global__ void __launch_bounds__(kF32Threads) attn_f32_kernel(const AttnParams 
 
   for (int run = 0; run < t.kv.runs; ++run) {
     const int kv0 = t.kv.run_start(run);
+    const int kv0_raster = RASTER ? t.kv.run_start_raster(run, p.H, p.W, p.ct, p.ch, p.cw) : 0;
     for (int c0 = 0; c0 < t.kv.run_len; c0 += kF32BN) {
       const int nvalid = min(kF32BN, t.kv.run_len - c0);
       __syncthreads();
@@ -721,7 +632,8 @@ __global__ void __launch_bounds__(kF32Threads) attn_f32_kernel(const AttnParams 
         const int key = i / (D / 4);
         float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
         if (key < nvalid) {
-          const long long off = (long long)(kv0 + c0) * (D / 4) + i;
+          const int tok = RASTER ? kv0_raster + run_offset_raster(p, c0 + key) : kv0 + c0 + key;
+          const long long off = (long long)tok * (D / 4) + (i - key * (D / 4));
           kx = kg[off];
           vx = vg[off];
         }
@@ -768,7 +680,7 @@ __global__ void __launch_bounds__(kF32Threads) attn_f32_kernel(const AttnParams 
   }
   if (row_ok) {
     const float inv = 1.0f / l;
-    float* dst = og + (long long)(t.row0 + tid) * D;
+    float* dst = og + (long long)q_tok * D;
 #pragma unroll
     for (int d = 0; d < D; ++d) dst[d] = o[d] * inv;
   }
@@ -789,11 +701,14 @@ void fill_params(const AttnProblem& pr, int rows_per_item, AttnParams* p) {
     p->unit_rows = pr.g.S;
     p->nt = p->nh = p->nw = 1;
     p->tau = pr.g.S;
+    p->H = p->W = p->ct = p->ch = p->cw = 1;
   } else {
     p->n_units = pr.g.n_tiles;
     p->unit_rows = pr.g.tau;
     p->nt = pr.g.nt; p->nh = pr.g.nh; p->nw = pr.g.nw;
     p->tau = pr.g.tau;
+    p->H = pr.g.H; p->W = pr.g.W;
+    p->ct = pr.g.ct; p->ch = pr.g.ch; p->cw = pr.g.cw;
     for (int h = 0; h < pr.heads; ++h)
       for (int a = 0; a < 3; ++a) p->omega[h][a] = pr.omega[h][a];
   }
@@ -803,6 +718,13 @@ void fill_params(const AttnProblem& pr, int rows_per_item, AttnParams* p) {
   p->per_xcd = (int)((tasks + kXcds - 1) / kXcds);
 }
 
+// LDS for the raster offsets of the longest window run, omega_w * tau keys.
+unsigned raster_table_bytes(const AttnProblem& pr) {
+  int run = 0;
+  for (int h = 0; h < pr.heads; ++h) run = pr.omega[h][2] * pr.g.tau > run ? pr.omega[h][2] * pr.g.tau : run;
+  return (unsigned)run * sizeof(int);
+}
+
 template <int D, int WAVES, int RB, int BN>
 int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
@@ -810,45 +732,14 @@ int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
   fill_params(pr, C::kRows, &p);
   const unsigned grid = (unsigned)p.per_xcd * kXcds;
   if (pr.dense)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true>), dim3(grid), dim3(C::kThreads),
-                       0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false>), dim3(grid), dim3(C::kThreads),
-                       0, stream, p);
-  return (int)hipGetLastError();
-}
-
-template <int D, int WAVES, int RB, int BN>
-int launch_bf16_sp(const AttnProblem& pr, hipStream_t stream) {
-  using C = Bf16Cfg<D, WAVES, RB, BN>;
-  AttnParams p;
-  fill_params(pr, C::kRows, &p);
-  const unsigned grid = (unsigned)p.per_xcd * kXcds;
-  if (pr.dense)
-    hipLaunchKernelGGL((attn_bf16_sp_kernel<D, WAVES, RB, BN, true>), dim3(grid),
+    hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false>), dim3(grid),
                        dim3(C::kThreads), 0, stream, p);
+  else if (pr.raster)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true>), dim3(grid),
+                       dim3(C::kThreads), raster_table_bytes(pr), stream, p);
   else
-    hipLaunchKernelGGL((attn_bf16_sp_kernel<D, WAVES, RB, BN, false>), dim3(grid),
+    hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false>), dim3(grid),
                        dim3(C::kThreads), 0, stream, p);
-  return (int)hipGetLastError();
-}
-
-// Ping-pong kernel for 384-row work items.
-#ifndef STA_PP_GROUPING
-#define STA_PP_GROUPING 0
-#endif
-template <int D, int RB, int BN>
-int launch_bf16_pp(const AttnProblem& pr, hipStream_t stream) {
-  using C = Bf16Cfg<D, 8, RB, BN>;
-  AttnParams p;
-  fill_params(pr, C::kRows, &p);
-  const unsigned grid = (unsigned)p.per_xcd * kXcds;
-  if (pr.dense)
-    hipLaunchKernelGGL((attn_bf16_pp_kernel<D, RB, BN, true, STA_PP_GROUPING>), dim3(grid),
-                       dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_bf16_pp_kernel<D, RB, BN, false, STA_PP_GROUPING>), dim3(grid),
-                       dim3(512), 0, stream, p);
   return (int)hipGetLastError();
 }
 
@@ -857,7 +748,10 @@ int launch_f32(const AttnProblem& pr, hipStream_t stream) {
   AttnParams p;
   fill_params(pr, kF32Threads, &p);
   const unsigned grid = (unsigned)p.per_xcd * kXcds;
-  hipLaunchKernelGGL((attn_f32_kernel<D>), dim3(grid), dim3(kF32Threads), 0, stream, p);
+  if (pr.raster && !pr.dense)
+    hipLaunchKernelGGL((attn_f32_kernel<D, true>), dim3(grid), dim3(kF32Threads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_f32_kernel<D, false>), dim3(grid), dim3(kF32Threads), 0, stream, p);
   return (int)hipGetLastError();
 }
 
@@ -865,9 +759,6 @@ int launch_f32(const AttnProblem& pr, hipStream_t stream) {
 template <int D>
 int dispatch_bf16(const AttnProblem& pr, hipStream_t stream) {
   const int unit_rows = pr.dense ? pr.g.S : pr.g.tau;
-#ifndef STA_ATTN_VARIANT
-#define STA_ATTN_VARIANT 0
-#endif
 #ifndef STA_CFG_WAVES
 #define STA_CFG_WAVES 8
 #endif
@@ -878,12 +769,7 @@ int dispatch_bf16(const AttnProblem& pr, hipStream_t stream) {
 #define STA_CFG_BN 64
 #endif
   constexpr int kBigRows = STA_CFG_WAVES * 16 * STA_CFG_RB;
-  if (unit_rows % kBigRows == 0) {
-    if (STA_ATTN_VARIANT == 1) return launch_bf16_pp<D, 3, 64>(pr, stream);
-    if (STA_ATTN_VARIANT == 2)
-      return launch_bf16_sp<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN>(pr, stream);
-    return launch_bf16<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN>(pr, stream);
-  }
+  if (unit_rows % kBigRows == 0) return launch_bf16<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN>(pr, stream);
   if (unit_rows <= 64) return launch_bf16<D, 4, 1, 64>(pr, stream);
   return launch_bf16<D, 4, 2, 64>(pr, stream);
 }

@@ -11,6 +11,10 @@
 
 namespace sta {
 
+// Largest window run, omega_w * tau keys, the raster-order attention handles
+// (the run's table of raster offsets is kept in LDS).
+constexpr int kMaxRasterRun = 8192;
+
 struct AttnProblem {
   const void* q;
   const void* k;
@@ -20,6 +24,7 @@ struct AttnProblem {
   int dtype;       // sta_dtype
   float scale;
   bool dense;      // true: every query attends to all S keys
+  bool raster;     // STA only: q, k, v, out in raster order (else tile-major)
   Geometry g;      // for dense problems only g.S is used
   // Window per head in tiles (sparse problems only).
   uint16_t omega[STA_MAX_HEADS][3];

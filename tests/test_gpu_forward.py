@@ -14,11 +14,12 @@ from tests.parity_util import assert_close, default_scale, to_gpu
 pytestmark = pytest.mark.gpu
 
 
-def run_sta(inp: workloads.Inputs, scale=None):
-    """The whole path: raster inputs -> reorder -> forward -> restore -> numpy."""
+def run_sta(inp: workloads.Inputs, scale=None, fused=True):
+    """The whole path on raster inputs -> numpy. fused: the one raster-order
+    kernel; else reorder -> tile-major forward -> restore."""
     w = inp.workload
     q, k, v = (to_gpu(x, w.dtype) for x in (inp.q, inp.k, inp.v))
-    out = binding.sliding_tile_attention(q, k, v, w.tile, inp.windows, scale)
+    out = binding.sliding_tile_attention(q, k, v, w.tile, inp.windows, scale, fused=fused)
     torch.cuda.synchronize()
     return out.float().cpu().numpy()
 
@@ -38,15 +39,48 @@ SMALL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["raster", "tile_major"])
 @pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: c[0])
-def test_forward_matches_oracle(case):
+def test_forward_matches_oracle(case, fused):
     name, volume, tile, windows, d, dtype = case
     w = workloads.small_case(volume, tile, windows, head_dim=d, dtype=dtype, seed=11, name=name)
-    print(f"[case] forward {w}", flush=True)
+    print(f"[case] forward fused={fused} {w}", flush=True)
     inp = workloads.make_inputs(w)
-    got = run_sta(inp)
+    got = run_sta(inp, fused=fused)
     ref = oracle.sta_attention(inp.q, inp.k, inp.v, tile, inp.windows, default_scale(d))
     assert_close(got, ref, dtype, name)
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: c[0])
+def test_raster_kernel_equals_three_call_path(case):
+    """The raster-order kernel does the same arithmetic in the same order as
+    reorder + tile-major forward + restore, so the outputs agree bit for bit."""
+    name, volume, tile, windows, d, dtype = case
+    w = workloads.small_case(volume, tile, windows, head_dim=d, dtype=dtype, B=2, seed=12, name=name)
+    print(f"[case] raster vs tile-major {w}", flush=True)
+    inp = workloads.make_inputs(w)
+    a = run_sta(inp, fused=True)
+    b = run_sta(inp, fused=False)
+    assert np.array_equal(a, b), f"{name}: max diff {np.abs(a - b).max()}"
+
+
+def test_raster_run_limit():
+    """A window run longer than the raster kernel's offset table (8192 keys) is
+    refused by sta_forward_raster; sliding_tile_attention then takes the
+    reorder path."""
+    w = workloads.small_case((1, 1, 8200), (1, 1, 8), [(1, 1, 8200)], head_dim=64, seed=13,
+                             name="run_8200")
+    print(f"[case] raster limit {w}", flush=True)
+    inp = workloads.make_inputs(w)
+    q, k, v = (to_gpu(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    assert not binding.raster_run_fits(w.tile, inp.windows, 1)
+    assert binding.raster_run_fits(w.tile, [(1, 1, 8192)], 1)
+    with pytest.raises(NotImplementedError):
+        binding.sta_forward_raster(q, k, v, w.tile, inp.windows)
+    got = run_sta(inp)
+    # The window spans the whole volume, so STA is full attention here.
+    ref = oracle.full_attention(inp.q, inp.k, inp.v, default_scale(64)).reshape(got.shape)
+    assert_close(got, ref, "bf16", w.name)
 
 
 def test_forward_batch_and_sinusoid():
@@ -146,3 +180,8 @@ def test_invalid_inputs_raise_before_launch():
     with pytest.raises(TypeError):
         x = torch.zeros((1, 1, 384, 128), dtype=torch.float16, device="cuda")
         binding.sta_forward(x, x.clone(), x.clone(), (6, 8, 8), (6, 8, 8), [(6, 8, 8)])
+    r = torch.zeros((1, 1, 6, 8, 8, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        binding.sta_forward_raster(r, r.clone(), r.clone(), (6, 8, 8), [(6, 8, 16)])
+    with pytest.raises(ValueError):
+        binding.sta_forward_raster(r, r.clone(), r, (6, 8, 8), [(6, 8, 8)], out=r)

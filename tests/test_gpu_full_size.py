@@ -1,7 +1,8 @@
 """GPU: the four 30x48x80 workloads at full size, in the launch configuration
-the benchmark times. The oracle computes sampled query rows one by one
-(corner, edge and interior tiles of several heads); whole-volume STA is also
-compared element by element with the dense kernel."""
+the benchmark times (the raster-order kernel). The oracle computes sampled
+query rows one by one (corner, edge and interior tiles of several heads);
+whole-volume STA is also compared element by element with the dense kernel,
+and the raster-order kernel with the reorder + tile-major path."""
 
 import numpy as np
 import pytest
@@ -68,3 +69,14 @@ def test_full_size_sampled_rows(w):
         print(f"[parity] whole-volume STA vs dense: max {diff.max().item():.3e} "
               f"mean {diff.mean().item():.3e}", flush=True)
         assert diff.max().item() <= 2e-2 and diff.mean().item() <= 2e-3
+
+
+@pytest.mark.parametrize("w", [workloads.STA_18_24_24, workloads.MIXED_HEADS], ids=lambda w: w.name)
+def test_full_size_raster_equals_three_call_path(w):
+    print(f"[case] full size {w.name}: raster kernel vs reorder path", flush=True)
+    inp = workloads.make_inputs(w)
+    q, k, v = (to_gpu(x, w.dtype) for x in (inp.q, inp.k, inp.v))
+    a = binding.sliding_tile_attention(q, k, v, w.tile, inp.windows, fused=True)
+    b = binding.sliding_tile_attention(q, k, v, w.tile, inp.windows, fused=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
