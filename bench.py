@@ -17,7 +17,8 @@ Printed as one JSON line. Besides the contract fields it carries
   cpu_baseline  the CPU oracle timed on a bounded sample of the workload;
   dense         the dense comparator at the same shape and the speed-up;
   three_call    the reorder -> tile-major forward -> restore path, with the
-                permutation kernels' achieved HBM bandwidth.
+                permutation kernels' achieved HBM bandwidth;
+  other_workloads  the fused kernel on the other named workloads.
 """
 
 from __future__ import annotations
@@ -108,6 +109,44 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+def other_workloads(main_w, args, torch, binding, workloads, q, k, v, out, stream, ev):
+    """The fused kernel on every other named workload: average launch time,
+    effective TFLOP/s and fraction of peak. Workloads of the headline shape
+    reuse its device tensors (timing does not depend on the values)."""
+    res = {}
+    for w in workloads.NAMED:
+        if w.name == main_w.name:
+            continue
+        windows = workloads.head_windows(w)
+        if not binding.raster_run_fits(w.tile, windows, w.heads):
+            continue
+        flops = algorithmic_flops(w, windows)
+        same = (w.B, w.heads, w.head_dim, tuple(w.volume), w.dtype) == \
+            (main_w.B, main_w.heads, main_w.head_dim, tuple(main_w.volume), main_w.dtype)
+        if same:
+            a, b, c, o = q, k, v, out
+        else:
+            a, b, c = gpu_inputs(w, torch)
+            o = torch.empty_like(a)
+        binding.sta_forward_raster(a, b, c, w.tile, windows, out=o)  # warm-up
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(args.config_reps):
+            binding.sta_forward_raster(a, b, c, w.tile, windows, out=o)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.config_reps
+        tf = flops / (ms * 1e-3) / 1e12
+        peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
+        res[w.name] = {"ms": ms, "tflops": tf, "frac_of_peak": tf / peak, "dtype": w.dtype,
+                       "algorithmic_tflop": flops / 1e12,
+                       "windows": sorted({tuple(x) for x in windows.tolist()})}
+        if not same:
+            del a, b, c, o
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +159,8 @@ def main(argv=None):
                     help="steps of the other path to time for comparison (0: skip)")
     ap.add_argument("--dense-reps", type=int, default=2, help="dense comparator launches to time (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--config-reps", type=int, default=3,
+                    help="launches per other named workload to time (0: skip)")
     ap.add_argument("--copy-reference", action="store_true",
                     help="run one plain device copy of a q-sized tensor first (counter calibration)")
     args = ap.parse_args(argv)
@@ -238,6 +279,10 @@ def main(argv=None):
                  "speedup_sta_vs_dense": dense_ms / attn_ms}
         del qd, kd, vd, od
 
+    others = None
+    if args.config_reps > 0:
+        others = other_workloads(w, args, torch, binding, workloads, q, k, v, out, stream, ev)
+
     cpu = cpu_baseline(w, args.cpu_budget) if args.cpu_budget > 0 else None
 
     result = {
@@ -276,6 +321,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "dense": dense,
         "three_call": three,
+        "other_workloads": others,
     }
     print(json.dumps(result), flush=True)
     return 0
