@@ -18,6 +18,7 @@ Printed as one JSON line. Besides the contract fields it carries
   dense         the dense comparator at the same shape and the speed-up;
   three_call    the reorder -> tile-major forward -> restore path, with the
                 permutation kernels' achieved HBM bandwidth;
+  backward      sta_forward_lse + sta_backward at the same shape;
   other_workloads  the fused kernel on the other named workloads.
 """
 
@@ -109,6 +110,45 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+def time_backward(w, args, torch, binding, q, k, v, windows, fwd_flops, stream, ev):
+    """sta_forward_lse + sta_backward (raster order) on the headline inputs with
+    a seeded N(0,1) upstream gradient. TFLOP/s count the five products of the
+    usual attention backward (QK^T, dO V^T, P^T dO, dS^T Q, dS K: 2.5 x the
+    forward's FLOPs); the kernels issue seven (QK^T and dO V^T are recomputed
+    on both the key side and the query side), reported as mfma_tflops."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed + 1000)
+    dout = torch.randn(q.shape, generator=g, device="cuda", dtype=torch.float32).to(q.dtype)
+    out, lse = binding.sta_forward_lse(q, k, v, w.tile, windows)
+    delta = torch.empty_like(lse)
+    binding.sta_backward(q, k, v, out, dout, lse, w.tile, windows, delta=delta)  # warm-up
+    torch.cuda.synchronize()
+    e0, e1, e2 = ev(), ev(), ev()
+    e0.record(stream)
+    for _ in range(args.backward_reps):
+        binding.sta_forward_lse(q, k, v, w.tile, windows, out=out, lse=lse)
+    e1.record(stream)
+    for _ in range(args.backward_reps):
+        grads = binding.sta_backward(q, k, v, out, dout, lse, w.tile, windows, delta=delta)
+    e2.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / args.backward_reps
+    bwd_ms = e1.elapsed_time(e2) / args.backward_reps
+    bwd_flops = 2.5 * fwd_flops
+    del grads, dout, out, lse, delta
+    return {
+        "forward_lse_ms": fwd_ms,
+        "backward_ms": bwd_ms,
+        "backward_tflops": bwd_flops / (bwd_ms * 1e-3) / 1e12,
+        "backward_frac_of_peak": bwd_flops / (bwd_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "backward_mfma_tflops": 3.5 * fwd_flops / (bwd_ms * 1e-3) / 1e12,
+        "algorithmic_tflop": bwd_flops / 1e12,
+        "train_step_ms": fwd_ms + bwd_ms,
+        "train_step_tflops": (fwd_flops + bwd_flops) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12,
+        "order": "raster",
+    }
+
+
 def other_workloads(main_w, args, torch, binding, workloads, q, k, v, out, stream, ev):
     """The fused kernel on every other named workload: average launch time,
     effective TFLOP/s and fraction of peak. Workloads of the headline shape
@@ -159,6 +199,8 @@ def main(argv=None):
                     help="steps of the other path to time for comparison (0: skip)")
     ap.add_argument("--dense-reps", type=int, default=2, help="dense comparator launches to time (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--backward-reps", type=int, default=3,
+                    help="STA backward launches to time at the headline workload (0: skip)")
     ap.add_argument("--config-reps", type=int, default=3,
                     help="launches per other named workload to time (0: skip)")
     ap.add_argument("--copy-reference", action="store_true",
@@ -279,6 +321,10 @@ def main(argv=None):
                  "speedup_sta_vs_dense": dense_ms / attn_ms}
         del qd, kd, vd, od
 
+    backward = None
+    if args.backward_reps > 0 and fused:
+        backward = time_backward(w, args, torch, binding, q, k, v, windows, flops, stream, ev)
+
     others = None
     if args.config_reps > 0:
         others = other_workloads(w, args, torch, binding, workloads, q, k, v, out, stream, ev)
@@ -321,6 +367,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "dense": dense,
         "three_call": three,
+        "backward": backward,
         "other_workloads": others,
     }
     print(json.dumps(result), flush=True)

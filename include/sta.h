@@ -1,5 +1,6 @@
 /*
- * libsta -- Sliding Tile Attention (STA) forward for AMD MI355X (gfx950).
+ * libsta -- Sliding Tile Attention (STA) forward and backward for AMD MI355X
+ * (gfx950).
  *
  * STA ("Fast Video Generation with Sliding Tile Attention") replaces full 3D
  * attention over a (T, H, W) latent video. The token grid is cut into tiles of
@@ -60,6 +61,11 @@ typedef enum {
   STA_F32 = 1   /* float32 storage and arithmetic */
 } sta_dtype;
 
+typedef enum {
+  STA_TILE_MAJOR = 0, /* tensors in tile-major token order */
+  STA_RASTER = 1      /* tensors in raster token order */
+} sta_order;
+
 /* Largest head count whose window table fits the kernel arguments. */
 #define STA_MAX_HEADS 256
 
@@ -103,6 +109,24 @@ int sta_kv_tiles(int* kv_list, int* kv_count, int heads, int T, int H, int W, co
                  const int* window, int max_kv, void* stream);
 
 /*
+ * The transposed relation: per head and key tile, the query tiles whose
+ * window holds it, i.e. the query tiles that read the key tile and so
+ * receive gradient from it. Needed by the backward pass, which is organised
+ * by key tile; under the clamped window rule it differs from the key tiles'
+ * own windows (a corner key tile is read by 2 x 2 x 2 query tiles at the
+ * 30x48x80 / (6,8,8) / (18,24,24) geometry, a central one by 3 x 3 x 3 or
+ * more). Per axis the query tiles form one contiguous interval.
+ *   q_list:  device int32 [heads][N_t][max_q]; entries 0..count-1 hold the
+ *            query tile indices in ascending order, the rest are -1.
+ *   q_count: device int32 [heads][N_t].
+ *   max_q:   row length of q_list; must be >= the longest list (else
+ *            STA_ERR_INVALID_ARG, and sta_last_error() names the length).
+ * Other arguments as sta_kv_tiles.
+ */
+int sta_q_tiles(int* q_list, int* q_count, int heads, int T, int H, int W, const int* tile,
+                const int* window, int max_q, void* stream);
+
+/*
  * Number of computed (query tile, key tile) pairs summed over heads, for one
  * batch entry: sum_h N_t * prod_a omega_a. Host only; enqueues nothing.
  * Returns a negative sta_status on invalid arguments.
@@ -144,6 +168,50 @@ int sta_forward(const void* q, const void* k, const void* v, void* out, int B, i
 int sta_forward_raster(const void* q, const void* k, const void* v, void* out, int B, int heads,
                        int head_dim, int T, int H, int W, const int* tile, const int* window,
                        float scale, int dtype, void* stream);
+
+/*
+ * STA forward that also writes, per query row, the log-sum-exp of its scores
+ *     lse_i = log sum_j exp(scale * q_i . k_j)   over the row's window keys
+ * (natural log, float32), which the backward pass needs to recompute the
+ * probabilities. Output values are identical to sta_forward (order =
+ * STA_TILE_MAJOR) or sta_forward_raster (order = STA_RASTER).
+ *   lse:   device float [B][heads][S], 4-byte aligned, same token order as
+ *          q; written. Must not overlap q, k, v or out.
+ *   order: sta_order of q, k, v, out and lse.
+ * Other arguments and rules as sta_forward / sta_forward_raster.
+ */
+int sta_forward_lse(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                    int heads, int head_dim, int T, int H, int W, const int* tile,
+                    const int* window, float scale, int dtype, int order, void* stream);
+
+/*
+ * STA backward: gradients of sum(dout * O) with respect to q, k and v, for
+ * training a model with a fixed STA window (the fine-tuning of the pages:
+ * podcast transcript, the answer on fine-tuning; atlas.scime.ai summary,
+ * "Approach"; dianyo ICML2025 blog, STA section). With P the window softmax
+ * of the forward, recomputed as P_ij = exp(scale * q_i . k_j - lse_i):
+ *     dV = P^T dO,  dS = P * (dO V^T - D),  D_i = dO_i . O_i,
+ *     dQ = scale * dS K,  dK = scale * dS^T Q.
+ *   q, k, v:    forward inputs; out: forward output O; dout: dO. Device,
+ *               [B][heads][S][head_dim], token order `order`, read.
+ *   lse:        device float [B][heads][S] from sta_forward_lse, read.
+ *   dq, dk, dv: device, same shape and order as q, written (every element).
+ *   delta:      device float [B][heads][S] workspace owned by the caller;
+ *               overwritten with D. Must stay alive until the stream has
+ *               passed the work.
+ * Outputs and the workspace must not overlap any input or one another.
+ * Accumulation is float32. For STA_BF16 the recomputed P and dS are rounded
+ * to bfloat16 before they enter a matrix product, and the gradients are
+ * rounded to bfloat16. Each gradient element is computed by one work item
+ * (no atomics): results are deterministic. With order = STA_RASTER the
+ * window runs and their transposes (the longest interval of query tiles
+ * along w times tau) must be at most 8192 tokens, else STA_ERR_UNSUPPORTED.
+ * Other arguments and rules as sta_forward.
+ */
+int sta_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int heads,
+                 int head_dim, int T, int H, int W, const int* tile, const int* window,
+                 float scale, int dtype, int order, void* stream);
 
 /*
  * Full softmax attention over all S keys (the computation STA replaces, used

@@ -132,14 +132,24 @@ def sta_backward(q, k, v, dout, tile, windows, scale):
     return dq, dk, dv
 
 
+def _visible_columns(allowed):
+    """Key tokens some query row of ``allowed`` sees; every other key has
+    P = 0 for all these rows and drops out of every sum."""
+    return np.nonzero(allowed.any(axis=0))[0]
+
+
 def sta_backward_query_rows(q, k, v, dout, tile, window, scale, b, h, query_tokens):
     """dQ for the given raster query tokens of (b, h), float64 (R, d)."""
     volume = q.shape[2:5]
     qf, kf, vf, dof = (_rows_f64(x, b, h) for x in (q, k, v, dout))
     rows = np.asarray(query_tokens)
     allowed = token_mask_rows(volume, tile, window, rows)
-    gq, _, _ = _tile_backward(qf, kf, vf, dof, rows, allowed, scale)
-    return gq
+    cols = _visible_columns(allowed)
+    p, _ = _softmax_rows(qf[rows], kf[cols], allowed[:, cols], scale)
+    o = p @ vf[cols]
+    do = dof[rows]
+    ds = p * (do @ vf[cols].T - np.sum(do * o, axis=1, keepdims=True))
+    return scale * (ds @ kf[cols])
 
 
 def sta_backward_key_rows(q, k, v, dout, tile, window, scale, b, h, key_tokens):
@@ -165,11 +175,14 @@ def sta_backward_key_rows(q, k, v, dout, tile, window, scale, b, h, key_tokens):
     for i in q_tiles:
         rows = tile_tokens(volume, tile, int(i))
         allowed = token_mask_rows(volume, tile, window, rows)
-        p, _ = _softmax_rows(qf[rows], kf, allowed, scale)
-        o = p @ vf
+        cols = _visible_columns(allowed)
+        p, _ = _softmax_rows(qf[rows], kf[cols], allowed[:, cols], scale)
+        o = p @ vf[cols]
         do = dof[rows]
         delta = np.sum(do * o, axis=1, keepdims=True)
-        pk = p[:, keys]
+        # P of the requested keys (0 where the tile does not see the key)
+        pos = np.minimum(np.searchsorted(cols, keys), len(cols) - 1)
+        pk = np.where((cols[pos] == keys)[None, :], p[:, pos], 0.0)
         ds = pk * (do @ vf[keys].T - delta)
         gk += scale * (ds.T @ qf[rows])
         gv += pk.T @ do

@@ -107,13 +107,13 @@ def token_mask_rows(volume, tile, window, query_tokens: np.ndarray) -> np.ndarra
     """
     tile_grid(volume, tile)
     om = window_in_tiles(window, tile, volume)
-    coords = token_coords(volume)
-    qc = coords[np.asarray(query_tokens)]  # (R, 3)
-    allowed = np.ones((qc.shape[0], coords.shape[0]), dtype=bool)
-    for a in range(3):
-        am = axis_mask(volume[a], tile[a], om[a])
-        allowed &= am[qc[:, a]][:, coords[:, a]]
-    return allowed
+    T, H, W = volume
+    qc = token_coords(volume)[np.asarray(query_tokens)]  # (R, 3)
+    at, ah, aw = (axis_mask(volume[a], tile[a], om[a])[qc[:, a]] for a in range(3))  # (R, extent_a)
+    # key token (t, y, x) is visible iff it is inside along t AND y AND x;
+    # the key axis is raster order, so the (R, T, H, W) AND flattens to (R, S)
+    allowed = at[:, :, None, None] & ah[:, None, :, None] & aw[:, None, None, :]
+    return allowed.reshape(qc.shape[0], T * H * W)
 
 
 def tile_tokens(volume, tile, tile_index: int) -> np.ndarray:

@@ -11,11 +11,15 @@ from .binding import (  # noqa: F401
     load_library,
     raster_run_fits,
     sliding_tile_attention,
+    sta_attention,
+    sta_backward,
     sta_forward,
+    sta_forward_lse,
     sta_forward_raster,
     sta_full_attention,
     sta_kv_pair_count,
     sta_kv_tiles,
+    sta_q_tiles,
     sta_reorder_tiles,
     sta_restore_order,
 )

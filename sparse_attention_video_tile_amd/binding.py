@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_PKG, "libsta.so")
 STA_OK, STA_ERR_INVALID_ARG, STA_ERR_UNSUPPORTED, STA_ERR_HIP = 0, -1, -2, -3
 STA_BF16, STA_F32 = 0, 1
 STA_MAX_HEADS = 256
-ABI_VERSION = 2
+ABI_VERSION = 3
+STA_TILE_MAJOR, STA_RASTER = 0, 1
 # Longest window run (omega_w * tau keys) sta_forward_raster accepts.
 STA_MAX_RASTER_RUN = 8192
 
@@ -30,9 +31,12 @@ EXPORTS = (
     "sta_reorder_tiles",
     "sta_restore_order",
     "sta_kv_tiles",
+    "sta_q_tiles",
     "sta_kv_pair_count",
     "sta_forward",
     "sta_forward_raster",
+    "sta_forward_lse",
+    "sta_backward",
     "sta_full_attention",
     "sta_last_error",
 )
@@ -70,8 +74,17 @@ def load_library(path: str = None) -> ctypes.CDLL:
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, int3, c_int, c_void_p]
-    lib.sta_kv_tiles.restype = c_int
-    lib.sta_kv_tiles.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, int3, int3, c_int, c_void_p]
+    for name in ("sta_kv_tiles", "sta_q_tiles"):
+        f = getattr(lib, name)
+        f.restype = c_int
+        f.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, int3, int3, c_int, c_void_p]
+    lib.sta_forward_lse.restype = c_int
+    lib.sta_forward_lse.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int,
+                                    c_int, c_int, c_int, c_int, int3, int3, c_float, c_int, c_int,
+                                    c_void_p]
+    lib.sta_backward.restype = c_int
+    lib.sta_backward.argtypes = [c_void_p] * 10 + [c_int, c_int, c_int, c_int, c_int, c_int, int3,
+                                                   int3, c_float, c_int, c_int, c_void_p]
     lib.sta_kv_pair_count.restype = ctypes.c_longlong
     lib.sta_kv_pair_count.argtypes = [c_int, c_int, c_int, c_int, int3, int3]
     for name in ("sta_forward", "sta_forward_raster"):
@@ -196,25 +209,54 @@ def sta_kv_pair_count(heads: int, volume: Sequence[int], tile: Sequence[int], wi
     return int(n)
 
 
-def sta_kv_tiles(heads: int, volume: Sequence[int], tile: Sequence[int], window,
-                 max_kv: Optional[int] = None, device="cuda") -> Tuple[torch.Tensor, torch.Tensor]:
-    """Per head and query tile, the window's key tiles (ascending) and their count."""
+def _tile_lists(fn_name: str, heads: int, volume, tile, window, max_len, device, transposed: bool):
     lib = load_library()
     T, H, W = (int(a) for a in volume)
     ws = _windows_per_head(window, heads)
-    n_tiles = (T // int(tile[0])) * (H // int(tile[1])) * (W // int(tile[2]))
-    if max_kv is None:
-        max_kv = max(
-            (ws[3 * h] // int(tile[0])) * (ws[3 * h + 1] // int(tile[1])) * (ws[3 * h + 2] // int(tile[2]))
-            for h in range(heads))
-    kv_list = torch.empty((heads, n_tiles, max_kv), dtype=torch.int32, device=device)
-    kv_count = torch.empty((heads, n_tiles), dtype=torch.int32, device=device)
-    dev = _require_gpu(kv_list, kv_count)
+    n = [int(e) // int(c) for e, c in zip((T, H, W), tile)]
+    n_tiles = n[0] * n[1] * n[2]
+    if max_len is None:
+        max_len = 0
+        for h in range(heads):
+            prod = 1
+            for a in range(3):
+                om = ws[3 * h + a] // int(tile[a])
+                if transposed:  # longest interval of query tiles along this axis
+                    om = max(_inverse_len(j, n[a], om) for j in range(n[a])) if n[a] > 0 else 0
+                prod *= om
+            max_len = max(max_len, prod)
+    lists = torch.empty((heads, n_tiles, max_len), dtype=torch.int32, device=device)
+    counts = torch.empty((heads, n_tiles), dtype=torch.int32, device=device)
+    dev = _require_gpu(lists, counts)
     with torch.cuda.device(dev):
-        rc = lib.sta_kv_tiles(kv_list.data_ptr(), kv_count.data_ptr(), heads, T, H, W,
-                              _int_array(tile), _int_array(ws), max_kv, _stream(dev))
-    _check(rc, "sta_kv_tiles")
-    return kv_list, kv_count
+        rc = getattr(lib, fn_name)(lists.data_ptr(), counts.data_ptr(), heads, T, H, W,
+                                   _int_array(tile), _int_array(ws), max_len, _stream(dev))
+    _check(rc, fn_name)
+    return lists, counts
+
+
+def _inverse_len(j: int, n: int, omega: int) -> int:
+    """Number of query tiles along an axis whose window holds key tile j
+    (for sizing only; the library computes the lists)."""
+    if omega <= 0 or omega > n:
+        return 0
+    half = omega // 2
+    hi = n - 1 if j >= n - omega else j + half
+    a = j - omega + 1
+    lo = 0 if a <= 0 else a + half
+    return hi - lo + 1
+
+
+def sta_kv_tiles(heads: int, volume: Sequence[int], tile: Sequence[int], window,
+                 max_kv: Optional[int] = None, device="cuda") -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per head and query tile, the window's key tiles (ascending) and their count."""
+    return _tile_lists("sta_kv_tiles", heads, volume, tile, window, max_kv, device, False)
+
+
+def sta_q_tiles(heads: int, volume: Sequence[int], tile: Sequence[int], window,
+                max_q: Optional[int] = None, device="cuda") -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per head and key tile, the query tiles whose window holds it (ascending) and their count."""
+    return _tile_lists("sta_q_tiles", heads, volume, tile, window, max_q, device, True)
 
 
 def sta_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, volume: Sequence[int],
@@ -296,12 +338,126 @@ def sta_forward_raster(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tile: 
     return out
 
 
-def raster_run_fits(tile: Sequence[int], window, heads: int) -> bool:
-    """Whether every head's window run (omega_w * tau keys) is within what
-    sta_forward_raster accepts."""
+def raster_run_fits(tile: Sequence[int], window, heads: int, volume: Optional[Sequence[int]] = None,
+                    backward: bool = False) -> bool:
+    """Whether every window run (omega_w * tau keys) -- and, for the backward
+    (which needs the volume), every transposed run -- is within what the
+    raster-order kernels accept."""
     ws = _windows_per_head(window, heads)
     tau = int(tile[0]) * int(tile[1]) * int(tile[2])
-    return all((ws[3 * h + 2] // int(tile[2])) * tau <= STA_MAX_RASTER_RUN for h in range(heads))
+    for h in range(heads):
+        om = ws[3 * h + 2] // int(tile[2])
+        if om * tau > STA_MAX_RASTER_RUN:
+            return False
+        if backward:
+            nw = int(volume[2]) // int(tile[2])
+            if max(_inverse_len(j, nw, om) for j in range(nw)) * tau > STA_MAX_RASTER_RUN:
+                return False
+    return True
+
+
+def _order_shapes(q: torch.Tensor, volume):
+    """(B, heads, d, (T, H, W), order code) of a raster 6-D or tile-major 4-D tensor."""
+    if q.dim() == 6:
+        B, heads, T, H, W, d = q.shape
+        return B, heads, d, (T, H, W), STA_RASTER
+    if q.dim() == 4:
+        if volume is None:
+            raise ValueError("tile-major (B, heads, S, d) tensors need the volume")
+        B, heads, S, d = q.shape
+        T, H, W = (int(a) for a in volume)
+        if S != T * H * W:
+            raise ValueError(f"S={S} does not match volume {tuple(volume)}")
+        return B, heads, d, (T, H, W), STA_TILE_MAJOR
+    raise ValueError("tensors must be raster (B, heads, T, H, W, d) or tile-major (B, heads, S, d)")
+
+
+def sta_forward_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tile: Sequence[int], window,
+                    scale: Optional[float] = None, volume: Optional[Sequence[int]] = None,
+                    out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """STA forward returning (out, lse). Raster (B, heads, T, H, W, d) tensors,
+    or tile-major (B, heads, S, d) ones with `volume`; lse is float32 of the
+    tensors' shape without d."""
+    lib = load_library()
+    if q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    B, heads, d, (T, H, W), order = _order_shapes(q, volume)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is None:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    elif lse.shape != q.shape[:-1] or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of q's shape without d")
+    dev = _require_gpu(q, k, v, out, lse)
+    with torch.cuda.device(dev):
+        rc = lib.sta_forward_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr(), B, heads, d, T, H, W, _int_array(tile),
+                                 _int_array(_windows_per_head(window, heads)), float(scale),
+                                 _dtype_code(q), order, _stream(dev))
+    _check(rc, "sta_forward_lse")
+    return out, lse
+
+
+def sta_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                 dout: torch.Tensor, lse: torch.Tensor, tile: Sequence[int], window,
+                 scale: Optional[float] = None, volume: Optional[Sequence[int]] = None,
+                 delta: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Gradients (dq, dk, dv) of sum(dout * out) for out = STA(q, k, v), from
+    the forward's out and lse. Same token order conventions as sta_forward_lse;
+    `delta` is an optional float32 workspace shaped like lse."""
+    lib = load_library()
+    for name, x in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if x.shape != q.shape or x.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    B, heads, d, (T, H, W), order = _order_shapes(q, volume)
+    if lse.shape != q.shape[:-1] or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of q's shape without d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if delta is None:
+        delta = torch.empty_like(lse)
+    elif delta.shape != lse.shape or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 tensor shaped like lse")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dev = _require_gpu(q, k, v, out, dout, lse, delta, dq, dk, dv)
+    with torch.cuda.device(dev):
+        rc = lib.sta_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), delta.data_ptr(), B, heads, d, T, H, W,
+                              _int_array(tile), _int_array(_windows_per_head(window, heads)),
+                              float(scale), _dtype_code(q), order, _stream(dev))
+    _check(rc, "sta_backward")
+    return dq, dk, dv
+
+
+class _STAFunction(torch.autograd.Function):
+    """Autograd wrapper: forward via sta_forward_lse, backward via sta_backward."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, tile, window, scale, volume):
+        out, lse = sta_forward_lse(q, k, v, tile, window, scale, volume)
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.cfg = (tuple(tile), window, scale, volume)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse = ctx.saved_tensors
+        tile, window, scale, volume = ctx.cfg
+        dq, dk, dv = sta_backward(q, k, v, out, dout.contiguous(), lse, tile, window, scale, volume)
+        return dq, dk, dv, None, None, None, None
+
+
+def sta_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tile: Sequence[int], window,
+                  scale: Optional[float] = None, volume: Optional[Sequence[int]] = None) -> torch.Tensor:
+    """STA as a differentiable torch op (raster 6-D tensors, or tile-major 4-D
+    ones with `volume`); gradients come from sta_backward."""
+    return _STAFunction.apply(q.contiguous(), k.contiguous(), v.contiguous(), tile, window, scale, volume)
 
 
 def sliding_tile_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tile: Sequence[int],

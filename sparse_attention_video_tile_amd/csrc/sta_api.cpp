@@ -146,15 +146,84 @@ int attention_common(sta::AttnProblem& p, void* stream) {
   return launched(rc);
 }
 
-int forward_common(const void* q, const void* k, const void* v, void* out, int B, int heads,
-                   int head_dim, int T, int H, int W, const int* tile, const int* window,
-                   float scale, int dtype, void* stream, bool raster);
+// Longest list of sta_kv_tiles (transposed = false) or sta_q_tiles (true)
+// over heads and tiles, and the longest run along w of such a list in tiles.
+void list_extents(const sta::Geometry& g, int heads, const uint16_t (*omega)[3], bool transposed,
+                  int* longest, int* longest_w) {
+  *longest = 0;
+  *longest_w = 0;
+  const int n[3] = {g.nt, g.nh, g.nw};
+  for (int h = 0; h < heads; ++h) {
+    int prod = 1;
+    for (int a = 0; a < 3; ++a) {
+      int m = omega[h][a];
+      if (transposed) {
+        m = 0;
+        for (int j = 0; j < n[a]; ++j) {
+          int lo, hi;
+          sta::window_inverse(j, n[a], omega[h][a], &lo, &hi);
+          m = hi - lo + 1 > m ? hi - lo + 1 : m;
+        }
+      }
+      prod *= m;
+      if (a == 2 && m > *longest_w) *longest_w = m;
+    }
+    *longest = prod > *longest ? prod : *longest;
+  }
+}
+
+int tile_lists_common(int* list, int* count, int heads, int T, int H, int W, const int* tile,
+                      const int* window, int max_len, bool transposed, void* stream) {
+  if (!list || !count) return fail(STA_ERR_INVALID_ARG, "list or count is NULL");
+  if (heads <= 0 || heads > STA_MAX_HEADS)
+    return fail(STA_ERR_INVALID_ARG, "heads=%d must be in [1, %d]", heads, STA_MAX_HEADS);
+  sta::Geometry g;
+  int rc = check_volume(T, H, W, tile, &g);
+  if (rc) return rc;
+  uint16_t omega[STA_MAX_HEADS][3];
+  if ((rc = check_windows(g, heads, window, omega))) return rc;
+  int need, need_w;
+  list_extents(g, heads, omega, transposed, &need, &need_w);
+  if (max_len < need)
+    return fail(STA_ERR_INVALID_ARG, "list length %d is below the longest list %d", max_len, need);
+  const size_t list_bytes = (size_t)heads * g.n_tiles * max_len * sizeof(int);
+  const size_t count_bytes = (size_t)heads * g.n_tiles * sizeof(int);
+  if (overlaps(list, list_bytes, count, count_bytes))
+    return fail(STA_ERR_INVALID_ARG, "list and count overlap");
+  if ((long long)heads * g.n_tiles * max_len > (1LL << 31) - 1)
+    return fail(STA_ERR_INVALID_ARG, "list is too large");
+  return launched(sta::launch_kv_tiles(list, count, heads, g, omega, max_len, transposed, stream));
+}
+
+// Raster-order kernels keep the raster offsets of one run in LDS: both the
+// window runs (omega_w tiles) and, for the backward, the transposed runs must
+// fit.
+int check_raster_runs(const sta::Geometry& g, int heads, const uint16_t (*omega)[3], bool backward) {
+  int longest, longest_w;
+  list_extents(g, heads, omega, false, &longest, &longest_w);
+  long long run = (long long)longest_w * g.tau;
+  if (backward) {
+    list_extents(g, heads, omega, true, &longest, &longest_w);
+    const long long trun = (long long)longest_w * g.tau;
+    run = trun > run ? trun : run;
+  }
+  if (run > sta::kMaxRasterRun)
+    return fail(STA_ERR_UNSUPPORTED,
+                "raster order: a window run has %lld keys (limit %d); reorder to tile-major order "
+                "and use the tile-major entry point",
+                run, sta::kMaxRasterRun);
+  return STA_OK;
+}
+
+int forward_common(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                   int heads, int head_dim, int T, int H, int W, const int* tile,
+                   const int* window, float scale, int dtype, void* stream, bool raster);
 
 }  // namespace
 
 extern "C" {
 
-int sta_abi_version(void) { return 2; }
+int sta_abi_version(void) { return 3; }
 
 const char* sta_last_error(void) { return g_last_error.c_str(); }
 
@@ -185,57 +254,100 @@ long long sta_kv_pair_count(int heads, int T, int H, int W, const int* tile, con
 
 int sta_kv_tiles(int* kv_list, int* kv_count, int heads, int T, int H, int W, const int* tile,
                  const int* window, int max_kv, void* stream) {
-  if (!kv_list || !kv_count) return fail(STA_ERR_INVALID_ARG, "kv_list or kv_count is NULL");
-  if (heads <= 0 || heads > STA_MAX_HEADS)
-    return fail(STA_ERR_INVALID_ARG, "heads=%d must be in [1, %d]", heads, STA_MAX_HEADS);
-  sta::Geometry g;
-  int rc = check_volume(T, H, W, tile, &g);
-  if (rc) return rc;
-  uint16_t omega[STA_MAX_HEADS][3];
-  if ((rc = check_windows(g, heads, window, omega))) return rc;
-  int need = 0;
-  for (int h = 0; h < heads; ++h) {
-    const int c = omega[h][0] * omega[h][1] * omega[h][2];
-    need = c > need ? c : need;
-  }
-  if (max_kv < need) return fail(STA_ERR_INVALID_ARG, "max_kv=%d is below the largest count %d", max_kv, need);
-  const size_t list_bytes = (size_t)heads * g.n_tiles * max_kv * sizeof(int);
-  const size_t count_bytes = (size_t)heads * g.n_tiles * sizeof(int);
-  if (overlaps(kv_list, list_bytes, kv_count, count_bytes))
-    return fail(STA_ERR_INVALID_ARG, "kv_list and kv_count overlap");
-  if ((long long)heads * g.n_tiles * max_kv > (1LL << 31) - 1)
-    return fail(STA_ERR_INVALID_ARG, "kv_list is too large");
-  return launched(sta::launch_kv_tiles(kv_list, kv_count, heads, g, omega, max_kv, stream));
+  return tile_lists_common(kv_list, kv_count, heads, T, H, W, tile, window, max_kv, false, stream);
+}
+
+int sta_q_tiles(int* q_list, int* q_count, int heads, int T, int H, int W, const int* tile,
+                const int* window, int max_q, void* stream) {
+  return tile_lists_common(q_list, q_count, heads, T, H, W, tile, window, max_q, true, stream);
 }
 
 }  // extern "C"
 
 namespace {
 
-int forward_common(const void* q, const void* k, const void* v, void* out, int B, int heads,
-                   int head_dim, int T, int H, int W, const int* tile, const int* window,
-                   float scale, int dtype, void* stream, bool raster) {
+int forward_common(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                   int heads, int head_dim, int T, int H, int W, const int* tile,
+                   const int* window, float scale, int dtype, void* stream, bool raster) {
   if (heads <= 0 || heads > STA_MAX_HEADS)
     return fail(STA_ERR_INVALID_ARG, "heads=%d must be in [1, %d]", heads, STA_MAX_HEADS);
   static thread_local sta::AttnProblem p;
-  p.q = q; p.k = k; p.v = v; p.out = out;
+  p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
   p.B = B; p.heads = heads; p.head_dim = head_dim; p.dtype = dtype; p.scale = scale;
   p.dense = false;
   p.raster = raster;
   int rc = check_volume(T, H, W, tile, &p.g);
   if (rc) return rc;
   if ((rc = check_windows(p.g, heads, window, p.omega))) return rc;
-  if (raster) {
-    for (int h = 0; h < heads; ++h) {
-      const long long run = (long long)p.omega[h][2] * p.g.tau;
-      if (run > sta::kMaxRasterRun)
-        return fail(STA_ERR_UNSUPPORTED,
-                    "raster order: window run of head %d has %lld keys (limit %d); reorder to "
-                    "tile-major order and use sta_forward",
-                    h, run, sta::kMaxRasterRun);
-    }
+  if (raster && (rc = check_raster_runs(p.g, heads, p.omega, false))) return rc;
+  if (lse) {
+    if (reinterpret_cast<uintptr_t>(lse) % 4) return fail(STA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+    const int es = elem_size(dtype);
+    const size_t bytes = (size_t)B * heads * p.g.S * (es ? es : 1) * head_dim;
+    const size_t lbytes = (size_t)B * heads * p.g.S * sizeof(float);
+    if (overlaps(lse, lbytes, q, bytes) || overlaps(lse, lbytes, k, bytes) ||
+        overlaps(lse, lbytes, v, bytes) || overlaps(lse, lbytes, out, bytes))
+      return fail(STA_ERR_INVALID_ARG, "lse overlaps a tensor");
   }
   return attention_common(p, stream);
+}
+
+int backward_common(const void* q, const void* k, const void* v, const void* out,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    float* delta, int B, int heads, int head_dim, int T, int H, int W,
+                    const int* tile, const int* window, float scale, int dtype, int order,
+                    void* stream) {
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !delta)
+    return fail(STA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (order != STA_TILE_MAJOR && order != STA_RASTER)
+    return fail(STA_ERR_INVALID_ARG, "unknown token order %d", order);
+  if (heads <= 0 || heads > STA_MAX_HEADS)
+    return fail(STA_ERR_INVALID_ARG, "heads=%d must be in [1, %d]", heads, STA_MAX_HEADS);
+  int rc = check_heads(B, heads, head_dim);
+  if (rc) return rc;
+  const int es = elem_size(dtype);
+  if (!es) return fail(STA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (!(scale > 0.0f) || !isfinite(scale))
+    return fail(STA_ERR_INVALID_ARG, "scale %g must be finite and positive", (double)scale);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(STA_ERR_UNSUPPORTED, "head_dim %d: kernels exist for 64 and 128", head_dim);
+  static thread_local sta::BwdProblem pb;
+  sta::AttnProblem& p = pb.attn;
+  p.q = q; p.k = k; p.v = v; p.out = const_cast<void*>(out); p.lse = nullptr;
+  p.B = B; p.heads = heads; p.head_dim = head_dim; p.dtype = dtype; p.scale = scale;
+  p.dense = false;
+  p.raster = order == STA_RASTER;
+  if ((rc = check_volume(T, H, W, tile, &p.g))) return rc;
+  if ((rc = check_windows(p.g, heads, window, p.omega))) return rc;
+  if (p.raster && (rc = check_raster_runs(p.g, heads, p.omega, true))) return rc;
+  const uintptr_t any16 = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                          reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out) |
+                          reinterpret_cast<uintptr_t>(dout) | reinterpret_cast<uintptr_t>(dq) |
+                          reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv);
+  if (any16 % 16) return fail(STA_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(delta)) % 4)
+    return fail(STA_ERR_INVALID_ARG, "lse and delta must be 4-byte aligned");
+  const long long BH = (long long)B * heads;
+  if (BH > (1LL << 24)) return fail(STA_ERR_INVALID_ARG, "B*heads=%lld is too large", BH);
+  const size_t tb = (size_t)BH * p.g.S * head_dim * es;
+  const size_t rb = (size_t)BH * p.g.S * sizeof(float);
+  const void* ins[6] = {q, k, v, out, dout, lse};
+  const size_t in_bytes[6] = {tb, tb, tb, tb, tb, rb};
+  const void* outs[4] = {dq, dk, dv, delta};
+  const size_t out_bytes[4] = {tb, tb, tb, rb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j]))
+        return fail(STA_ERR_INVALID_ARG, "an output or the delta workspace overlaps an input");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j]))
+        return fail(STA_ERR_INVALID_ARG, "outputs overlap each other or the delta workspace");
+  }
+  pb.dout = dout; pb.lse = lse; pb.delta = delta;
+  pb.dq = dq; pb.dk = dk; pb.dv = dv;
+  rc = sta::launch_backward(pb, stream);
+  if (rc < 0) return fail(rc, "no kernel for dtype %d with head_dim %d", dtype, head_dim);
+  return launched(rc);
 }
 
 }  // namespace
@@ -245,15 +357,33 @@ extern "C" {
 int sta_forward(const void* q, const void* k, const void* v, void* out, int B, int heads,
                 int head_dim, int T, int H, int W, const int* tile, const int* window, float scale,
                 int dtype, void* stream) {
-  return forward_common(q, k, v, out, B, heads, head_dim, T, H, W, tile, window, scale, dtype,
-                        stream, false);
+  return forward_common(q, k, v, out, nullptr, B, heads, head_dim, T, H, W, tile, window, scale,
+                        dtype, stream, false);
 }
 
 int sta_forward_raster(const void* q, const void* k, const void* v, void* out, int B, int heads,
                        int head_dim, int T, int H, int W, const int* tile, const int* window,
                        float scale, int dtype, void* stream) {
-  return forward_common(q, k, v, out, B, heads, head_dim, T, H, W, tile, window, scale, dtype,
-                        stream, true);
+  return forward_common(q, k, v, out, nullptr, B, heads, head_dim, T, H, W, tile, window, scale,
+                        dtype, stream, true);
+}
+
+int sta_forward_lse(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                    int heads, int head_dim, int T, int H, int W, const int* tile,
+                    const int* window, float scale, int dtype, int order, void* stream) {
+  if (!lse) return fail(STA_ERR_INVALID_ARG, "lse is NULL");
+  if (order != STA_TILE_MAJOR && order != STA_RASTER)
+    return fail(STA_ERR_INVALID_ARG, "unknown token order %d", order);
+  return forward_common(q, k, v, out, lse, B, heads, head_dim, T, H, W, tile, window, scale,
+                        dtype, stream, order == STA_RASTER);
+}
+
+int sta_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int heads,
+                 int head_dim, int T, int H, int W, const int* tile, const int* window,
+                 float scale, int dtype, int order, void* stream) {
+  return backward_common(q, k, v, out, dout, lse, dq, dk, dv, delta, B, heads, head_dim, T, H, W,
+                         tile, window, scale, dtype, order, stream);
 }
 
 int sta_full_attention(const void* q, const void* k, const void* v, void* out, int B, int heads,
@@ -262,6 +392,7 @@ int sta_full_attention(const void* q, const void* k, const void* v, void* out, i
   static thread_local sta::AttnProblem p;
   memset(&p.g, 0, sizeof(p.g));
   p.raster = false;
+  p.lse = nullptr;
   p.q = q; p.k = k; p.v = v; p.out = out;
   p.B = B; p.heads = heads; p.head_dim = head_dim; p.dtype = dtype; p.scale = scale;
   p.dense = true;

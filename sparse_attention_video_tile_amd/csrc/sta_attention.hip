@@ -22,238 +22,10 @@
 // FMA arithmetic; it serves float32 problems.
 #include <hip/hip_runtime.h>
 
-#include "sta_kernels.h"
+#include "sta_attn_common.h"
 
 namespace sta {
 namespace {
-
-typedef __bf16 bf16_t;
-typedef bf16_t bf16x8 __attribute__((ext_vector_type(8)));
-typedef bf16_t bf16x4 __attribute__((ext_vector_type(4)));
-typedef bf16_t bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kXcds = 8;  // MI355X dispatches workgroups round-robin over 8 XCDs
-
-// Parameters shared by both kernels.
-struct AttnParams {
-  const void* q;
-  const void* k;
-  const void* v;
-  void* out;
-  int S;            // tokens per (batch, head)
-  int heads;
-  int n_tasks;      // work items
-  int per_xcd;      // ceil(n_tasks / kXcds)
-  int row_blocks;   // work items per query unit
-  int n_units;      // query units per (batch, head): tiles, or 1 if dense
-  int unit_rows;    // rows per query unit: tau, or S if dense
-  float scale_log2; // scale * log2(e)
-  int dense;
-  int nt, nh, nw, tau;
-  int H, W, ct, ch, cw;  // volume and tile, for raster-order addressing
-  uint16_t omega[STA_MAX_HEADS][3];
-};
-
-
-// Maps the hardware workgroup id to a logical task so that consecutive
-// logical tasks (the row blocks of one query tile, then neighbouring tiles
-// that share most of their keys) run on the same XCD and share its L2.
-__device__ __forceinline__ int logical_task(const AttnParams& p) {
-  const int bid = blockIdx.x;
-  return (bid % kXcds) * p.per_xcd + bid / kXcds;
-}
-
-// Key runs of one work item: `runs` runs of `run_len` tokens; run r starts at
-// token run_start(r).
-struct KvRuns {
-  int runs, run_len;
-  int oh;             // omega_h (runs per t-step)
-  int st, sh, sw;     // window start in tiles
-  int nh, nw, tau;
-  int dense;
-  // Token index (tile-major order) of run r's first key.
-  __device__ __forceinline__ int run_start(int r) const {
-    if (dense) return 0;
-    const int it = r / oh, ih = r - (r / oh) * oh;
-    return (((st + it) * nh + (sh + ih)) * nw + sw) * tau;
-  }
-  // Raster token index of run r's first key (the run's tile-major key e sits
-  // at this plus the run offset table entry e).
-  __device__ __forceinline__ int run_start_raster(int r, int H, int W, int ct, int ch, int cw) const {
-    const int it = r / oh, ih = r - (r / oh) * oh;
-    return (((st + it) * ct) * H + (sh + ih) * ch) * W + sw * cw;
-  }
-};
-
-struct Task {
-  long long head_base;  // element offset of this (batch, head)
-  int row0;             // first query row (token index) of the work item
-  int valid_rows;       // rows of the work item inside its unit
-  int local0;           // first row of the work item within its unit
-  int qt, qh, qw;       // query tile coordinates (STA)
-  KvRuns kv;
-};
-
-// Raster token index of row `local` (tile-major order inside the tile) of
-// query tile (qt, qh, qw).
-__device__ __forceinline__ int tile_row_raster(const AttnParams& p, int qt, int qh, int qw, int local) {
-  const int plane = p.ch * p.cw;
-  const int lt = local / plane;
-  const int rem = local - lt * plane;
-  const int lh = rem / p.cw;
-  const int lw = rem - lh * p.cw;
-  return ((qt * p.ct + lt) * p.H + qh * p.ch + lh) * p.W + qw * p.cw + lw;
-}
-
-// Raster offset, relative to the run's first key, of key e of a window run
-// (tile-major order within the run: tile along w, then the tile's tokens).
-__device__ __forceinline__ int run_offset_raster(const AttnParams& p, int e) {
-  const int tw = e / p.tau;
-  const int local = e - tw * p.tau;
-  const int plane = p.ch * p.cw;
-  const int lt = local / plane;
-  const int rem = local - lt * plane;
-  const int lh = rem / p.cw;
-  const int lw = rem - lh * p.cw;
-  return (lt * p.H + lh) * p.W + tw * p.cw + lw;
-}
-
-template <int ROWS>
-__device__ __forceinline__ Task decode_task(const AttnParams& p, int task, int D) {
-  Task t;
-  const int rb = task % p.row_blocks;
-  const int unit_bh = task / p.row_blocks;
-  const int unit = unit_bh % p.n_units;
-  const int bh = unit_bh / p.n_units;
-  const int h = bh % p.heads;
-  t.head_base = (long long)bh * p.S * D;
-  const int unit_row0 = unit * p.unit_rows;
-  t.row0 = unit_row0 + rb * ROWS;
-  t.local0 = rb * ROWS;
-  t.valid_rows = min(ROWS, p.unit_rows - rb * ROWS);
-  t.qt = t.qh = t.qw = 0;
-  KvRuns& kv = t.kv;
-  kv.dense = p.dense;
-  kv.nh = p.nh; kv.nw = p.nw; kv.tau = p.tau;
-  if (p.dense) {
-    kv.runs = 1; kv.run_len = p.S; kv.oh = 1; kv.st = kv.sh = kv.sw = 0;
-  } else {
-    const int ot = p.omega[h][0], oh = p.omega[h][1], ow = p.omega[h][2];
-    const int qw = unit % p.nw;
-    const int qh = (unit / p.nw) % p.nh;
-    const int qt = unit / (p.nw * p.nh);
-    t.qt = qt; t.qh = qh; t.qw = qw;
-    kv.st = window_start(qt, p.nt, ot);
-    kv.sh = window_start(qh, p.nh, oh);
-    kv.sw = window_start(qw, p.nw, ow);
-    kv.oh = oh;
-    kv.runs = ot * oh;
-    kv.run_len = ow * p.tau;
-  }
-  return t;
-}
-
-// Max / sum of x over the four lanes l, l^16, l^32, l^48 (the lanes that
-// hold one query row in the MFMA output layouts). A permlane swap of x with
-// itself yields, in its two results, x of this lane and of its partner lane
-// (l^16 for the 16-lane swap, l^32 for the 32-lane swap), in some order.
-__device__ __forceinline__ float pair16(float x, bool is_max) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-  return is_max ? fmaxf(a, b) : a + b;
-}
-__device__ __forceinline__ float pair32(float x, bool is_max) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-  return is_max ? fmaxf(a, b) : a + b;
-}
-__device__ __forceinline__ float row_max4(float x) { return pair32(pair16(x, true), true); }
-__device__ __forceinline__ float row_sum4(float x) { return pair32(pair16(x, false), false); }
-__device__ __forceinline__ float wave_xor_sum(float x, int mask) {
-  return x + __shfl_xor(x, mask, 64);
-}
-
-// ---------------------------------------------------------------------------
-// bf16 kernel
-// ---------------------------------------------------------------------------
-
-template <int D, int WAVES, int RB, int BN>
-struct Bf16Cfg {
-  static constexpr int kD = D;
-  static constexpr int kBN = BN;
-  static constexpr int kThreads = WAVES * 64;
-  static constexpr int kRowsWave = 16 * RB;
-  static constexpr int kRows = WAVES * kRowsWave;
-  static constexpr int kDK = D / 32;            // k-steps of S^T = K Q^T
-  static constexpr int kDB = D / 16;            // 16-row blocks of O^T
-  static constexpr int kKT = BN / 16;           // 16-key score tiles per chunk
-  static constexpr int kKP = BN / 32;           // 32-key steps of O^T += V^T P^T
-  static constexpr int kRowBytes = D * 2;       // one key row of K or V
-  static constexpr int kCPR = kRowBytes / 16;   // 16-byte chunks per row
-  static constexpr int kChunkBytes = BN * kRowBytes;       // K (or V) of one chunk
-  static constexpr int kBlocks = kChunkBytes / 1024;       // 1 KB LDS-DMA blocks per chunk
-  static constexpr int kRowsPerBlock = 1024 / kRowBytes;
-  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-};
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-// Physical byte offset of 16-byte chunk `c` of key row `row` in a K/V buffer.
-// Chunks are XOR-swizzled by the row so that the operand fetches of the MFMA
-// loops hit distinct LDS banks: with 256-byte rows every row starts at bank 0
-// and the chunk slot is c ^ rotl4(row % 16). The K fetch reads one chunk of
-// 16 consecutive rows (rotl4 is a bijection on 0..15); the transposing V
-// fetch reads chunks 2m and 2m+1 of 8 consecutive rows, which rotl4 also
-// spreads over 16 distinct slots. With 128-byte rows the slot is c ^ (row % 8).
-template <int CPR>
-__device__ __forceinline__ int swz(int row, int c) {
-  int key;
-  if (CPR == 16) {
-    const int r = row & 15;
-    key = ((r << 1) | (r >> 3)) & 15;
-  } else {
-    key = row % CPR;
-  }
-  return row * (CPR * 16) + ((c ^ key) << 4);
-}
-
-// Issue this wave's share of the direct-to-LDS loads of one K (or V) chunk:
-// key rows kv_row0 .. kv_row0 + BN - 1 of the head (rows past `nvalid` repeat
-// the last valid row; their scores are masked). Each instruction fills one
-// 1 KB block; WAVES wavefronts share the chunk.
-template <class C, int WAVES>
-__device__ __forceinline__ void load_rows(const bf16_t* src, int kv_row0, int nvalid, char* buf,
-                                          int wave, int lane, const int* rtab = nullptr) {
-  constexpr int kIter = (C::kBlocks + WAVES - 1) / WAVES;
-#pragma unroll
-  for (int b = 0; b < kIter; ++b) {
-    const int blk = wave + WAVES * b;
-    if (kIter * WAVES != C::kBlocks && blk >= C::kBlocks) break;  // wave-uniform
-    const int row = blk * C::kRowsPerBlock + lane / C::kCPR;
-    const int pos = lane % C::kCPR;                      // slot this lane fills
-    const int c = pos ^ ((swz<C::kCPR>(row, 0) >> 4) & (C::kCPR - 1));  // chunk it holds
-    // Tile-major order: the chunk's keys are consecutive token rows from
-    // kv_row0. Raster order: kv_row0 is the run's first raster token and
-    // rtab (already offset to the chunk) gives each key's raster offset.
-    const int key = min(row, nvalid - 1);
-    const int src_row = rtab ? kv_row0 + rtab[key] : kv_row0 + key;
-    const long long off = (long long)src_row * (C::kRowBytes / 2) + c * 8;
-    __builtin_amdgcn_global_load_lds(src + off, (lds_void*)(buf + blk * 1024), 16, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void wait_vm_all() {
-  // vmcnt(0); expcnt and lgkmcnt left at their maxima (not waited on).
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-
-// Rare branches (a ragged last chunk, a growing row max) hold code the
-// compiler would otherwise turn into unconditional selects and multiplies on
-// every chunk; an empty volatile asm statement keeps them real branches.
-__device__ __forceinline__ void keep_branch() { asm volatile(""); }
 
 // Per-wave state of the flash loop: Q fragments, O^T accumulators, running
 // max m (log2 units) and partial row sums, the current scores and the bf16
@@ -419,28 +191,6 @@ __device__ __forceinline__ void pv_chunk(WaveState<C, RB>& w, const char* vbuf, 
   }
 }
 
-// Token index (in the tensor's own order) of each of this lane's query rows,
-// and whether the row exists (work items may be ragged).
-template <class C, int RB>
-struct RowMap {
-  int tok[RB];
-  bool ok[RB];
-};
-
-template <class C, int RB, bool RASTER>
-__device__ __forceinline__ RowMap<C, RB> map_rows(const AttnParams& p, const Task& t, int wave,
-                                                  int l16) {
-  RowMap<C, RB> rm;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = wave * C::kRowsWave + 16 * rb + l16;
-    rm.ok[rb] = r < t.valid_rows;
-    const int rr = rm.ok[rb] ? r : 0;
-    rm.tok[rb] = RASTER ? tile_row_raster(p, t.qt, t.qh, t.qw, t.local0 + rr) : t.row0 + rr;
-  }
-  return rm;
-}
-
 template <class C, int RB>
 __device__ __forceinline__ void load_q_init(WaveState<C, RB>& w, const bf16_t* qg,
                                             const RowMap<C, RB>& rm, int l16, int g) {
@@ -463,11 +213,14 @@ __device__ __forceinline__ void load_q_init(WaveState<C, RB>& w, const bf16_t* q
 
 // Normalise and store: lane holds O[row l16][16*db + 4g + r].
 template <class C, int RB>
-__device__ __forceinline__ void store_out(WaveState<C, RB>& w, bf16_t* og, const RowMap<C, RB>& rm,
-                                          int g) {
+__device__ __forceinline__ void store_out(WaveState<C, RB>& w, bf16_t* og, float* lse,
+                                          const RowMap<C, RB>& rm, int g) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const float inv = 1.0f / row_sum4(w.lsum[rb]);
+    const float l = row_sum4(w.lsum[rb]);
+    const float inv = 1.0f / l;
+    // log sum_j exp(scale q.k_j) = ln 2 * (m + log2 l), m and l in base 2.
+    if (lse && rm.ok[rb] && g == 0) lse[rm.tok[rb]] = (w.m[rb] + __log2f(l)) * kLn2;
     if (rm.ok[rb]) {
       bf16_t* dst = og + (long long)rm.tok[rb] * C::kD + 4 * g;
 #pragma unroll
@@ -479,41 +232,6 @@ __device__ __forceinline__ void store_out(WaveState<C, RB>& w, bf16_t* og, const
       }
     }
   }
-}
-
-// Walks the key chunks of a work item: chunk `it` covers keys
-// row0(it) .. + BN of the head, of which nvalid(it) are inside the run.
-struct ChunkWalk {
-  int chunks_per_run, n_chunks, run_len, bn;
-  KvRuns kv;
-  bool dense;
-  __device__ __forceinline__ void at(int it, int* row0, int* nvalid) const {
-    const int run = it / chunks_per_run;
-    const int c0 = (it - run * chunks_per_run) * bn;
-    *row0 = (dense ? 0 : kv.run_start(run)) + c0;
-    *nvalid = min(bn, run_len - c0);
-  }
-  // Raster order: the run's first raster token, the chunk's first key within
-  // the run, and the number of valid keys.
-  __device__ __forceinline__ void at_raster(const AttnParams& p, int it, int* base, int* c0,
-                                            int* nvalid) const {
-    const int run = it / chunks_per_run;
-    *c0 = (it - run * chunks_per_run) * bn;
-    *base = kv.run_start_raster(run, p.H, p.W, p.ct, p.ch, p.cw);
-    *nvalid = min(bn, run_len - *c0);
-  }
-};
-
-template <int BN, bool DENSE>
-__device__ __forceinline__ ChunkWalk make_walk(const Task& t, int S) {
-  ChunkWalk cw;
-  cw.kv = t.kv;
-  cw.dense = DENSE;
-  cw.run_len = DENSE ? S : t.kv.run_len;
-  cw.bn = BN;
-  cw.chunks_per_run = (cw.run_len + BN - 1) / BN;
-  cw.n_chunks = (DENSE ? 1 : t.kv.runs) * cw.chunks_per_run;
-  return cw;
 }
 
 // Flash loop: every wave runs QK^T, softmax and PV of a chunk in turn; the
@@ -587,7 +305,7 @@ attn_bf16_kernel(const AttnParams p) {
     chunk_step(kb0, vb0, kb1, vb1, it);
     if (it + 1 < walk.n_chunks) chunk_step(kb1, vb1, kb0, vb0, it + 1);
   }
-  store_out<C, RB>(w, og, rm, g);
+  store_out<C, RB>(w, og, p.lse ? p.lse + t.head_base / D : nullptr, rm, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -680,6 +398,7 @@ __global__ void __launch_bounds__(kF32Threads) attn_f32_kernel(const AttnParams 
   }
   if (row_ok) {
     const float inv = 1.0f / l;
+    if (p.lse) p.lse[t.head_base / D + q_tok] = (m + __log2f(l)) * kLn2;
     float* dst = og + (long long)q_tok * D;
 #pragma unroll
     for (int d = 0; d < D; ++d) dst[d] = o[d] * inv;
@@ -692,6 +411,7 @@ __global__ void __launch_bounds__(kF32Threads) attn_f32_kernel(const AttnParams 
 
 void fill_params(const AttnProblem& pr, int rows_per_item, AttnParams* p) {
   p->q = pr.q; p->k = pr.k; p->v = pr.v; p->out = pr.out;
+  p->lse = pr.lse;
   p->S = pr.g.S;
   p->heads = pr.heads;
   p->dense = pr.dense ? 1 : 0;

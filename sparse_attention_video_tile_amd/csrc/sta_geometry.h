@@ -26,6 +26,18 @@ STA_HD int window_start(int q, int n, int omega) {
   return s > hi ? hi : s;
 }
 
+// Query tiles along one axis whose window holds key tile j: the interval
+// [*lo, *hi]. window_start is nondecreasing in q, so the set is an interval.
+// start(q) <= j holds for every q once j >= n - omega, else exactly for
+// q <= j + omega/2; start(q) >= j - omega + 1 holds for every q when that
+// bound is <= 0, else exactly for q >= j - omega + 1 + omega/2.
+STA_HD void window_inverse(int j, int n, int omega, int* lo, int* hi) {
+  const int half = omega / 2;
+  *hi = j >= n - omega ? n - 1 : j + half;
+  const int a = j - omega + 1;
+  *lo = a <= 0 ? 0 : a + half;
+}
+
 struct Geometry {
   int T, H, W;     // tokens per axis
   int ct, ch, cw;  // tile size in tokens

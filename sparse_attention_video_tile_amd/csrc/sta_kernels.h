@@ -20,6 +20,7 @@ struct AttnProblem {
   const void* k;
   const void* v;
   void* out;
+  float* lse;      // optional [B][heads][S] log-sum-exp per query row (natural log)
   int B, heads, head_dim;
   int dtype;       // sta_dtype
   float scale;
@@ -33,12 +34,29 @@ struct AttnProblem {
 int launch_reorder(const void* src, void* dst, int BH, int row_bytes, const Geometry& g,
                    bool to_tiles, void* stream);
 
+// transposed: list, per key tile, the query tiles whose window holds it.
 int launch_kv_tiles(int* kv_list, int* kv_count, int heads, const Geometry& g,
-                    const uint16_t (*omega)[3], int max_kv, void* stream);
+                    const uint16_t (*omega)[3], int max_kv, bool transposed, void* stream);
 
 // Returns STA_ERR_UNSUPPORTED (as a negative value) when no kernel exists for
 // the (dtype, head_dim) pair, 0 on success, or a positive hipError_t.
 int launch_attention(const AttnProblem& p, void* stream);
+
+// Gradients of STA (sparse problems only). attn.out holds the forward output
+// O; delta is a [B][heads][S] float workspace the launch fills with
+// rowsum(dO * O) before the gradient kernels read it.
+struct BwdProblem {
+  AttnProblem attn;
+  const void* dout;
+  const float* lse;
+  float* delta;
+  void* dq;
+  void* dk;
+  void* dv;
+};
+
+// Same return convention as launch_attention.
+int launch_backward(const BwdProblem& p, void* stream);
 
 const char* hip_error_string(int code);
 

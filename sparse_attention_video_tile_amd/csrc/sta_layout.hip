@@ -7,9 +7,9 @@
 // contiguous in raster order, so both sides are coalesced. Eight chunks per
 // lane are loaded before any is stored, to keep enough bytes in flight.
 //
-// kv_tiles_kernel: one thread per (head, query tile, list slot) writes the
-// slot's key tile, walking the window box in (t, h, w) lexicographic order,
-// which is ascending tile index.
+// kv_tiles_kernel: one thread per (head, tile, list slot) writes the slot's
+// tile of the window box (or of the transposed window), in (t, h, w)
+// lexicographic order, which is ascending tile index.
 #include <hip/hip_runtime.h>
 
 #include "sta_kernels.h"
@@ -115,30 +115,43 @@ struct KvTilesParams {
   int* kv_count;
   long long total;  // heads * n_tiles * max_kv
   int max_kv, n_tiles, nt, nh, nw;
+  int transposed;   // 0: key tiles of each query tile's window; 1: query tiles whose window holds each key tile
   uint16_t omega[STA_MAX_HEADS][3];
 };
 
+// One thread per (head, tile, list slot). Per axis the listed tiles form an
+// interval [lo, hi] (the window, or its transpose); slots enumerate the box in
+// (t, h, w) lexicographic order, which is ascending tile index.
 __global__ void __launch_bounds__(256) kv_tiles_kernel(const KvTilesParams p) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= p.total) return;
   const int slot = (int)(idx % p.max_kv);
   const long long rest = idx / p.max_kv;
-  const int qtile = (int)(rest % p.n_tiles);
+  const int tile = (int)(rest % p.n_tiles);
   const int h = (int)(rest / p.n_tiles);
-  const int ot = p.omega[h][0], oh = p.omega[h][1], ow = p.omega[h][2];
-  const int qw = qtile % p.nw;
-  const int qh = (qtile / p.nw) % p.nh;
-  const int qt = qtile / (p.nw * p.nh);
-  const int st = window_start(qt, p.nt, ot);
-  const int sh = window_start(qh, p.nh, oh);
-  const int sw = window_start(qw, p.nw, ow);
-  const int count = ot * oh * ow;
+  const int tw = tile % p.nw;
+  const int th = (tile / p.nw) % p.nh;
+  const int tt = tile / (p.nw * p.nh);
+  int lo[3], len[3];
+  const int c[3] = {tt, th, tw};
+  const int n[3] = {p.nt, p.nh, p.nw};
+  for (int a = 0; a < 3; ++a) {
+    if (p.transposed) {
+      int hi;
+      window_inverse(c[a], n[a], p.omega[h][a], &lo[a], &hi);
+      len[a] = hi - lo[a] + 1;
+    } else {
+      lo[a] = window_start(c[a], n[a], p.omega[h][a]);
+      len[a] = p.omega[h][a];
+    }
+  }
+  const int count = len[0] * len[1] * len[2];
   int value = -1;
   if (slot < count) {
-    const int a = slot / (oh * ow);
-    const int b = (slot / ow) % oh;
-    const int c = slot % ow;
-    value = ((st + a) * p.nh + (sh + b)) * p.nw + (sw + c);
+    const int a = slot / (len[1] * len[2]);
+    const int b = (slot / len[2]) % len[1];
+    const int d = slot % len[2];
+    value = ((lo[0] + a) * p.nh + (lo[1] + b)) * p.nw + (lo[2] + d);
   }
   p.kv_list[idx] = value;
   if (slot == 0) p.kv_count[rest] = count;
@@ -171,8 +184,9 @@ int launch_reorder(const void* src, void* dst, int BH, int row_bytes, const Geom
 }
 
 int launch_kv_tiles(int* kv_list, int* kv_count, int heads, const Geometry& g,
-                    const uint16_t (*omega)[3], int max_kv, void* stream) {
+                    const uint16_t (*omega)[3], int max_kv, bool transposed, void* stream) {
   KvTilesParams p;
+  p.transposed = transposed ? 1 : 0;
   p.kv_list = kv_list;
   p.kv_count = kv_count;
   p.total = (long long)heads * g.n_tiles * max_kv;

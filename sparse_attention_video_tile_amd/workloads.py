@@ -188,6 +188,15 @@ def make_inputs(w: Workload) -> Inputs:
     return Inputs(w, q, k, v, windows)
 
 
+def make_grad_output(w: Workload) -> np.ndarray:
+    """The upstream gradient dO for backward tests: N(0,1) of the workload's
+    shape from its own stream default_rng((seed, 3)), rounded like the inputs."""
+    T, H, W = w.volume
+    shape = (w.B, w.heads, T, H, W, w.head_dim)
+    g = np.random.default_rng((w.seed, 3)).standard_normal(shape, dtype=np.float32)
+    return round_to_bf16(g) if w.dtype == "bf16" else g
+
+
 def small_case(
     volume: Triple,
     tile: Triple,

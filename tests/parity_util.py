@@ -55,3 +55,34 @@ def assert_close(got, ref, dtype: str, what: str = ""):
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+# Gradient tolerances, relative to the reference (gradient magnitudes depend on
+# the window size and the scale, so absolute bounds would mean nothing).
+# bf16 path: the recomputed P and dS are rounded to bf16 before each matrix
+# product and the gradients are rounded to bf16 (relative error <= 2^-9 each),
+# so the relative L2 error stays well under 1e-2; single elements may lose
+# more to cancellation, so their bound is relative to the largest element.
+GRAD_BF16_REL_L2 = 1e-2
+GRAD_BF16_MAX_REL = 2e-2
+GRAD_F32_REL_L2 = 1e-5
+GRAD_F32_MAX_REL = 1e-4
+# Log-sum-exp: the bf16 forward sums the bf16-rounded probabilities (the
+# values that multiply V), which moves lse by at most log(1 + 2^-9) < 2e-3.
+LSE_BF16_MAX_ABS = 4e-3
+LSE_F32_MAX_ABS = 1e-5
+
+
+def assert_grad_close(got, ref, dtype: str, what: str = ""):
+    e = errors(got, ref)
+    scale = float(np.abs(np.asarray(ref, dtype=np.float64)).max())
+    e["max_abs_rel_to_max"] = e["max_abs"] / max(scale, 1e-300)
+    print(f"[parity] {what} {e}", flush=True)
+    assert np.isfinite(np.asarray(got, dtype=np.float64)).all(), f"{what}: non-finite gradient"
+    if dtype == "bf16":
+        assert e["rel_l2"] <= GRAD_BF16_REL_L2, (what, e)
+        assert e["max_abs_rel_to_max"] <= GRAD_BF16_MAX_REL, (what, e)
+    else:
+        assert e["rel_l2"] <= GRAD_F32_REL_L2, (what, e)
+        assert e["max_abs_rel_to_max"] <= GRAD_F32_MAX_REL, (what, e)
+    return e

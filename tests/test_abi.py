@@ -119,3 +119,83 @@ def test_kv_pair_count_matches_oracle(heads, volume, tile, windows):
 
 def test_kv_pair_count_rejects_bad_window(lib):
     assert lib.sta_kv_pair_count(1, 30, 48, 80, i3(6, 8, 8), i3(18, 24, 25)) == -1
+
+
+def test_q_tiles_rejects_bad_arguments(lib):
+    t = i3(6, 8, 8)
+    w = i3(18, 24, 24)
+    # the longest transposed list at this geometry: 5 x 4 x 4 = 80 query tiles
+    # (the central key tile along t, of 5, is read by all 5 query tiles)
+    longest = int(oracle.q_tile_lists((30, 48, 80), (6, 8, 8), [(18, 24, 24)])[1].max())
+    assert longest == 80
+    assert lib.sta_q_tiles(None, FAKE, 1, 30, 48, 80, t, w, 80, None) == -1
+    assert lib.sta_q_tiles(FAKE, FAKE * 1000, 1, 30, 48, 80, t, w, 79, None) == -1
+    assert "longest list 80" in binding.last_error()
+    assert lib.sta_q_tiles(FAKE, FAKE + 4, 1, 30, 48, 80, t, w, 80, None) == -1
+
+
+def test_forward_lse_rejects_bad_arguments(lib):
+    t, w = i3(6, 8, 8), i3(18, 24, 24)
+    f = lib.sta_forward_lse
+    base = [FAKE, FAKE * 2, FAKE * 3, FAKE * 1000, FAKE * 5000, 1, 1, 128, 30, 48, 80, t, w, 0.1, 0]
+    bad = list(base)
+    bad[4] = None
+    assert f(*bad, 0, None) == -1                     # lse NULL
+    assert f(*base, 2, None) == -1                    # unknown order
+    bad = list(base)
+    bad[4] = FAKE * 2 + 64
+    assert f(*bad, 1, None) == -1                     # lse overlaps k
+    assert "overlap" in binding.last_error()
+
+
+def backward_args(**kw):
+    a = dict(q=FAKE, k=FAKE * 2000, v=FAKE * 4000, o=FAKE * 6000, do=FAKE * 8000, lse=FAKE * 10000,
+             dq=FAKE * 12000, dk=FAKE * 14000, dv=FAKE * 16000, delta=FAKE * 18000, B=1, heads=1,
+             d=128, T=30, H=48, W=80, tile=i3(6, 8, 8), win=i3(18, 24, 24), scale=0.1, dt=0, order=0)
+    a.update(kw)
+    return a
+
+
+def call_backward(lib, a):
+    return lib.sta_backward(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                            a["dv"], a["delta"], a["B"], a["heads"], a["d"], a["T"], a["H"], a["W"],
+                            a["tile"], a["win"], a["scale"], a["dt"], a["order"], None)
+
+
+def test_backward_rejects_bad_arguments(lib):
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "delta"):
+        assert call_backward(lib, backward_args(**{name: None})) == -1, name
+    assert call_backward(lib, backward_args(order=3)) == -1
+    assert call_backward(lib, backward_args(win=i3(18, 24, 20))) == -1
+    assert call_backward(lib, backward_args(d=96)) == -2
+    assert call_backward(lib, backward_args(dt=4)) == -1
+    assert call_backward(lib, backward_args(scale=-1.0)) == -1
+    assert call_backward(lib, backward_args(dq=FAKE * 2000 + 256)) == -1    # dq overlaps k
+    assert "overlap" in binding.last_error()
+    assert call_backward(lib, backward_args(delta=FAKE * 14000 + 64)) == -1  # delta overlaps dk
+    assert call_backward(lib, backward_args(dk=FAKE * 16000)) == -1          # dk aliases dv
+    assert call_backward(lib, backward_args(q=FAKE + 8)) == -2               # misaligned
+    # raster order: a whole-width window run of 10 tiles x 384 tokens fits, a
+    # 1 x 1 x 8200-token run does not
+    assert call_backward(lib, backward_args(order=1, T=1, H=1, W=8200, tile=i3(1, 1, 8),
+                                            win=i3(1, 1, 8200), d=64)) == -2
+    assert "raster order" in binding.last_error()
+
+
+def test_raster_run_fits_matches_library_limit():
+    assert binding.raster_run_fits((6, 8, 8), [(18, 24, 24)], 1, (30, 48, 80), backward=True)
+    assert binding.raster_run_fits((1, 1, 8), [(1, 1, 8192)], 1, (1, 1, 8192), backward=True)
+    assert not binding.raster_run_fits((1, 1, 8), [(1, 1, 8200)], 1, (1, 1, 8200), backward=True)
+    # transposed runs can be longer than the window: n_w = 4, omega_w = 2 gives
+    # key tile 1 three query tiles
+    assert binding._inverse_len(1, 4, 2) == 3
+    # n_w = 4 tiles of 4096, omega_w = 2: window runs of 8192 fit, the
+    # transposed run of key tile 1 (3 query tiles, 12288 tokens) does not
+    assert binding.raster_run_fits((1, 1, 4096), [(1, 1, 8192)], 1, (1, 1, 16384), backward=False)
+    assert not binding.raster_run_fits((1, 1, 4096), [(1, 1, 8192)], 1, (1, 1, 16384), backward=True)
+
+
+def test_backward_raster_limit_counts_transposed_runs(lib):
+    a = backward_args(order=1, T=1, H=1, W=16384, tile=i3(1, 1, 4096), win=i3(1, 1, 8192), d=64)
+    assert call_backward(lib, a) == -2
+    assert "12288" in binding.last_error()
