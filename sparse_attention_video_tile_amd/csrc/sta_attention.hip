@@ -434,8 +434,7 @@ void fill_params(const AttnProblem& pr, int rows_per_item, AttnParams* p) {
   }
   p->row_blocks = (p->unit_rows + rows_per_item - 1) / rows_per_item;
   const long long tasks = (long long)pr.B * pr.heads * p->n_units * p->row_blocks;
-  p->n_tasks = (int)tasks;
-  p->per_xcd = (int)((tasks + kXcds - 1) / kXcds);
+  plan_tasks(p, tasks, pr.heads, pr.dense);
 }
 
 // LDS for the raster offsets of the longest window run, omega_w * tau keys.

@@ -34,7 +34,8 @@ struct AttnParams {
   int S;            // tokens per (batch, head)
   int heads;
   int n_tasks;      // work items
-  int per_xcd;      // ceil(n_tasks / kXcds)
+  int per_xcd;      // workgroups each XCD runs (the grid is kXcds * per_xcd)
+  int group;        // logical tasks an XCD takes in a row before the next XCD's turn
   int row_blocks;   // work items per query unit
   int n_units;      // query units per (batch, head): tiles, or 1 if dense
   int unit_rows;    // rows per query unit: tau, or S if dense
@@ -43,6 +44,7 @@ struct AttnParams {
   int nt, nh, nw, tau;
   int H, W, ct, ch, cw;  // volume and tile, for raster-order addressing
   uint16_t omega[STA_MAX_HEADS][3];
+  uint8_t head_order[STA_MAX_HEADS];  // logical head slot -> head (heaviest windows first)
 };
 
 
@@ -51,7 +53,45 @@ struct AttnParams {
 // that share most of their keys) run on the same XCD and share its L2.
 __device__ __forceinline__ int logical_task(const AttnParams& p) {
   const int bid = blockIdx.x;
-  return (bid % kXcds) * p.per_xcd + bid / kXcds;
+  const int x = bid % kXcds, r = bid / kXcds;
+  return (r / p.group) * (kXcds * p.group) + x * p.group + r % p.group;
+}
+
+// Host side: order the work and size the grid. With equal windows on every
+// head, each XCD takes one contiguous share of the tasks (group = share), so
+// neighbouring tiles, which read mostly the same keys, meet in one L2. With
+// unequal windows the heads are ordered by window size, heaviest first, and
+// the XCDs take turns in blocks of kMixedGroup tasks: every XCD then gets the
+// same mix of heavy and light work, and the light work comes last.
+constexpr int kMixedGroup = 32;
+
+inline void plan_tasks(AttnParams* p, long long tasks, int heads, bool dense) {
+  p->n_tasks = (int)tasks;
+  int cost[STA_MAX_HEADS];
+  bool equal = true;
+  for (int h = 0; h < heads; ++h) {
+    cost[h] = dense ? 1 : p->omega[h][0] * p->omega[h][1] * p->omega[h][2];
+    p->head_order[h] = (uint8_t)h;
+    equal = equal && cost[h] == cost[0];
+  }
+  const long long share = (tasks + kXcds - 1) / kXcds;
+  if (equal) {
+    p->group = (int)(share > 0 ? share : 1);
+    p->per_xcd = p->group;
+    return;
+  }
+  for (int i = 1; i < heads; ++i) {  // stable insertion sort, descending cost
+    const uint8_t h = p->head_order[i];
+    int j = i;
+    while (j > 0 && cost[p->head_order[j - 1]] < cost[h]) {
+      p->head_order[j] = p->head_order[j - 1];
+      --j;
+    }
+    p->head_order[j] = h;
+  }
+  p->group = kMixedGroup;
+  const long long blocks = (tasks + (long long)kXcds * kMixedGroup - 1) / ((long long)kXcds * kMixedGroup);
+  p->per_xcd = (int)(blocks * kMixedGroup);
 }
 
 // Key runs of one work item: `runs` runs of `run_len` tokens; run r starts at
@@ -121,8 +161,8 @@ __device__ __forceinline__ Task decode_task(const AttnParams& p, int task, int D
   const int unit_bh = task / p.row_blocks;
   const int unit = unit_bh % p.n_units;
   const int bh = unit_bh / p.n_units;
-  const int h = bh % p.heads;
-  t.head_base = (long long)bh * p.S * D;
+  const int h = p.head_order[bh % p.heads];
+  t.head_base = ((long long)(bh / p.heads) * p.heads + h) * p.S * D;
   const int unit_row0 = unit * p.unit_rows;
   t.row0 = unit_row0 + rb * ROWS;
   t.local0 = rb * ROWS;

@@ -557,8 +557,7 @@ void fill_bwd_params(const BwdProblem& pr, int rows_per_item, AttnParams* p, Bwd
     for (int x = 0; x < 3; ++x) p->omega[h][x] = a.omega[h][x];
   p->row_blocks = (p->unit_rows + rows_per_item - 1) / rows_per_item;
   const long long tasks = (long long)a.B * a.heads * p->n_units * p->row_blocks;
-  p->n_tasks = (int)tasks;
-  p->per_xcd = (int)((tasks + kXcds - 1) / kXcds);
+  plan_tasks(p, tasks, a.heads, false);
   b->dout = pr.dout;
   b->lse = pr.lse;
   b->delta = pr.delta;
