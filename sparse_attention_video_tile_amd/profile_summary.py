@@ -10,6 +10,9 @@ RUN_DIR holds what one profiling session of bench.py wrote:
       rocprofv3 --pmc <counter> --kernel-trace -d RUN_DIR/<counter> -o run -f csv --
           python3 bench.py --steps 2 --warmup 1 --cpu-budget 0 --dense-reps 1
           --compare-reps 1 --copy-reference
+  MFMA/run_counter_collection.csv (optional)
+      rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace
+          -d RUN_DIR/MFMA -o run -f csv -- python3 bench.py <same arguments>
 
 Writes, for the workload named in bench.json, a kernel-time table, an HBM
 traffic table, and per path (fused, three_call) a JSON record of the bytes
@@ -39,6 +42,11 @@ TRACE_CMD = "rocprofv3 --kernel-trace --stats -d <outdir> -o bench -f csv -- pyt
 PMC_ARGS = "--steps 2 --warmup 1 --cpu-budget 0 --dense-reps 1 --compare-reps 1 --copy-reference"
 
 
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE"
+N_CU = 256          # MI355X compute units
+SIMD_PER_CU = 4
+
+
 def pmc_cmd(counter: str) -> str:
     return f"rocprofv3 --pmc {counter} --kernel-trace -d <outdir> -o run -f csv -- python3 bench.py {PMC_ARGS}"
 
@@ -63,6 +71,12 @@ def short_name(n: str) -> str:
 
 
 def role(name: str) -> str:
+    if "bwd_dkdv_kernel" in name or "bwd_f32_dkdv" in name:
+        return "STA backward, key side (dK, dV)"
+    if "bwd_dq_kernel" in name or "bwd_f32_dq" in name:
+        return "STA backward, query side (dQ)"
+    if "delta_kernel" in name:
+        return "STA backward, D = rowsum(dO * O)"
     if "attn_bf16_kernel" in name or "attn_f32_kernel" in name:
         args = name[name.index("<") + 1:name.index(">")].split(",")
         dense, raster = args[-2].strip() == "true", args[-1].strip() == "true"
@@ -74,9 +88,11 @@ def role(name: str) -> str:
     return ""
 
 
-def per_dispatch(path: str):
+def per_dispatch(path: str, counter: str = None):
     agg = collections.OrderedDict()
     for r in csv.DictReader(open(path)):
+        if counter is not None and r.get("Counter_Name") != counter:
+            continue
         k = (int(r["Dispatch_Id"]), r["Kernel_Name"])
         agg[k] = agg.get(k, 0.0) + float(r["Counter_Value"])
     return agg
@@ -102,8 +118,9 @@ def main(argv=None) -> int:
     L = [f"# Kernel time, bench.py on {title}\n", "Command (repo root, MI355X, ROCm 7.2):\n",
          f"```\n{TRACE_CMD}\n```\n",
          "bench.py defaults: 3 warm-up + 20 timed steps of the fused path (one raster-order STA launch), "
-         "then 1 + 3 steps of the three-call path (reorder q, k, v; tile-major STA; restore), then "
-         "1 + 2 dense-comparator launches at the same shape.\n",
+         "then 1 + 3 steps of the three-call path (reorder q, k, v; tile-major STA; restore), "
+         "1 + 2 dense-comparator launches, 1 + 3 forward-with-lse and backward passes at the same "
+         "shape, then 1 + 3 launches on each other named workload (the same kernels).\n",
          "| kernel | role | calls | average (ms) | min (ms) | max (ms) | share |",
          "|---|---|---|---|---|---|---|"]
     for r in rows:
@@ -111,10 +128,28 @@ def main(argv=None) -> int:
                  f"{float(r['AverageNs']) / 1e6:.3f} | {float(r['MinNs']) / 1e6:.3f} | "
                  f"{float(r['MaxNs']) / 1e6:.3f} | {float(r['Percentage']):.1f}% |")
     rf = bench["roofline"]
-    L += ["", f"bench.py's HIP-event average for the timed kernel ({rf['kernel']}) in the same command "
-          f"without the profiler: {rf['launch_ms']:.3f} ms, {rf['achieved']:.1f} TFLOP/s of algorithmic "
-          f"work ({cfg['algorithmic_tflop_per_step']:.4f} TFLOP per launch), "
-          f"{100 * rf['frac']:.1f}% of the {rf['peak']:.0f} TFLOP/s dense peak."]
+    # The same kernel also serves the backward's forward and the other
+    # workloads later in the run, so the --stats average mixes shapes; the
+    # timed launches are the first warmup + steps dispatches of the kernel.
+    timed = None
+    tpath = os.path.join(run, "trace", "bench_kernel_trace.csv")
+    if os.path.exists(tpath):
+        want = "true>" if cfg.get("path", "fused") == "fused" else "false, false>"
+        disp = sorted((int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                      for r in csv.DictReader(open(tpath))
+                      if "attn_bf16_kernel" in r["Kernel_Name"] and want in r["Kernel_Name"]
+                      and "true, false>" not in r["Kernel_Name"])
+        w0, ns = bench["warmup"], bench["steps"]
+        if len(disp) >= w0 + ns:
+            sel = [d for _, d in disp[w0:w0 + ns]]
+            timed = sum(sel) / len(sel) / 1e6
+    L += ["", f"Timed launches: dispatches {bench['warmup'] + 1}..{bench['warmup'] + bench['steps']} of "
+          f"the {rf['kernel']} (the first warm-up + timed launches of that kernel in the run) average "
+          + (f"{timed:.3f} ms in the trace." if timed is not None else "n/a (no kernel trace)."),
+          f"bench.py's HIP-event average for the same launches in the same command without the "
+          f"profiler: {rf['launch_ms']:.3f} ms, {rf['achieved']:.1f} TFLOP/s of algorithmic work "
+          f"({cfg['algorithmic_tflop_per_step']:.4f} TFLOP per launch), {100 * rf['frac']:.1f}% of "
+          f"the {rf['peak']:.0f} TFLOP/s dense peak."]
     name = f"attn_{bench['dtype']}_{wl}_kernel_stats.md"
     open(os.path.join(out, name), "w").write("\n".join(L) + "\n")
 
@@ -174,6 +209,35 @@ def main(argv=None) -> int:
     for path, rec in records.items():
         fn = os.path.join(out, f"attn_{bench['dtype']}_{path}_{wl}_traffic.json")
         json.dump(rec, open(fn, "w"), indent=1)
+
+    # MFMA busy fraction.
+    mpath = os.path.join(run, "MFMA", "run_counter_collection.csv")
+    if os.path.exists(mpath):
+        busy = per_dispatch(mpath, "SQ_VALU_MFMA_BUSY_CYCLES")
+        gui = per_dispatch(mpath, "GRBM_GUI_ACTIVE")
+        sq = per_dispatch(mpath, "SQ_BUSY_CYCLES")
+        L = [f"# Matrix-core busy fraction, bench.py on {title}\n",
+             "Command (repo root), one pass:\n",
+             f"```\nrocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace -d <outdir> -o run -f csv -- "
+             f"python3 bench.py {PMC_ARGS}\n```\n",
+             f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {N_CU} CUs x "
+             f"{SIMD_PER_CU} SIMDs), per dispatch, averaged over the dispatches of each kernel. "
+             "GRBM_GUI_ACTIVE counts GPU-busy cycles of the dispatch (its clock, not 2.4 GHz), so "
+             "the ratio is the matrix cores' duty cycle independent of the clock the chip ran at.\n",
+             "| kernel | role | dispatches | MFMA busy | SQ_BUSY_CYCLES / GRBM_GUI_ACTIVE |",
+             "|---|---|---|---|---|"]
+        names = list(dict.fromkeys(n for (_, n) in busy if role(n)))
+        util = {}
+        for n in names:
+            ks = [k for k in busy if k[1] == n]
+            fr = [busy[k] / (gui[k] * N_CU * SIMD_PER_CU) for k in ks if gui.get(k)]
+            sb = [sq[k] / gui[k] for k in ks if gui.get(k) and k in sq]
+            if not fr:
+                continue
+            util[n] = sum(fr) / len(fr)
+            L.append(f"| `{short_name(n)}` | {role(n)} | {len(fr)} | {100 * util[n]:.1f}% | "
+                     f"{(sum(sb) / len(sb)) if sb else float('nan'):.2f} |")
+        open(os.path.join(out, f"attn_{bench['dtype']}_{wl}_mfma_busy.md"), "w").write("\n".join(L) + "\n")
     print(json.dumps({p: r["bytes_per_launch"] for p, r in records.items()}))
     return 0
 
