@@ -19,6 +19,7 @@ Printed as one JSON line. Besides the contract fields it carries
   three_call    the reorder -> tile-major forward -> restore path, with the
                 permutation kernels' achieved HBM bandwidth;
   backward      sta_forward_lse + sta_backward at the same shape;
+  recall        sta_window_recall over five candidate windows at the same shape;
   other_workloads  the fused kernel on the other named workloads.
 """
 
@@ -149,6 +150,34 @@ def time_backward(w, args, torch, binding, q, k, v, windows, fwd_flops, stream, 
     }
 
 
+def time_recall(w, args, torch, binding, workloads, q, k, stream, ev):
+    """sta_window_recall over the five window options of the mixed workload
+    on the headline q, k. Work counted: the QK^T products of the dense
+    log-sum-exp (2 S^2 d per head) and of every candidate window (2 tau^2 d
+    per computed tile pair); the exponentials are not counted."""
+    cands = [tuple(c) for c in workloads.MIXED_WINDOW_OPTIONS]
+    S = w.seq_len
+    tau = w.tile[0] * w.tile[1] * w.tile[2]
+    flops = float(w.B) * w.heads * 2.0 * S * S * w.head_dim
+    for c in cands:
+        flops += float(w.B) * binding.sta_kv_pair_count(w.heads, w.volume, w.tile, [c]) * 2.0 * tau * tau * w.head_dim
+    ws = torch.empty((2, w.B, w.heads, S), dtype=torch.float32, device="cuda")
+    r = binding.sta_window_recall(q, k, w.tile, cands, workspace=ws)  # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(args.recall_reps):
+        r = binding.sta_window_recall(q, k, w.tile, cands, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.recall_reps
+    tf = flops / (ms * 1e-3) / 1e12
+    mean = r.mean(dim=(0, 1)).cpu().tolist()
+    del ws, r
+    return {"ms": ms, "tflops": tf, "frac_of_peak": tf / BF16_PEAK_TFLOPS, "algorithmic_tflop": flops / 1e12,
+            "candidates": cands, "mean_recall_on_iid_inputs": mean}
+
+
 def other_workloads(main_w, args, torch, binding, workloads, q, k, v, out, stream, ev):
     """The fused kernel on every other named workload: average launch time,
     effective TFLOP/s and fraction of peak. Workloads of the headline shape
@@ -201,6 +230,8 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--backward-reps", type=int, default=3,
                     help="STA backward launches to time at the headline workload (0: skip)")
+    ap.add_argument("--recall-reps", type=int, default=2,
+                    help="window-recall scoring runs to time at the headline shape (0: skip)")
     ap.add_argument("--config-reps", type=int, default=3,
                     help="launches per other named workload to time (0: skip)")
     ap.add_argument("--copy-reference", action="store_true",
@@ -325,6 +356,10 @@ def main(argv=None):
     if args.backward_reps > 0 and fused:
         backward = time_backward(w, args, torch, binding, q, k, v, windows, flops, stream, ev)
 
+    recall = None
+    if args.recall_reps > 0 and fused:
+        recall = time_recall(w, args, torch, binding, workloads, q, k, stream, ev)
+
     others = None
     if args.config_reps > 0:
         others = other_workloads(w, args, torch, binding, workloads, q, k, v, out, stream, ev)
@@ -368,6 +403,7 @@ def main(argv=None):
         "dense": dense,
         "three_call": three,
         "backward": backward,
+        "recall": recall,
         "other_workloads": others,
     }
     print(json.dumps(result), flush=True)

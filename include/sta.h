@@ -214,6 +214,33 @@ int sta_backward(const void* q, const void* k, const void* v, const void* out, c
                  float scale, int dtype, int order, void* stream);
 
 /*
+ * Window recall: for every batch entry b, head h and candidate window c,
+ *     recall[b][h][c] = (1/S) sum_i sum_{j in W_c(i)} softmax_j(scale * q_i . k_j)
+ * where the softmax runs over ALL S keys (full attention) and W_c(i) is the
+ * key set of query i under candidate window c (the clamped tile window). It is
+ * the share of full-attention probability a window keeps: the "attention
+ * recall" the pages use to show that attention is local and to configure a
+ * window per head by profiling (podcast transcript, the answers on attention
+ * recall and on choosing the window per head; dianyo ICML2025 blog, STA
+ * section, recall of local windows across prompts).
+ * Computed as the mean of exp(lse_c(i) - lse_full(i)) from the two row
+ * log-sum-exps (the attention kernels in a log-sum-exp-only mode: no V, no
+ * output), then a deterministic double-precision reduction per (b, h).
+ *   q, k:        device [B][heads][S][head_dim], token order `order`, read.
+ *   recall:      device float [B][heads][n_candidates], written.
+ *   workspace:   device float [2][B][heads][S], caller-owned scratch.
+ *   candidates:  host int[n_candidates][3], token windows, each valid for
+ *                the volume and tile (same rule as `window`); applied to
+ *                every head.
+ * Dtype, head_dim, scale and the raster run limit as sta_forward_lse. No
+ * buffer may overlap another.
+ */
+int sta_window_recall(const void* q, const void* k, float* recall, float* workspace, int B,
+                      int heads, int head_dim, int T, int H, int W, const int* tile,
+                      const int* candidates, int n_candidates, float scale, int dtype, int order,
+                      void* stream);
+
+/*
  * Full softmax attention over all S keys (the computation STA replaces, used
  * as the speed-up denominator: atlas.scime.ai summary, "Key results").
  *   q, k, v, out: device [B][heads][S][head_dim], any common token order.

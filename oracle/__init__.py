@@ -10,4 +10,5 @@ from .sta_backward_oracle import (  # noqa: F401
     sta_backward_key_rows,
     sta_backward_query_rows,
     sta_lse,
+    window_recall,
 )

@@ -187,3 +187,26 @@ def sta_backward_key_rows(q, k, v, dout, tile, window, scale, b, h, key_tokens):
         gk += scale * (ds.T @ qf[rows])
         gv += pk.T @ do
     return gk, gv
+
+
+def window_recall(q, k, tile, candidates, scale) -> np.ndarray:
+    """Attention recall, float64 (B, heads, n_candidates): for each candidate
+    window, the mean over query rows of the full-attention probability (softmax
+    over all keys) that falls on the keys the window shows the row (podcast
+    transcript, the answer on attention recall; dianyo ICML2025 blog, STA
+    section)."""
+    B, heads = q.shape[:2]
+    volume = q.shape[2:5]
+    candidates = [tuple(int(x) for x in c) for c in np.asarray(candidates).reshape(-1, 3)]
+    n = tile_grid(volume, tile)
+    S = volume[0] * volume[1] * volume[2]
+    out = np.zeros((B, heads, len(candidates)), dtype=np.float64)
+    for b in range(B):
+        for h in range(heads):
+            qf, kf = _rows_f64(q, b, h), _rows_f64(k, b, h)
+            for i in range(n[0] * n[1] * n[2]):
+                rows = tile_tokens(volume, tile, i)
+                p, _ = _softmax_rows(qf[rows], kf, np.ones((len(rows), S), dtype=bool), scale)
+                for c, w in enumerate(candidates):
+                    out[b, h, c] += np.sum(p[token_mask_rows(volume, tile, w, rows)])
+    return out / S

@@ -22,4 +22,5 @@ from .binding import (  # noqa: F401
     sta_q_tiles,
     sta_reorder_tiles,
     sta_restore_order,
+    sta_window_recall,
 )

@@ -37,6 +37,7 @@ EXPORTS = (
     "sta_forward_raster",
     "sta_forward_lse",
     "sta_backward",
+    "sta_window_recall",
     "sta_full_attention",
     "sta_last_error",
 )
@@ -92,6 +93,9 @@ def load_library(path: str = None) -> ctypes.CDLL:
         f.restype = c_int
         f.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                       c_int, c_int, c_int, int3, int3, c_float, c_int, c_void_p]
+    lib.sta_window_recall.restype = c_int
+    lib.sta_window_recall.argtypes = [c_void_p] * 4 + [c_int, c_int, c_int, c_int, c_int, c_int, int3,
+                                                       int3, c_int, c_float, c_int, c_int, c_void_p]
     lib.sta_full_attention.restype = c_int
     lib.sta_full_attention.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int,
                                        c_int, c_int, c_float, c_int, c_void_p]
@@ -433,6 +437,37 @@ def sta_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
                               float(scale), _dtype_code(q), order, _stream(dev))
     _check(rc, "sta_backward")
     return dq, dk, dv
+
+
+def sta_window_recall(q: torch.Tensor, k: torch.Tensor, tile: Sequence[int], candidates,
+                      scale: Optional[float] = None, volume: Optional[Sequence[int]] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Share of full-attention probability each candidate window keeps, averaged
+    over the query rows: float32 (B, heads, n_candidates). Raster 6-D tensors,
+    or tile-major 4-D ones with `volume`."""
+    lib = load_library()
+    if k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("k must match q in shape and dtype")
+    B, heads, d, (T, H, W), order = _order_shapes(q, volume)
+    cand = [int(x) for x in torch.as_tensor(candidates, dtype=torch.int64).reshape(-1).tolist()]
+    if len(cand) == 0 or len(cand) % 3:
+        raise ValueError("candidates must be a non-empty list of (t, h, w) windows")
+    n = len(cand) // 3
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    S = T * H * W
+    if workspace is None:
+        workspace = torch.empty((2, B, heads, S), dtype=torch.float32, device=q.device)
+    elif workspace.numel() < 2 * B * heads * S or workspace.dtype != torch.float32 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous float32 tensor of at least 2*B*heads*S elements")
+    recall = torch.empty((B, heads, n), dtype=torch.float32, device=q.device)
+    dev = _require_gpu(q, k, recall, workspace)
+    with torch.cuda.device(dev):
+        rc = lib.sta_window_recall(q.data_ptr(), k.data_ptr(), recall.data_ptr(), workspace.data_ptr(),
+                                   B, heads, d, T, H, W, _int_array(tile), _int_array(cand), n,
+                                   float(scale), _dtype_code(q), order, _stream(dev))
+    _check(rc, "sta_window_recall")
+    return recall
 
 
 class _STAFunction(torch.autograd.Function):

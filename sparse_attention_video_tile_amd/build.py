@@ -23,7 +23,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsta.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SOURCES = ["sta_layout.hip", "sta_attention.hip", "sta_backward.hip"]
+HIP_SOURCES = ["sta_layout.hip", "sta_attention.hip", "sta_backward.hip", "sta_recall.hip"]
 CXX_SOURCES = ["sta_api.cpp"]
 
 HIPCC_FLAGS = [

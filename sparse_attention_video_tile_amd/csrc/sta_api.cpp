@@ -276,6 +276,7 @@ int forward_common(const void* q, const void* k, const void* v, void* out, float
   p.B = B; p.heads = heads; p.head_dim = head_dim; p.dtype = dtype; p.scale = scale;
   p.dense = false;
   p.raster = raster;
+  p.lse_only = false;
   int rc = check_volume(T, H, W, tile, &p.g);
   if (rc) return rc;
   if ((rc = check_windows(p.g, heads, window, p.omega))) return rc;
@@ -317,6 +318,7 @@ int backward_common(const void* q, const void* k, const void* v, const void* out
   p.B = B; p.heads = heads; p.head_dim = head_dim; p.dtype = dtype; p.scale = scale;
   p.dense = false;
   p.raster = order == STA_RASTER;
+  p.lse_only = false;
   if ((rc = check_volume(T, H, W, tile, &p.g))) return rc;
   if ((rc = check_windows(p.g, heads, window, p.omega))) return rc;
   if (p.raster && (rc = check_raster_runs(p.g, heads, p.omega, true))) return rc;
@@ -386,12 +388,78 @@ int sta_backward(const void* q, const void* k, const void* v, const void* out, c
                          tile, window, scale, dtype, order, stream);
 }
 
+int sta_window_recall(const void* q, const void* k, float* recall, float* workspace, int B,
+                      int heads, int head_dim, int T, int H, int W, const int* tile,
+                      const int* candidates, int n_candidates, float scale, int dtype, int order,
+                      void* stream) {
+  if (!q || !k || !recall || !workspace || !candidates)
+    return fail(STA_ERR_INVALID_ARG, "a pointer is NULL");
+  if (n_candidates <= 0) return fail(STA_ERR_INVALID_ARG, "n_candidates=%d must be positive", n_candidates);
+  if (order != STA_TILE_MAJOR && order != STA_RASTER)
+    return fail(STA_ERR_INVALID_ARG, "unknown token order %d", order);
+  if (heads <= 0 || heads > STA_MAX_HEADS)
+    return fail(STA_ERR_INVALID_ARG, "heads=%d must be in [1, %d]", heads, STA_MAX_HEADS);
+  int rc = check_heads(B, heads, head_dim);
+  if (rc) return rc;
+  const int es = elem_size(dtype);
+  if (!es) return fail(STA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (!(scale > 0.0f) || !isfinite(scale))
+    return fail(STA_ERR_INVALID_ARG, "scale %g must be finite and positive", (double)scale);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(STA_ERR_UNSUPPORTED, "head_dim %d: kernels exist for 64 and 128", head_dim);
+  static thread_local sta::AttnProblem dense, win;
+  if ((rc = check_volume(T, H, W, tile, &win.g))) return rc;
+  // every candidate is a valid window (checked as one head each)
+  static thread_local uint16_t om[STA_MAX_HEADS][3];
+  for (int c = 0; c < n_candidates; ++c)
+    if ((rc = check_windows(win.g, 1, candidates + 3 * c, om))) return rc;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) % 16)
+    return fail(STA_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(recall) | reinterpret_cast<uintptr_t>(workspace)) % 4)
+    return fail(STA_ERR_INVALID_ARG, "recall and workspace must be 4-byte aligned");
+  const long long BH = (long long)B * heads;
+  if (BH > (1LL << 24)) return fail(STA_ERR_INVALID_ARG, "B*heads=%lld is too large", BH);
+  const size_t tb = (size_t)BH * win.g.S * head_dim * es;
+  const size_t wb = 2 * (size_t)BH * win.g.S * sizeof(float);
+  const size_t rb = (size_t)BH * n_candidates * sizeof(float);
+  if (overlaps(workspace, wb, q, tb) || overlaps(workspace, wb, k, tb) ||
+      overlaps(recall, rb, q, tb) || overlaps(recall, rb, k, tb) || overlaps(recall, rb, workspace, wb))
+    return fail(STA_ERR_INVALID_ARG, "recall or workspace overlaps an input or each other");
+  float* lse_full = workspace;
+  float* lse_win = workspace + (size_t)BH * win.g.S;
+  // full-attention lse (token order does not matter for all-keys attention)
+  dense.q = q; dense.k = k; dense.v = k; dense.out = nullptr; dense.lse = lse_full;
+  dense.B = B; dense.heads = heads; dense.head_dim = head_dim; dense.dtype = dtype; dense.scale = scale;
+  dense.dense = true; dense.raster = false; dense.lse_only = true;
+  memset(&dense.g, 0, sizeof(dense.g));
+  dense.g.S = win.g.S;
+  rc = sta::launch_attention(dense, stream);
+  if (rc) return rc < 0 ? fail(rc, "no kernel for dtype %d with head_dim %d", dtype, head_dim) : launched(rc);
+  win.q = q; win.k = k; win.v = k; win.out = nullptr; win.lse = lse_win;
+  win.B = B; win.heads = heads; win.head_dim = head_dim; win.dtype = dtype; win.scale = scale;
+  win.dense = false; win.raster = order == STA_RASTER; win.lse_only = true;
+  for (int c = 0; c < n_candidates; ++c) {
+    for (int h = 0; h < heads; ++h) {
+      win.omega[h][0] = (uint16_t)(candidates[3 * c] / win.g.ct);
+      win.omega[h][1] = (uint16_t)(candidates[3 * c + 1] / win.g.ch);
+      win.omega[h][2] = (uint16_t)(candidates[3 * c + 2] / win.g.cw);
+    }
+    if (win.raster && (rc = check_raster_runs(win.g, heads, win.omega, false))) return rc;
+    rc = sta::launch_attention(win, stream);
+    if (rc) return rc < 0 ? fail(rc, "no kernel for dtype %d with head_dim %d", dtype, head_dim) : launched(rc);
+    rc = sta::launch_recall_reduce(lse_full, lse_win, recall, (int)BH, win.g.S, n_candidates, c, stream);
+    if (rc) return launched(rc);
+  }
+  return ok();
+}
+
 int sta_full_attention(const void* q, const void* k, const void* v, void* out, int B, int heads,
                        int head_dim, int S, float scale, int dtype, void* stream) {
   if (S <= 0 || S > (1 << 30)) return fail(STA_ERR_INVALID_ARG, "S=%d must be in [1, 2^30]", S);
   static thread_local sta::AttnProblem p;
   memset(&p.g, 0, sizeof(p.g));
   p.raster = false;
+  p.lse_only = false;
   p.lse = nullptr;
   p.q = q; p.k = k; p.v = v; p.out = out;
   p.B = B; p.heads = heads; p.head_dim = head_dim; p.dtype = dtype; p.scale = scale;

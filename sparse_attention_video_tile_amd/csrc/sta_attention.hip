@@ -221,7 +221,7 @@ __device__ __forceinline__ void store_out(WaveState<C, RB>& w, bf16_t* og, float
     const float inv = 1.0f / l;
     // log sum_j exp(scale q.k_j) = ln 2 * (m + log2 l), m and l in base 2.
     if (lse && rm.ok[rb] && g == 0) lse[rm.tok[rb]] = (w.m[rb] + __log2f(l)) * kLn2;
-    if (rm.ok[rb]) {
+    if (og && rm.ok[rb]) {
       bf16_t* dst = og + (long long)rm.tok[rb] * C::kD + 4 * g;
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db) {
@@ -240,7 +240,9 @@ __device__ __forceinline__ void store_out(WaveState<C, RB>& w, bf16_t* og, float
 // tile-major order is folded into the addressing): query rows map through
 // tile_row_raster, and every key of a window run through a table of raster
 // offsets built in dynamic LDS at the start (all runs of a work item share it).
-template <int D, int WAVES, int RB, int BN, bool DENSE, bool RASTER>
+// LSE_ONLY: only the row log-sum-exp is wanted (window scoring); V is neither
+// loaded nor multiplied and no output is written.
+template <int D, int WAVES, int RB, int BN, bool DENSE, bool RASTER, bool LSE_ONLY = false>
 __global__ void __launch_bounds__(WAVES * 64, (WAVES <= 4 ? 2 : 1))
 attn_bf16_kernel(const AttnParams p) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
@@ -277,12 +279,12 @@ attn_bf16_kernel(const AttnParams p) {
       int base, c0, nv;
       walk.at_raster(p, it, &base, &c0, &nv);
       load_rows<C, WAVES>(kg, base, nv, kdst, wave, lane, rtab + c0);
-      load_rows<C, WAVES>(vg, base, nv, vdst, wave, lane, rtab + c0);
+      if (!LSE_ONLY) load_rows<C, WAVES>(vg, base, nv, vdst, wave, lane, rtab + c0);
     } else {
       int row0, nv;
       walk.at(it, &row0, &nv);
       load_rows<C, WAVES>(kg, row0, nv, kdst, wave, lane);
-      load_rows<C, WAVES>(vg, row0, nv, vdst, wave, lane);
+      if (!LSE_ONLY) load_rows<C, WAVES>(vg, row0, nv, vdst, wave, lane);
     }
   };
   dma(0, kb0, vb0);
@@ -299,13 +301,13 @@ attn_bf16_kernel(const AttnParams p) {
     if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
     qk_chunk<C, RB>(w, kcur, l16, g);
     softmax_chunk<C, RB>(w, nvalid, p.scale_log2, g);
-    pv_chunk<C, RB>(w, vcur, l16, g);
+    if constexpr (!LSE_ONLY) pv_chunk<C, RB>(w, vcur, l16, g);
   };
   for (int it = 0; it < walk.n_chunks; it += 2) {
     chunk_step(kb0, vb0, kb1, vb1, it);
     if (it + 1 < walk.n_chunks) chunk_step(kb1, vb1, kb0, vb0, it + 1);
   }
-  store_out<C, RB>(w, og, p.lse ? p.lse + t.head_base / D : nullptr, rm, g);
+  store_out<C, RB>(w, LSE_ONLY ? nullptr : og, p.lse ? p.lse + t.head_base / D : nullptr, rm, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -325,7 +327,7 @@ __global__ void __launch_bounds__(kF32Threads) attn_f32_kernel(const AttnParams 
   const float* qg = static_cast<const float*>(p.q) + t.head_base;
   const float4* kg = reinterpret_cast<const float4*>(static_cast<const float*>(p.k) + t.head_base);
   const float4* vg = reinterpret_cast<const float4*>(static_cast<const float*>(p.v) + t.head_base);
-  float* og = static_cast<float*>(p.out) + t.head_base;
+  float* og = p.out ? static_cast<float*>(p.out) + t.head_base : nullptr;
 
   const int tid = threadIdx.x;
   const bool row_ok = tid < t.valid_rows;
@@ -399,9 +401,11 @@ __global__ void __launch_bounds__(kF32Threads) attn_f32_kernel(const AttnParams 
   if (row_ok) {
     const float inv = 1.0f / l;
     if (p.lse) p.lse[t.head_base / D + q_tok] = (m + __log2f(l)) * kLn2;
-    float* dst = og + (long long)q_tok * D;
+    if (og) {
+      float* dst = og + (long long)q_tok * D;
 #pragma unroll
-    for (int d = 0; d < D; ++d) dst[d] = o[d] * inv;
+      for (int d = 0; d < D; ++d) dst[d] = o[d] * inv;
+    }
   }
 }
 
@@ -450,7 +454,17 @@ int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
   AttnParams p;
   fill_params(pr, C::kRows, &p);
   const unsigned grid = (unsigned)p.per_xcd * kXcds;
-  if (pr.dense)
+  if (pr.lse_only) {
+    if (pr.dense)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false, true>), dim3(grid),
+                         dim3(C::kThreads), 0, stream, p);
+    else if (pr.raster)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, true>), dim3(grid),
+                         dim3(C::kThreads), raster_table_bytes(pr), stream, p);
+    else
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false, true>), dim3(grid),
+                         dim3(C::kThreads), 0, stream, p);
+  } else if (pr.dense)
     hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false>), dim3(grid),
                        dim3(C::kThreads), 0, stream, p);
   else if (pr.raster)

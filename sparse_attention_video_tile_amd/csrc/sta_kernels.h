@@ -26,6 +26,7 @@ struct AttnProblem {
   float scale;
   bool dense;      // true: every query attends to all S keys
   bool raster;     // STA only: q, k, v, out in raster order (else tile-major)
+  bool lse_only;   // write lse only (out and v are not touched)
   Geometry g;      // for dense problems only g.S is used
   // Window per head in tiles (sparse problems only).
   uint16_t omega[STA_MAX_HEADS][3];
@@ -57,6 +58,11 @@ struct BwdProblem {
 
 // Same return convention as launch_attention.
 int launch_backward(const BwdProblem& p, void* stream);
+
+// recall[bh * n_cand + c] = mean over the S rows of exp(lse_win - lse_full),
+// for bh < BH (both lse arrays [BH][S]).
+int launch_recall_reduce(const float* lse_full, const float* lse_win, float* recall, int BH, int S,
+                         int n_cand, int c, void* stream);
 
 const char* hip_error_string(int code);
 

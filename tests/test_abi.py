@@ -199,3 +199,26 @@ def test_backward_raster_limit_counts_transposed_runs(lib):
     a = backward_args(order=1, T=1, H=1, W=16384, tile=i3(1, 1, 4096), win=i3(1, 1, 8192), d=64)
     assert call_backward(lib, a) == -2
     assert "12288" in binding.last_error()
+
+
+def test_window_recall_rejects_bad_arguments(lib):
+    f = lib.sta_window_recall
+    t = i3(6, 8, 8)
+    cands = binding._int_array([18, 24, 24, 30, 40, 40])
+    base = dict(q=FAKE, k=FAKE * 2000, r=FAKE * 4000, ws=FAKE * 6000, B=1, heads=2, d=128, T=30,
+                H=48, W=80, tile=t, c=cands, n=2, scale=0.1, dt=0, order=1)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["q"], a["k"], a["r"], a["ws"], a["B"], a["heads"], a["d"], a["T"], a["H"],
+                 a["W"], a["tile"], a["c"], a["n"], a["scale"], a["dt"], a["order"], None)
+
+    assert call(q=None) == -1
+    assert call(ws=None) == -1
+    assert call(n=0) == -1
+    assert call(order=7) == -1
+    assert call(c=binding._int_array([18, 24, 24, 30, 40, 41])) == -1   # second candidate invalid
+    assert "window" in binding.last_error()
+    assert call(d=32) == -2
+    assert call(ws=FAKE * 2000 + 64) == -1                              # workspace overlaps k
+    assert "overlap" in binding.last_error()

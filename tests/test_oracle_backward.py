@@ -167,3 +167,39 @@ def test_transposed_window_is_not_symmetric_under_clamping():
     assert counts[0, 0] == 8
     assert counts.min() == 8 and counts.max() > 27
     assert counts.sum() == 300 * 27
+
+
+# ----------------------------------------------------------------------------
+# Window recall
+# ----------------------------------------------------------------------------
+
+RECALL_VOL, RECALL_TILE = (6, 4, 6), (2, 2, 2)
+RECALL_CANDS = [(2, 2, 2), (4, 2, 4), (2, 4, 6), (6, 4, 6)]
+
+
+def test_recall_equals_lse_difference_from_a_library_logsumexp():
+    """recall = mean_i exp(lse_window(i) - logsumexp over all keys(i)); the full
+    log-sum-exp here comes from scipy, the window one from the pinned lse."""
+    q, k, _, _ = draw((2, 2) + RECALL_VOL + (8,), 14)
+    got = oracle.window_recall(q, k, RECALL_TILE, RECALL_CANDS, 0.5)
+    for b in range(2):
+        for h in range(2):
+            s = 0.5 * q[b, h].reshape(-1, 8) @ k[b, h].reshape(-1, 8).T
+            full = logsumexp(s, axis=1)
+            for c, w in enumerate(RECALL_CANDS):
+                lw = oracle.sta_lse(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], RECALL_TILE, [w], 0.5)
+                want = np.mean(np.exp(lw.reshape(-1) - full))
+                assert abs(got[b, h, c] - want) <= 1e-12
+
+
+def test_recall_special_cases():
+    """Whole-volume window keeps everything; with q = 0 attention is uniform, so
+    a window keeps its share of the keys; recall grows with nested windows."""
+    q, k, _, _ = draw((1, 1) + RECALL_VOL + (8,), 15)
+    got = oracle.window_recall(q, k, RECALL_TILE, RECALL_CANDS, 0.7)[0, 0]
+    assert abs(got[-1] - 1.0) <= 1e-12
+    assert 0 < got[0] < got[1] < got[-1]   # (2,2,2) inside (4,2,4) inside the volume
+    S = 6 * 4 * 6
+    zero = oracle.window_recall(np.zeros_like(q), k, RECALL_TILE, RECALL_CANDS, 0.7)[0, 0]
+    for c, w in enumerate(RECALL_CANDS):
+        assert abs(zero[c] - w[0] * w[1] * w[2] / S) <= 1e-12
