@@ -270,12 +270,21 @@ attn_bf16_kernel(const AttnParams p) {
   const int l16 = lane & 15;
   const int g = lane >> 4;
   const ChunkWalk walk = make_walk<BN, DENSE>(t, p.S);
-  if (RASTER) {
+  // Plane chunks: raster rows by arithmetic (no table); else the table.
+  const bool plane = RASTER && BN == 64 && p.plane_cpt > 0;
+  int lane_row[(C::kBlocks + WAVES - 1) / WAVES];
+  if (plane) {
+    plane_lane_rows<C, WAVES>(p, wave, lane, lane_row);
+  } else if (RASTER) {
     for (int e = threadIdx.x; e < walk.run_len; e += C::kThreads) rtab[e] = run_offset_raster(p, e);
     __syncthreads();
   }
   auto dma = [&](int it, char* kdst, char* vdst) __attribute__((always_inline)) {
-    if (RASTER) {
+    if (RASTER && plane) {
+      const int row0 = walk.at_plane(p, it);
+      load_rows_plane<C, WAVES>(kg, row0, lane_row, kdst, wave, lane);
+      if (!LSE_ONLY) load_rows_plane<C, WAVES>(vg, row0, lane_row, vdst, wave, lane);
+    } else if (RASTER) {
       int base, c0, nv;
       walk.at_raster(p, it, &base, &c0, &nv);
       load_rows<C, WAVES>(kg, base, nv, kdst, wave, lane, rtab + c0);
@@ -426,6 +435,7 @@ void fill_params(const AttnProblem& pr, int rows_per_item, AttnParams* p) {
     p->nt = p->nh = p->nw = 1;
     p->tau = pr.g.S;
     p->H = p->W = p->ct = p->ch = p->cw = 1;
+    p->plane_cpt = p->plane_cpp = 0;
   } else {
     p->n_units = pr.g.n_tiles;
     p->unit_rows = pr.g.tau;
@@ -433,6 +443,7 @@ void fill_params(const AttnProblem& pr, int rows_per_item, AttnParams* p) {
     p->tau = pr.g.tau;
     p->H = pr.g.H; p->W = pr.g.W;
     p->ct = pr.g.ct; p->ch = pr.g.ch; p->cw = pr.g.cw;
+    set_plane_chunks(p);
     for (int h = 0; h < pr.heads; ++h)
       for (int a = 0; a < 3; ++a) p->omega[h][a] = pr.omega[h][a];
   }
@@ -454,13 +465,15 @@ int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
   AttnParams p;
   fill_params(pr, C::kRows, &p);
   const unsigned grid = (unsigned)p.per_xcd * kXcds;
+  // plane chunks address K/V by arithmetic and need no offset table
+  const unsigned table = (BN == 64 && p.plane_cpt > 0) ? 0 : raster_table_bytes(pr);
   if (pr.lse_only) {
     if (pr.dense)
       hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false, true>), dim3(grid),
                          dim3(C::kThreads), 0, stream, p);
     else if (pr.raster)
       hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, true>), dim3(grid),
-                         dim3(C::kThreads), raster_table_bytes(pr), stream, p);
+                         dim3(C::kThreads), table, stream, p);
     else
       hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false, true>), dim3(grid),
                          dim3(C::kThreads), 0, stream, p);
@@ -469,7 +482,7 @@ int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
                        dim3(C::kThreads), 0, stream, p);
   else if (pr.raster)
     hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true>), dim3(grid),
-                       dim3(C::kThreads), raster_table_bytes(pr), stream, p);
+                       dim3(C::kThreads), table, stream, p);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false>), dim3(grid),
                        dim3(C::kThreads), 0, stream, p);

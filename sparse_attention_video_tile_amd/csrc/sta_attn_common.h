@@ -43,6 +43,10 @@ struct AttnParams {
   int dense;
   int nt, nh, nw, tau;
   int H, W, ct, ch, cw;  // volume and tile, for raster-order addressing
+  // Raster order, key chunks of 64 rows that each lie inside one t-plane of
+  // one tile (64 divides c_h * c_w, c_w divides 64, tau a multiple of 64):
+  // chunks per tile and per plane. 0 when that does not hold.
+  int plane_cpt, plane_cpp;
   uint16_t omega[STA_MAX_HEADS][3];
   uint8_t head_order[STA_MAX_HEADS];  // logical head slot -> head (heaviest windows first)
 };
@@ -64,6 +68,17 @@ __device__ __forceinline__ int logical_task(const AttnParams& p) {
 // the XCDs take turns in blocks of kMixedGroup tasks: every XCD then gets the
 // same mix of heavy and light work, and the light work comes last.
 constexpr int kMixedGroup = 32;
+
+// Host side: plane_cpt / plane_cpp of a sparse problem (needs tau, ch, cw).
+inline void set_plane_chunks(AttnParams* p) {
+  const int plane = p->ch * p->cw;
+  if (p->tau % 64 == 0 && plane % 64 == 0 && 64 % p->cw == 0) {
+    p->plane_cpt = p->tau / 64;
+    p->plane_cpp = plane / 64;
+  } else {
+    p->plane_cpt = p->plane_cpp = 0;
+  }
+}
 
 inline void plan_tasks(AttnParams* p, long long tasks, int heads, bool dense) {
   p->n_tasks = (int)tasks;
@@ -290,6 +305,41 @@ __device__ __forceinline__ void load_rows(const bf16_t* src, int kv_row0, int nv
   }
 }
 
+// The same loads when every key of the chunk lies in one t-plane of one tile
+// (plane_cpt > 0): the raster row of key `row` of the chunk is
+// chunk_row0 + lane_row[b], with lane_row the row's offset inside its plane
+// ((row / c_w) * W + row % c_w), computed once per lane.
+template <class C, int WAVES>
+__device__ __forceinline__ int plane_iters() { return (C::kBlocks + WAVES - 1) / WAVES; }
+
+template <class C, int WAVES>
+__device__ __forceinline__ void plane_lane_rows(const AttnParams& p, int wave, int lane,
+                                                int (&lane_row)[(C::kBlocks + WAVES - 1) / WAVES]) {
+  constexpr int kIter = (C::kBlocks + WAVES - 1) / WAVES;
+#pragma unroll
+  for (int b = 0; b < kIter; ++b) {
+    const int row = (wave + WAVES * b) * C::kRowsPerBlock + lane / C::kCPR;
+    lane_row[b] = (row / p.cw) * p.W + row % p.cw;
+  }
+}
+
+template <class C, int WAVES>
+__device__ __forceinline__ void load_rows_plane(const bf16_t* src, int chunk_row0,
+                                                const int (&lane_row)[(C::kBlocks + WAVES - 1) / WAVES],
+                                                char* buf, int wave, int lane) {
+  constexpr int kIter = (C::kBlocks + WAVES - 1) / WAVES;
+#pragma unroll
+  for (int b = 0; b < kIter; ++b) {
+    const int blk = wave + WAVES * b;
+    if (kIter * WAVES != C::kBlocks && blk >= C::kBlocks) break;  // wave-uniform
+    const int row = blk * C::kRowsPerBlock + lane / C::kCPR;
+    const int pos = lane % C::kCPR;
+    const int c = pos ^ ((swz<C::kCPR>(row, 0) >> 4) & (C::kCPR - 1));
+    const long long off = (long long)(chunk_row0 + lane_row[b]) * (C::kRowBytes / 2) + c * 8;
+    __builtin_amdgcn_global_load_lds(src + off, (lds_void*)(buf + blk * 1024), 16, 0, 0);
+  }
+}
+
 __device__ __forceinline__ void wait_vm_all() {
   // vmcnt(0); expcnt and lgkmcnt left at their maxima (not waited on).
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -333,6 +383,18 @@ struct ChunkWalk {
     const int c0 = (it - run * chunks_per_run) * bn;
     *row0 = (dense ? 0 : kv.run_start(run)) + c0;
     *nvalid = min(bn, run_len - c0);
+  }
+  // Raster order, plane chunks: the raster token of the chunk's first key
+  // (the chunk is one 64-row piece of one t-plane of one tile).
+  __device__ __forceinline__ int at_plane(const AttnParams& p, int it) const {
+    const int run = it / chunks_per_run;
+    const int j = it - run * chunks_per_run;
+    const int tw = j / p.plane_cpt;
+    const int pp = j - tw * p.plane_cpt;
+    const int lt = pp / p.plane_cpp;
+    const int sub = pp - lt * p.plane_cpp;
+    return kv.run_start_raster(run, p.H, p.W, p.ct, p.ch, p.cw) +
+           (lt * p.H + sub * (64 / p.cw)) * p.W + tw * p.cw;
   }
   // Raster order: the run's first raster token, the chunk's first key within
   // the run, and the number of valid keys.

@@ -553,6 +553,7 @@ void fill_bwd_params(const BwdProblem& pr, int rows_per_item, AttnParams* p, Bwd
   p->tau = a.g.tau;
   p->H = a.g.H; p->W = a.g.W;
   p->ct = a.g.ct; p->ch = a.g.ch; p->cw = a.g.cw;
+  set_plane_chunks(p);
   for (int h = 0; h < a.heads; ++h)
     for (int x = 0; x < 3; ++x) p->omega[h][x] = a.omega[h][x];
   p->row_blocks = (p->unit_rows + rows_per_item - 1) / rows_per_item;
