@@ -30,6 +30,11 @@ Readings taken where the pages are silent:
 * Softmax is base e with a positive scale (1/sqrt(d) by default).
 * Tile-major order: tiles in raster (t, h, w) order, tokens inside a tile in
   raster order.
+* A volume the tile does not divide is covered by the grid of ceil(extent /
+  c) tiles per axis, as if padded up to whole tiles; windows are counted in
+  tiles of that grid with the same rule. Padded positions are not tokens:
+  they are never keys and have no output. Tile-major tensors of such a volume
+  hold n_tiles * tau rows, the padded positions as zero rows.
 
 All arithmetic here is float64. The attention is the plain definition: an
 explicit token-level mask built from token coordinates, then a two-pass
@@ -50,20 +55,27 @@ Triple = Tuple[int, int, int]
 # ----------------------------------------------------------------------------
 
 def tile_grid(volume: Sequence[int], tile: Sequence[int]) -> Triple:
-    """Number of tiles per axis, n_a = extent_a / c_a (the tile must divide the volume)."""
+    """Number of tiles per axis, n_a = ceil(extent_a / c_a) (the last tile of an
+    axis the tile does not divide is partly padding)."""
     n = []
     for e, c in zip(volume, tile):
-        if c <= 0 or e <= 0 or e % c:
-            raise ValueError(f"tile {tuple(tile)} does not divide volume {tuple(volume)}")
-        n.append(e // c)
+        if c <= 0 or e <= 0:
+            raise ValueError(f"tile {tuple(tile)} and volume {tuple(volume)} must be positive")
+        n.append(-(-e // c))
     return tuple(n)
 
 
+def is_padded(volume: Sequence[int], tile: Sequence[int]) -> bool:
+    return any(e % c for e, c in zip(volume, tile))
+
+
 def window_in_tiles(window: Sequence[int], tile: Sequence[int], volume: Sequence[int]) -> Triple:
-    """Window size in tiles, w_a / c_a; the window must be whole tiles inside the volume."""
+    """Window size in tiles, w_a / c_a; the window must be whole tiles within the
+    tile grid (at most n_a tiles)."""
     out = []
-    for w, c, e in zip(window, tile, volume):
-        if w <= 0 or w % c or w > e:
+    n = tile_grid(volume, tile)
+    for w, c, na in zip(window, tile, n):
+        if w <= 0 or w % c or w // c > na:
             raise ValueError(f"window {tuple(window)} is not whole tiles of {tuple(tile)} within {tuple(volume)}")
         out.append(w // c)
     return tuple(out)
@@ -92,7 +104,7 @@ def axis_mask(extent: int, c: int, omega: int) -> np.ndarray:
     and spans ``omega`` tiles; the key is inside iff its own tile floor(r'/c)
     lies in that span.
     """
-    n = extent // c
+    n = -(-extent // c)
     r = np.arange(extent)
     start = np.array([window_start(int(x) // c, n, omega) for x in r])
     k_tile = r // c
@@ -122,9 +134,10 @@ def tile_tokens(volume, tile, tile_index: int) -> np.ndarray:
     n = tile_grid(volume, tile)
     it, rem = divmod(tile_index, n[1] * n[2])
     ih, iw = divmod(rem, n[2])
-    t = np.arange(it * tile[0], (it + 1) * tile[0])
-    y = np.arange(ih * tile[1], (ih + 1) * tile[1])
-    x = np.arange(iw * tile[2], (iw + 1) * tile[2])
+    # positions past the volume (a partly padded tile) are not tokens
+    t = np.arange(it * tile[0], min((it + 1) * tile[0], T))
+    y = np.arange(ih * tile[1], min((ih + 1) * tile[1], H))
+    x = np.arange(iw * tile[2], min((iw + 1) * tile[2], W))
     tt, yy, xx = np.meshgrid(t, y, x, indexing="ij")
     return ((tt * H + yy) * W + xx).ravel()
 
@@ -155,8 +168,11 @@ def tile_selection(volume, tile, window) -> np.ndarray:
     """
     n = tile_grid(volume, tile)
     om = window_in_tiles(window, tile, volume)
+    # The rule applied to every position of the tile grid (padded ones too)
+    # gives whole blocks; on a divisible volume these are exactly the token
+    # mask's blocks.
     per_axis = [
-        _classify_blocks(axis_mask(volume[a], tile[a], om[a]), tile[a], tile[a]) for a in range(3)
+        _classify_blocks(axis_mask(n[a] * tile[a], tile[a], om[a]), tile[a], tile[a]) for a in range(3)
     ]
     sel = (per_axis[0][:, None, None, :, None, None]
            & per_axis[1][None, :, None, None, :, None]
@@ -166,7 +182,10 @@ def tile_selection(volume, tile, window) -> np.ndarray:
 
 
 def tile_selection_from_token_mask(volume, tile, window) -> np.ndarray:
-    """Same as :func:`tile_selection`, from the full 3-D token mask (small volumes only)."""
+    """Same as :func:`tile_selection`, from the full 3-D token mask (small,
+    tile-divisible volumes only)."""
+    if is_padded(volume, tile):
+        raise ValueError("needs a volume the tile divides")
     n = tile_grid(volume, tile)
     n_tiles = n[0] * n[1] * n[2]
     S = volume[0] * volume[1] * volume[2]
@@ -294,25 +313,29 @@ def full_attention_rows(q, k, v, scale, b: int, h: int, query_rows) -> np.ndarra
 # ----------------------------------------------------------------------------
 
 def to_tile_major(x: np.ndarray, tile: Sequence[int]) -> np.ndarray:
-    """(B, heads, T, H, W, d) raster -> (B, heads, S, d) tile-major.
+    """(B, heads, T, H, W, d) raster -> (B, heads, n_tiles * tau, d) tile-major.
 
     Tiles in raster order of tile coordinates, tokens within a tile in raster
-    order of their local coordinates.
+    order of their local coordinates; padded positions are zero rows.
     """
     B, heads, T, H, W, d = x.shape
     ct, ch, cw = tile
     nt, nh, nw = tile_grid((T, H, W), tile)
-    y = x.reshape(B, heads, nt, ct, nh, ch, nw, cw, d)
+    xp = np.zeros((B, heads, nt * ct, nh * ch, nw * cw, d), dtype=x.dtype)
+    xp[:, :, :T, :H, :W] = x
+    y = xp.reshape(B, heads, nt, ct, nh, ch, nw, cw, d)
     y = y.transpose(0, 1, 2, 4, 6, 3, 5, 7, 8)
-    return np.ascontiguousarray(y).reshape(B, heads, T * H * W, d)
+    return np.ascontiguousarray(y).reshape(B, heads, nt * nh * nw * ct * ch * cw, d)
 
 
 def from_tile_major(y: np.ndarray, volume: Sequence[int], tile: Sequence[int]) -> np.ndarray:
-    """Inverse of :func:`to_tile_major`: (B, heads, S, d) -> (B, heads, T, H, W, d)."""
+    """Inverse of :func:`to_tile_major`: (B, heads, n_tiles * tau, d) ->
+    (B, heads, T, H, W, d); padded rows are dropped."""
     B, heads, S, d = y.shape
     T, H, W = volume
     ct, ch, cw = tile
     nt, nh, nw = tile_grid(volume, tile)
     z = y.reshape(B, heads, nt, nh, nw, ct, ch, cw, d)
     z = z.transpose(0, 1, 2, 5, 3, 6, 4, 7, 8)
-    return np.ascontiguousarray(z).reshape(B, heads, T, H, W, d)
+    z = z.reshape(B, heads, nt * ct, nh * ch, nw * cw, d)[:, :, :T, :H, :W]
+    return np.ascontiguousarray(z)

@@ -22,6 +22,7 @@ CASES = [
     ("tile48_ragged", (9, 8, 12), (3, 4, 4), [(6, 4, 8), (9, 8, 12)], 128, "bf16"),
     ("tile128", (8, 8, 16), (4, 4, 8), [(4, 8, 8)], 128, "bf16"),
     ("tile8_tiny", (4, 4, 6), (2, 2, 2), [(2, 2, 2), (4, 2, 4)], 64, "bf16"),
+    ("image_2d_tile8x8", (1, 32, 48), (1, 8, 8), [(1, 24, 24), (1, 8, 16)], 128, "bf16"),
     ("f32_d64", (12, 16, 16), (4, 4, 4), [(12, 12, 12), (4, 8, 12)], 64, "f32"),
     ("f32_d128_ragged", (9, 8, 12), (3, 4, 4), [(6, 4, 8)], 128, "f32"),
 ]

@@ -33,6 +33,8 @@ SMALL_CASES = [
     ("tile128", (8, 8, 16), (4, 4, 8), [(4, 8, 8), (8, 4, 16)], 128, "bf16"),
     ("tile8_tiny", (4, 4, 6), (2, 2, 2), [(2, 2, 2), (4, 4, 6), (4, 2, 4)], 128, "bf16"),
     ("one_tile_volume", (6, 8, 8), (6, 8, 8), [(6, 8, 8)], 128, "bf16"),
+    # 2D (image) STA: one frame, tiles of 1 x 8 x 8 (a 2D window slid tile by tile)
+    ("image_2d_tile8x8", (1, 32, 48), (1, 8, 8), [(1, 24, 24), (1, 32, 48), (1, 8, 16)], 128, "bf16"),
     ("f32_tiny_like", (12, 16, 16), (4, 4, 4), [(12, 12, 12), (4, 8, 12)], 64, "f32"),
     ("f32_d128", (6, 8, 8), (2, 4, 4), [(4, 8, 4), (6, 8, 8)], 128, "f32"),
     ("f32_ragged", (9, 8, 12), (3, 4, 4), [(6, 4, 8)], 64, "f32"),

@@ -187,11 +187,14 @@ def test_kv_pair_count():
 
 def test_invalid_geometry_rejected():
     with pytest.raises(ValueError):
-        oracle.tile_grid((30, 48, 80), (7, 8, 8))
+        oracle.tile_grid((30, 48, 80), (0, 8, 8))
     with pytest.raises(ValueError):
         oracle.window_in_tiles((20, 24, 24), (6, 8, 8), (30, 48, 80))
     with pytest.raises(ValueError):
         oracle.window_in_tiles((36, 24, 24), (6, 8, 8), (30, 48, 80))
+    # a tile that does not divide the volume covers it with a padded grid
+    assert oracle.tile_grid((30, 48, 80), (7, 8, 8)) == (5, 6, 10)
+    assert oracle.window_in_tiles((35, 24, 24), (7, 8, 8), (30, 48, 80)) == (5, 3, 3)
 
 
 # ----------------------------------------------------------------------------
