@@ -25,8 +25,18 @@
  *   tile-major: s' = tile * tau + local, tau = c_t * c_h * c_w,
  *               tile  = (floor(t/c_t) * n_h + floor(y/c_h)) * n_w + floor(x/c_w),
  *               local = ((t % c_t) * c_h + (y % c_h)) * c_w + (x % c_w)
- *   with n_a = extent_a / c_a. Tensors are [B][heads][S][head_dim], contiguous,
- *   S = T * H * W, in one of these orders as each call states.
+ *   with n_a = ceil(extent_a / c_a). Tensors are [B][heads][rows][head_dim],
+ *   contiguous, in one of these orders as each call states: raster tensors
+ *   have S = T * H * W rows, tile-major tensors n_tiles * tau rows.
+ *
+ * Volumes the tile does not divide (a reading; the pages do not describe
+ * padding): the tile grid covers the volume padded up to whole tiles, windows
+ * are counted in tiles of that grid with the same rule, and positions past
+ * the volume are not tokens -- they are never keys and have no output. In
+ * tile-major order they are rows of zeros (sta_reorder_tiles writes zeros,
+ * the attention calls leave output rows of padding unwritten). Float32
+ * attention on such a volume is refused (STA_ERR_UNSUPPORTED); the layout
+ * calls accept it.
  *
  * Conventions for every call.
  *   - Device pointers are caller-owned device memory (e.g. torch tensors). The
@@ -79,7 +89,7 @@ int sta_abi_version(void);
  * contiguous run of tau rows so that attention can stream it.
  *   x_raster: device, [B][heads][S][head_dim] raster order, read.
  *   x_tiled:  device, same size, written in tile-major order. No overlap.
- *   tile:     host int[3] (c_t, c_h, c_w), each dividing (T, H, W).
+ *   tile:     host int[3] (c_t, c_h, c_w), positive (see padding above).
  *   dtype:    sta_dtype; head_dim * element size must be a multiple of 16 bytes.
  */
 int sta_reorder_tiles(const void* x_raster, void* x_tiled, int B, int heads, int head_dim,
@@ -101,9 +111,9 @@ int sta_restore_order(const void* x_tiled, void* x_raster, int B, int heads, int
  *             tile coordinates), the rest are -1.
  *   kv_count: device int32 [heads][N_t]; omega_t * omega_h * omega_w.
  *   window:   host int[heads][3], tokens, each a multiple of the tile and at
- *             most the volume on its axis.
+ *             most the tile grid (n_a * c_a) on its axis.
  *   max_kv:   row length of kv_list; must be >= the largest count.
- * N_t = (T/c_t) * (H/c_h) * (W/c_w).
+ * N_t = n_t * n_h * n_w.
  */
 int sta_kv_tiles(int* kv_list, int* kv_count, int heads, int T, int H, int W, const int* tile,
                  const int* window, int max_kv, void* stream);

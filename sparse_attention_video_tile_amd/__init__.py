@@ -23,4 +23,5 @@ from .binding import (  # noqa: F401
     sta_reorder_tiles,
     sta_restore_order,
     sta_window_recall,
+    tile_major_rows,
 )

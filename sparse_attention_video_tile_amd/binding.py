@@ -149,6 +149,15 @@ def _stream(dev: torch.device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+def tile_major_rows(volume: Sequence[int], tile: Sequence[int]) -> int:
+    """Rows of a tile-major tensor: n_tiles * tau, with n = ceil(extent / c) per
+    axis (a volume the tile does not divide is padded up to whole tiles)."""
+    rows = 1
+    for e, c in zip(volume, tile):
+        rows *= -(-int(e) // int(c)) * int(c)
+    return rows
+
+
 def _windows_per_head(window, heads: int):
     w = torch.as_tensor(window, dtype=torch.int64).reshape(-1, 3)
     if w.shape[0] == 1 and heads > 1:
@@ -163,14 +172,16 @@ def _windows_per_head(window, heads: int):
 # ---------------------------------------------------------------------------
 
 def sta_reorder_tiles(x: torch.Tensor, tile: Sequence[int], out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Raster (B, heads, T, H, W, d) -> tile-major (B, heads, S, d)."""
+    """Raster (B, heads, T, H, W, d) -> tile-major (B, heads, n_tiles * tau, d);
+    padding rows of a volume the tile does not divide are zeros."""
     lib = load_library()
     if x.dim() != 6:
         raise ValueError("x must be (B, heads, T, H, W, d)")
     B, heads, T, H, W, d = x.shape
+    rows = tile_major_rows((T, H, W), tile)
     if out is None:
-        out = torch.empty((B, heads, T * H * W, d), dtype=x.dtype, device=x.device)
-    elif tuple(out.shape) != (B, heads, T * H * W, d) or out.dtype != x.dtype:
+        out = torch.empty((B, heads, rows, d), dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != (B, heads, rows, d) or out.dtype != x.dtype:
         raise ValueError("out must be (B, heads, S, d) with the input's dtype")
     dev = _require_gpu(x, out)
     with torch.cuda.device(dev):
@@ -188,8 +199,8 @@ def sta_restore_order(x: torch.Tensor, volume: Sequence[int], tile: Sequence[int
         raise ValueError("x must be (B, heads, S, d)")
     B, heads, S, d = x.shape
     T, H, W = (int(a) for a in volume)
-    if S != T * H * W:
-        raise ValueError(f"S={S} does not match volume {tuple(volume)}")
+    if S != tile_major_rows(volume, tile):
+        raise ValueError(f"S={S} does not match volume {tuple(volume)} with tile {tuple(tile)}")
     if out is None:
         out = torch.empty((B, heads, T, H, W, d), dtype=x.dtype, device=x.device)
     elif tuple(out.shape) != (B, heads, T, H, W, d) or out.dtype != x.dtype:
@@ -217,7 +228,7 @@ def _tile_lists(fn_name: str, heads: int, volume, tile, window, max_len, device,
     lib = load_library()
     T, H, W = (int(a) for a in volume)
     ws = _windows_per_head(window, heads)
-    n = [int(e) // int(c) for e, c in zip((T, H, W), tile)]
+    n = [-(-int(e) // int(c)) for e, c in zip((T, H, W), tile)]
     n_tiles = n[0] * n[1] * n[2]
     if max_len is None:
         max_len = 0
@@ -274,8 +285,8 @@ def sta_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, volume: Seque
         raise ValueError("q, k, v must share a dtype")
     B, heads, S, d = q.shape
     T, H, W = (int(a) for a in volume)
-    if S != T * H * W:
-        raise ValueError(f"S={S} does not match volume {tuple(volume)}")
+    if S != tile_major_rows(volume, tile):
+        raise ValueError(f"S={S} does not match volume {tuple(volume)} with tile {tuple(tile)}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -354,13 +365,13 @@ def raster_run_fits(tile: Sequence[int], window, heads: int, volume: Optional[Se
         if om * tau > STA_MAX_RASTER_RUN:
             return False
         if backward:
-            nw = int(volume[2]) // int(tile[2])
+            nw = -(-int(volume[2]) // int(tile[2]))
             if max(_inverse_len(j, nw, om) for j in range(nw)) * tau > STA_MAX_RASTER_RUN:
                 return False
     return True
 
 
-def _order_shapes(q: torch.Tensor, volume):
+def _order_shapes(q: torch.Tensor, volume, tile):
     """(B, heads, d, (T, H, W), order code) of a raster 6-D or tile-major 4-D tensor."""
     if q.dim() == 6:
         B, heads, T, H, W, d = q.shape
@@ -370,8 +381,8 @@ def _order_shapes(q: torch.Tensor, volume):
             raise ValueError("tile-major (B, heads, S, d) tensors need the volume")
         B, heads, S, d = q.shape
         T, H, W = (int(a) for a in volume)
-        if S != T * H * W:
-            raise ValueError(f"S={S} does not match volume {tuple(volume)}")
+        if S != tile_major_rows(volume, tile):
+            raise ValueError(f"S={S} does not match volume {tuple(volume)} with tile {tuple(tile)}")
         return B, heads, d, (T, H, W), STA_TILE_MAJOR
     raise ValueError("tensors must be raster (B, heads, T, H, W, d) or tile-major (B, heads, S, d)")
 
@@ -386,7 +397,7 @@ def sta_forward_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tile: Seq
     lib = load_library()
     if q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype:
         raise ValueError("q, k, v must share shape and dtype")
-    B, heads, d, (T, H, W), order = _order_shapes(q, volume)
+    B, heads, d, (T, H, W), order = _order_shapes(q, volume, tile)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -418,7 +429,7 @@ def sta_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
     for name, x in (("k", k), ("v", v), ("out", out), ("dout", dout)):
         if x.shape != q.shape or x.dtype != q.dtype:
             raise ValueError(f"{name} must match q in shape and dtype")
-    B, heads, d, (T, H, W), order = _order_shapes(q, volume)
+    B, heads, d, (T, H, W), order = _order_shapes(q, volume, tile)
     if lse.shape != q.shape[:-1] or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor of q's shape without d")
     if scale is None:
@@ -448,14 +459,14 @@ def sta_window_recall(q: torch.Tensor, k: torch.Tensor, tile: Sequence[int], can
     lib = load_library()
     if k.shape != q.shape or k.dtype != q.dtype:
         raise ValueError("k must match q in shape and dtype")
-    B, heads, d, (T, H, W), order = _order_shapes(q, volume)
+    B, heads, d, (T, H, W), order = _order_shapes(q, volume, tile)
     cand = [int(x) for x in torch.as_tensor(candidates, dtype=torch.int64).reshape(-1).tolist()]
     if len(cand) == 0 or len(cand) % 3:
         raise ValueError("candidates must be a non-empty list of (t, h, w) windows")
     n = len(cand) // 3
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    S = T * H * W
+    S = T * H * W if order == STA_RASTER else tile_major_rows((T, H, W), tile)
     if workspace is None:
         workspace = torch.empty((2, B, heads, S), dtype=torch.float32, device=q.device)
     elif workspace.numel() < 2 * B * heads * S or workspace.dtype != torch.float32 or not workspace.is_contiguous():

@@ -46,44 +46,59 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
-// Checks the volume and tile, fills g. Returns STA_OK or an error status.
+// Checks the volume and tile, fills g. A tile that does not divide the volume
+// is allowed: the grid then covers the volume padded up to whole tiles.
 int check_volume(int T, int H, int W, const int* tile, sta::Geometry* g) {
   if (!tile) return fail(STA_ERR_INVALID_ARG, "tile is NULL");
   if (T <= 0 || H <= 0 || W <= 0)
     return fail(STA_ERR_INVALID_ARG, "volume (%d,%d,%d) must be positive", T, H, W);
   if (tile[0] <= 0 || tile[1] <= 0 || tile[2] <= 0)
     return fail(STA_ERR_INVALID_ARG, "tile (%d,%d,%d) must be positive", tile[0], tile[1], tile[2]);
-  if (T % tile[0] || H % tile[1] || W % tile[2])
-    return fail(STA_ERR_INVALID_ARG, "tile (%d,%d,%d) does not divide volume (%d,%d,%d)", tile[0],
-                tile[1], tile[2], T, H, W);
   const long long S = (long long)T * H * W;
-  if (S > (1LL << 30)) return fail(STA_ERR_INVALID_ARG, "volume of %lld tokens is too large", S);
   g->T = T; g->H = H; g->W = W;
   g->ct = tile[0]; g->ch = tile[1]; g->cw = tile[2];
-  g->nt = T / tile[0]; g->nh = H / tile[1]; g->nw = W / tile[2];
-  g->n_tiles = g->nt * g->nh * g->nw;
-  g->tau = tile[0] * tile[1] * tile[2];
+  g->nt = (T + tile[0] - 1) / tile[0];
+  g->nh = (H + tile[1] - 1) / tile[1];
+  g->nw = (W + tile[2] - 1) / tile[2];
+  const long long tau = (long long)tile[0] * tile[1] * tile[2];
+  const long long n_tiles = (long long)g->nt * g->nh * g->nw;
+  if (tau * n_tiles > (1LL << 30))
+    return fail(STA_ERR_INVALID_ARG, "volume of %lld tokens (%lld with tile padding) is too large", S,
+                tau * n_tiles);
+  g->n_tiles = (int)n_tiles;
+  g->tau = (int)tau;
   g->S = (int)S;
+  g->S_pad = (int)(tau * n_tiles);
+  g->padded = g->S_pad != g->S;
   return STA_OK;
 }
 
 // Checks the per-head windows against the geometry; fills omega (tiles).
 int check_windows(const sta::Geometry& g, int heads, const int* window, uint16_t (*omega)[3]) {
   if (!window) return fail(STA_ERR_INVALID_ARG, "window is NULL");
-  const int ext[3] = {g.T, g.H, g.W};
   const int c[3] = {g.ct, g.ch, g.cw};
+  const int n[3] = {g.nt, g.nh, g.nw};
   for (int h = 0; h < heads; ++h) {
     for (int a = 0; a < 3; ++a) {
       const int w = window[3 * h + a];
-      if (w <= 0 || w % c[a] || w > ext[a])
+      if (w <= 0 || w % c[a] || w / c[a] > n[a])
         return fail(STA_ERR_INVALID_ARG,
                     "window (%d,%d,%d) of head %d must be a positive multiple of the tile "
-                    "(%d,%d,%d) and at most the volume (%d,%d,%d)",
-                    window[3 * h], window[3 * h + 1], window[3 * h + 2], h, g.ct, g.ch, g.cw, g.T,
-                    g.H, g.W);
+                    "(%d,%d,%d) and at most the tile grid (%d,%d,%d)",
+                    window[3 * h], window[3 * h + 1], window[3 * h + 2], h, g.ct, g.ch, g.cw,
+                    n[0] * c[0], n[1] * c[1], n[2] * c[2]);
       omega[h][a] = (uint16_t)(w / c[a]);
     }
   }
+  return STA_OK;
+}
+
+// float32 attention kernels take volumes the tile divides only.
+int check_f32_padding(const sta::Geometry& g, int dtype) {
+  if (g.padded && dtype == STA_F32)
+    return fail(STA_ERR_UNSUPPORTED,
+                "float32 attention needs a volume the tile divides (volume %dx%dx%d, tile %dx%dx%d)",
+                g.T, g.H, g.W, g.ct, g.ch, g.cw);
   return STA_OK;
 }
 
@@ -117,8 +132,10 @@ int reorder_common(const void* src, void* dst, int B, int heads, int head_dim, i
     return fail(STA_ERR_UNSUPPORTED, "input and output must be 16-byte aligned");
   const long long BH = (long long)B * heads;
   if (BH > (1LL << 24)) return fail(STA_ERR_INVALID_ARG, "B*heads=%lld is too large", BH);
-  const size_t bytes = (size_t)BH * g.S * row_bytes;
-  if (overlaps(src, bytes, dst, bytes)) return fail(STA_ERR_INVALID_ARG, "input and output overlap");
+  const size_t raster_bytes = (size_t)BH * g.S * row_bytes;
+  const size_t tiled_bytes = (size_t)BH * g.S_pad * row_bytes;
+  if (overlaps(src, to_tiles ? raster_bytes : tiled_bytes, dst, to_tiles ? tiled_bytes : raster_bytes))
+    return fail(STA_ERR_INVALID_ARG, "input and output overlap");
   return launched(sta::launch_reorder(src, dst, (int)BH, (int)row_bytes, g, to_tiles, stream));
 }
 
@@ -137,7 +154,8 @@ int attention_common(sta::AttnProblem& p, void* stream) {
   if (any % 16) return fail(STA_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
   const long long BH = (long long)p.B * p.heads;
   if (BH > (1LL << 24)) return fail(STA_ERR_INVALID_ARG, "B*heads=%lld is too large", BH);
-  const size_t bytes = (size_t)BH * p.g.S * p.head_dim * es;
+  const int rows = p.dense || p.raster ? p.g.S : p.g.S_pad;
+  const size_t bytes = (size_t)BH * rows * p.head_dim * es;
   if (overlaps(p.out, bytes, p.q, bytes) || overlaps(p.out, bytes, p.k, bytes) ||
       overlaps(p.out, bytes, p.v, bytes))
     return fail(STA_ERR_INVALID_ARG, "output overlaps an input");
@@ -280,12 +298,14 @@ int forward_common(const void* q, const void* k, const void* v, void* out, float
   int rc = check_volume(T, H, W, tile, &p.g);
   if (rc) return rc;
   if ((rc = check_windows(p.g, heads, window, p.omega))) return rc;
+  if ((rc = check_f32_padding(p.g, dtype))) return rc;
   if (raster && (rc = check_raster_runs(p.g, heads, p.omega, false))) return rc;
   if (lse) {
     if (reinterpret_cast<uintptr_t>(lse) % 4) return fail(STA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
     const int es = elem_size(dtype);
-    const size_t bytes = (size_t)B * heads * p.g.S * (es ? es : 1) * head_dim;
-    const size_t lbytes = (size_t)B * heads * p.g.S * sizeof(float);
+    const int rows = raster ? p.g.S : p.g.S_pad;
+    const size_t bytes = (size_t)B * heads * rows * (es ? es : 1) * head_dim;
+    const size_t lbytes = (size_t)B * heads * rows * sizeof(float);
     if (overlaps(lse, lbytes, q, bytes) || overlaps(lse, lbytes, k, bytes) ||
         overlaps(lse, lbytes, v, bytes) || overlaps(lse, lbytes, out, bytes))
       return fail(STA_ERR_INVALID_ARG, "lse overlaps a tensor");
@@ -321,6 +341,7 @@ int backward_common(const void* q, const void* k, const void* v, const void* out
   p.lse_only = false;
   if ((rc = check_volume(T, H, W, tile, &p.g))) return rc;
   if ((rc = check_windows(p.g, heads, window, p.omega))) return rc;
+  if ((rc = check_f32_padding(p.g, dtype))) return rc;
   if (p.raster && (rc = check_raster_runs(p.g, heads, p.omega, true))) return rc;
   const uintptr_t any16 = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out) |
@@ -331,8 +352,9 @@ int backward_common(const void* q, const void* k, const void* v, const void* out
     return fail(STA_ERR_INVALID_ARG, "lse and delta must be 4-byte aligned");
   const long long BH = (long long)B * heads;
   if (BH > (1LL << 24)) return fail(STA_ERR_INVALID_ARG, "B*heads=%lld is too large", BH);
-  const size_t tb = (size_t)BH * p.g.S * head_dim * es;
-  const size_t rb = (size_t)BH * p.g.S * sizeof(float);
+  const int rows = p.raster ? p.g.S : p.g.S_pad;
+  const size_t tb = (size_t)BH * rows * head_dim * es;
+  const size_t rb = (size_t)BH * rows * sizeof(float);
   const void* ins[6] = {q, k, v, out, dout, lse};
   const size_t in_bytes[6] = {tb, tb, tb, tb, tb, rb};
   const void* outs[4] = {dq, dk, dv, delta};
@@ -409,6 +431,11 @@ int sta_window_recall(const void* q, const void* k, float* recall, float* worksp
     return fail(STA_ERR_UNSUPPORTED, "head_dim %d: kernels exist for 64 and 128", head_dim);
   static thread_local sta::AttnProblem dense, win;
   if ((rc = check_volume(T, H, W, tile, &win.g))) return rc;
+  if ((rc = check_f32_padding(win.g, dtype))) return rc;
+  if (win.g.padded && order != STA_RASTER)
+    return fail(STA_ERR_UNSUPPORTED,
+                "window recall on a volume the tile does not divide needs raster order (the "
+                "full-attention pass would see the padding rows of a tile-major tensor)");
   // every candidate is a valid window (checked as one head each)
   static thread_local uint16_t om[STA_MAX_HEADS][3];
   for (int c = 0; c < n_candidates; ++c)

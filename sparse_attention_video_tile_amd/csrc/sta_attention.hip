@@ -85,16 +85,19 @@ __device__ __forceinline__ void qk_chunk(WaveState<C, RB>& w, const char* kbuf, 
 
 template <class C, int RB>
 __device__ __forceinline__ void softmax_max(WaveState<C, RB>& w, f32x4 (&sc)[RB][C::kKT],
-                                            int nvalid, float scale_log2, int g) {
-  if (nvalid < C::kBN) {
+                                            int nvalid, unsigned long long real, float scale_log2,
+                                            int g) {
+  if (nvalid < C::kBN || real != ~0ull) {
     keep_branch();
 #pragma unroll
     for (int kt = 0; kt < C::kKT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * kt + 4 * g + r >= nvalid)
+      for (int r = 0; r < 4; ++r) {
+        const int key = 16 * kt + 4 * g + r;
+        if (key >= nvalid || !((real >> key) & 1ull))
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) sc[rb][kt][r] = -INFINITY;
+      }
   }
   float mx[RB];
   bool grow = false;
@@ -159,9 +162,9 @@ __device__ __forceinline__ void softmax_exp(WaveState<C, RB>& w, f32x4 (&sc)[RB]
 // (then O and the row sum are rescaled); in between, probabilities stay below
 // 2^8, which fp32 sums and bf16 P hold as well as values below 1.
 template <class C, int RB>
-__device__ __forceinline__ void softmax_chunk(WaveState<C, RB>& w, int nvalid, float scale_log2,
-                                              int g) {
-  softmax_max<C, RB>(w, w.s, nvalid, scale_log2, g);
+__device__ __forceinline__ void softmax_chunk(WaveState<C, RB>& w, int nvalid,
+                                              unsigned long long real, float scale_log2, int g) {
+  softmax_max<C, RB>(w, w.s, nvalid, real, scale_log2, g);
   softmax_exp<C, RB>(w, w.s, scale_log2);
 }
 
@@ -242,7 +245,8 @@ __device__ __forceinline__ void store_out(WaveState<C, RB>& w, bf16_t* og, float
 // offsets built in dynamic LDS at the start (all runs of a work item share it).
 // LSE_ONLY: only the row log-sum-exp is wanted (window scoring); V is neither
 // loaded nor multiplied and no output is written.
-template <int D, int WAVES, int RB, int BN, bool DENSE, bool RASTER, bool LSE_ONLY = false>
+template <int D, int WAVES, int RB, int BN, bool DENSE, bool RASTER, bool LSE_ONLY = false,
+          bool PAD = false, bool PLANE = false>
 __global__ void __launch_bounds__(WAVES * 64, (WAVES <= 4 ? 2 : 1))
 attn_bf16_kernel(const AttnParams p) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
@@ -271,24 +275,25 @@ attn_bf16_kernel(const AttnParams p) {
   const int g = lane >> 4;
   const ChunkWalk walk = make_walk<BN, DENSE>(t, p.S);
   // Plane chunks: raster rows by arithmetic (no table); else the table.
-  const bool plane = RASTER && BN == 64 && p.plane_cpt > 0;
+  constexpr bool plane = RASTER && PLANE && BN == 64;
   int lane_row[(C::kBlocks + WAVES - 1) / WAVES];
-  if (plane) {
+  if constexpr (plane) {
     plane_lane_rows<C, WAVES>(p, wave, lane, lane_row);
   } else if (RASTER) {
     for (int e = threadIdx.x; e < walk.run_len; e += C::kThreads) rtab[e] = run_offset_raster(p, e);
     __syncthreads();
   }
   auto dma = [&](int it, char* kdst, char* vdst) __attribute__((always_inline)) {
-    if (RASTER && plane) {
+    if constexpr (plane) {
       const int row0 = walk.at_plane(p, it);
       load_rows_plane<C, WAVES>(kg, row0, lane_row, kdst, wave, lane);
       if (!LSE_ONLY) load_rows_plane<C, WAVES>(vg, row0, lane_row, vdst, wave, lane);
     } else if (RASTER) {
       int base, c0, nv;
       walk.at_raster(p, it, &base, &c0, &nv);
-      load_rows<C, WAVES>(kg, base, nv, kdst, wave, lane, rtab + c0);
-      if (!LSE_ONLY) load_rows<C, WAVES>(vg, base, nv, vdst, wave, lane, rtab + c0);
+      const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
+      load_rows<C, WAVES>(kg, base, nv, kdst, wave, lane, rtab + c0, real);
+      if (!LSE_ONLY) load_rows<C, WAVES>(vg, base, nv, vdst, wave, lane, rtab + c0, real);
     } else {
       int row0, nv;
       walk.at(it, &row0, &nv);
@@ -309,7 +314,7 @@ attn_bf16_kernel(const AttnParams p) {
     __syncthreads();   // ... and every wave's; chunk it-1's buffers are free
     if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
     qk_chunk<C, RB>(w, kcur, l16, g);
-    softmax_chunk<C, RB>(w, nvalid, p.scale_log2, g);
+    softmax_chunk<C, RB>(w, nvalid, chunk_real_keys<PAD && !DENSE>(p, walk, it, lane), p.scale_log2, g);
     if constexpr (!LSE_ONLY) pv_chunk<C, RB>(w, vcur, l16, g);
   };
   for (int it = 0; it < walk.n_chunks; it += 2) {
@@ -425,7 +430,9 @@ __global__ void __launch_bounds__(kF32Threads) attn_f32_kernel(const AttnParams 
 void fill_params(const AttnProblem& pr, int rows_per_item, AttnParams* p) {
   p->q = pr.q; p->k = pr.k; p->v = pr.v; p->out = pr.out;
   p->lse = pr.lse;
-  p->S = pr.g.S;
+  // rows per (batch, head) of the tensors: tile-major tensors of a padded
+  // tile grid hold n_tiles * tau rows
+  p->S = pr.dense || pr.raster ? pr.g.S : pr.g.S_pad;
   p->heads = pr.heads;
   p->dense = pr.dense ? 1 : 0;
   p->scale_log2 = pr.scale * kLog2e;
@@ -434,15 +441,17 @@ void fill_params(const AttnProblem& pr, int rows_per_item, AttnParams* p) {
     p->unit_rows = pr.g.S;
     p->nt = p->nh = p->nw = 1;
     p->tau = pr.g.S;
-    p->H = p->W = p->ct = p->ch = p->cw = 1;
+    p->T = p->H = p->W = p->ct = p->ch = p->cw = 1;
+    p->pad = 0;
     p->plane_cpt = p->plane_cpp = 0;
   } else {
     p->n_units = pr.g.n_tiles;
     p->unit_rows = pr.g.tau;
     p->nt = pr.g.nt; p->nh = pr.g.nh; p->nw = pr.g.nw;
     p->tau = pr.g.tau;
-    p->H = pr.g.H; p->W = pr.g.W;
+    p->T = pr.g.T; p->H = pr.g.H; p->W = pr.g.W;
     p->ct = pr.g.ct; p->ch = pr.g.ch; p->cw = pr.g.cw;
+    p->pad = pr.g.padded;
     set_plane_chunks(p);
     for (int h = 0; h < pr.heads; ++h)
       for (int a = 0; a < 3; ++a) p->omega[h][a] = pr.omega[h][a];
@@ -459,6 +468,34 @@ unsigned raster_table_bytes(const AttnProblem& pr) {
   return (unsigned)run * sizeof(int);
 }
 
+template <int D, int WAVES, int RB, int BN, bool PAD>
+void launch_sparse(const AttnProblem& pr, const AttnParams& p, unsigned grid, unsigned table,
+                   hipStream_t stream) {
+  using C = Bf16Cfg<D, WAVES, RB, BN>;
+  const bool plane = !PAD && BN == 64 && p.plane_cpt > 0;
+  if (pr.lse_only) {
+    if (pr.raster && plane)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, true, false, true>),
+                         dim3(grid), dim3(C::kThreads), 0, stream, p);
+    else if (pr.raster)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, true, PAD>), dim3(grid),
+                         dim3(C::kThreads), table, stream, p);
+    else
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false, true, PAD>), dim3(grid),
+                         dim3(C::kThreads), 0, stream, p);
+  } else {
+    if (pr.raster && plane)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, false, false, true>),
+                         dim3(grid), dim3(C::kThreads), 0, stream, p);
+    else if (pr.raster)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, false, PAD>), dim3(grid),
+                         dim3(C::kThreads), table, stream, p);
+    else
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false, false, PAD>), dim3(grid),
+                         dim3(C::kThreads), 0, stream, p);
+  }
+}
+
 template <int D, int WAVES, int RB, int BN>
 int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
@@ -467,25 +504,18 @@ int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
   const unsigned grid = (unsigned)p.per_xcd * kXcds;
   // plane chunks address K/V by arithmetic and need no offset table
   const unsigned table = (BN == 64 && p.plane_cpt > 0) ? 0 : raster_table_bytes(pr);
-  if (pr.lse_only) {
-    if (pr.dense)
+  if (pr.dense) {
+    if (pr.lse_only)
       hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false, true>), dim3(grid),
                          dim3(C::kThreads), 0, stream, p);
-    else if (pr.raster)
-      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, true>), dim3(grid),
-                         dim3(C::kThreads), table, stream, p);
     else
-      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false, true>), dim3(grid),
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false>), dim3(grid),
                          dim3(C::kThreads), 0, stream, p);
-  } else if (pr.dense)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false>), dim3(grid),
-                       dim3(C::kThreads), 0, stream, p);
-  else if (pr.raster)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true>), dim3(grid),
-                       dim3(C::kThreads), table, stream, p);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false>), dim3(grid),
-                       dim3(C::kThreads), 0, stream, p);
+  } else if (pr.g.padded) {
+    launch_sparse<D, WAVES, RB, BN, true>(pr, p, grid, table, stream);
+  } else {
+    launch_sparse<D, WAVES, RB, BN, false>(pr, p, grid, table, stream);
+  }
   return (int)hipGetLastError();
 }
 

@@ -43,6 +43,8 @@ struct AttnParams {
   int dense;
   int nt, nh, nw, tau;
   int H, W, ct, ch, cw;  // volume and tile, for raster-order addressing
+  int T;
+  int pad;               // the tile grid reaches past the volume (padded tiles)
   // Raster order, key chunks of 64 rows that each lie inside one t-plane of
   // one tile (64 divides c_h * c_w, c_w divides 64, tau a multiple of 64):
   // chunks per tile and per plane. 0 when that does not hold.
@@ -72,7 +74,7 @@ constexpr int kMixedGroup = 32;
 // Host side: plane_cpt / plane_cpp of a sparse problem (needs tau, ch, cw).
 inline void set_plane_chunks(AttnParams* p) {
   const int plane = p->ch * p->cw;
-  if (p->tau % 64 == 0 && plane % 64 == 0 && 64 % p->cw == 0) {
+  if (!p->pad && p->tau % 64 == 0 && plane % 64 == 0 && 64 % p->cw == 0) {
     p->plane_cpt = p->tau / 64;
     p->plane_cpp = plane / 64;
   } else {
@@ -139,6 +141,34 @@ struct Task {
   int qt, qh, qw;       // query tile coordinates (STA)
   KvRuns kv;
 };
+
+// Whether row `local` (tile-major order inside the tile) of tile (qt, qh, qw)
+// is a token of the volume (false for padding positions of a partly padded
+// tile).
+__device__ __forceinline__ bool tile_row_real(const AttnParams& p, int qt, int qh, int qw, int local) {
+  const int plane = p.ch * p.cw;
+  const int lt = local / plane;
+  const int rem = local - lt * plane;
+  const int lh = rem / p.cw;
+  const int lw = rem - lh * p.cw;
+  return qt * p.ct + lt < p.T && qh * p.ch + lh < p.H && qw * p.cw + lw < p.W;
+}
+
+// Whether run r of a walk reaches past the volume (only then can its keys
+// include padding positions).
+__device__ __forceinline__ bool run_padded(const AttnParams& p, const KvRuns& kv, int r) {
+  const int it = r / kv.oh, ih = r - (r / kv.oh) * kv.oh;
+  const int tiles_w = kv.run_len / kv.tau;
+  return (kv.st + it + 1) * p.ct > p.T || (kv.sh + ih + 1) * p.ch > p.H ||
+         (kv.sw + tiles_w) * p.cw > p.W;
+}
+
+// Whether key e (tile-major order within the run) of run r is a token.
+__device__ __forceinline__ bool run_key_real(const AttnParams& p, const KvRuns& kv, int r, int e) {
+  const int it = r / kv.oh, ih = r - (r / kv.oh) * kv.oh;
+  const int tw = e / p.tau;
+  return tile_row_real(p, kv.st + it, kv.sh + ih, kv.sw + tw, e - tw * p.tau);
+}
 
 // Raster token index of row `local` (tile-major order inside the tile) of
 // query tile (qt, qh, qw).
@@ -283,10 +313,13 @@ __device__ __forceinline__ int swz(int row, int c) {
 // Issue this wave's share of the direct-to-LDS loads of one K (or V) chunk:
 // key rows kv_row0 .. kv_row0 + BN - 1 of the head (rows past `nvalid` repeat
 // the last valid row; their scores are masked). Each instruction fills one
-// 1 KB block; WAVES wavefronts share the chunk.
+// 1 KB block; WAVES wavefronts share the chunk. Keys whose bit in `real` is
+// clear are padding positions: they load row kv_row0 instead (the run's first
+// key, always a token) and are masked later.
 template <class C, int WAVES>
 __device__ __forceinline__ void load_rows(const bf16_t* src, int kv_row0, int nvalid, char* buf,
-                                          int wave, int lane, const int* rtab = nullptr) {
+                                          int wave, int lane, const int* rtab = nullptr,
+                                          unsigned long long real = ~0ull) {
   constexpr int kIter = (C::kBlocks + WAVES - 1) / WAVES;
 #pragma unroll
   for (int b = 0; b < kIter; ++b) {
@@ -299,7 +332,8 @@ __device__ __forceinline__ void load_rows(const bf16_t* src, int kv_row0, int nv
     // kv_row0. Raster order: kv_row0 is the run's first raster token and
     // rtab (already offset to the chunk) gives each key's raster offset.
     const int key = min(row, nvalid - 1);
-    const int src_row = rtab ? kv_row0 + rtab[key] : kv_row0 + key;
+    int src_row = rtab ? kv_row0 + rtab[key] : kv_row0 + key;
+    if (!((real >> key) & 1ull)) src_row = kv_row0;
     const long long off = (long long)src_row * (C::kRowBytes / 2) + c * 8;
     __builtin_amdgcn_global_load_lds(src + off, (lds_void*)(buf + blk * 1024), 16, 0, 0);
   }
@@ -365,9 +399,12 @@ __device__ __forceinline__ RowMap<C, RB> map_rows(const AttnParams& p, const Tas
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int r = wave * C::kRowsWave + 16 * rb + l16;
-    rm.ok[rb] = r < t.valid_rows;
-    const int rr = rm.ok[rb] ? r : 0;
-    rm.tok[rb] = RASTER ? tile_row_raster(p, t.qt, t.qh, t.qw, t.local0 + rr) : t.row0 + rr;
+    rm.ok[rb] = r < t.valid_rows &&
+                (!p.pad || tile_row_real(p, t.qt, t.qh, t.qw, t.local0 + r));
+    // rows that do not exist read the unit's first row (a token of every tile,
+    // also of a partly padded one) and are never stored
+    const int local = rm.ok[rb] ? t.local0 + r : 0;
+    rm.tok[rb] = RASTER ? tile_row_raster(p, t.qt, t.qh, t.qw, local) : t.row0 - t.local0 + local;
   }
   return rm;
 }
@@ -406,6 +443,21 @@ struct ChunkWalk {
     *nvalid = min(bn, run_len - *c0);
   }
 };
+
+// Bit k set iff key k (0..63) of chunk `it` is a token of the volume: all
+// ones unless the problem is padded (PAD, a kernel variant of its own so that
+// unpadded launches carry no masking code) and the chunk's run reaches past
+// the volume. One key per lane (64-key chunks), then a wave ballot.
+template <bool PAD>
+__device__ __forceinline__ unsigned long long chunk_real_keys(const AttnParams& p, const ChunkWalk& w,
+                                                               int it, int lane) {
+  if (!PAD) return ~0ull;
+  const int run = it / w.chunks_per_run;
+  if (!run_padded(p, w.kv, run)) return ~0ull;
+  const int e = (it - run * w.chunks_per_run) * w.bn + lane;
+  const bool real = e < w.run_len && run_key_real(p, w.kv, run, e);
+  return __ballot(real);
+}
 
 template <int BN, bool DENSE>
 __device__ __forceinline__ ChunkWalk make_walk(const Task& t, int S) {

@@ -191,9 +191,10 @@ __device__ __forceinline__ void store_rows(const f32x4 (&acc)[RB][C::kDB], bf16_
 // One float per streamed row of a chunk (lse or D) into LDS with a single
 // direct-to-LDS dword load: lane i fills slot i (BN = 64 rows, one wave).
 __device__ __forceinline__ void load_row_values(const float* src, int row0, int nvalid, float* buf,
-                                                int lane, const int* rtab) {
+                                                int lane, const int* rtab, unsigned long long real) {
   const int key = min(lane, nvalid - 1);
-  const int src_row = rtab ? row0 + rtab[key] : row0 + key;
+  int src_row = rtab ? row0 + rtab[key] : row0 + key;
+  if (!((real >> key) & 1ull)) src_row = row0;
   __builtin_amdgcn_global_load_lds(src + src_row, (lds_void*)buf, 4, 0, 0);
 }
 
@@ -201,7 +202,7 @@ __device__ __forceinline__ void load_row_values(const float* src, int row0, int 
 // dq kernel (own rows: queries; streamed: K and V of the window)
 // ---------------------------------------------------------------------------
 
-template <int D, int WAVES, int RB, int BN, bool RASTER>
+template <int D, int WAVES, int RB, int BN, bool RASTER, bool PAD>
 __global__ void __launch_bounds__(WAVES * 64, (WAVES <= 4 ? 2 : 1))
 bwd_dq_kernel(const AttnParams p, const BwdParams b) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
@@ -234,8 +235,9 @@ bwd_dq_kernel(const AttnParams p, const BwdParams b) {
     if (RASTER) {
       int base, c0, nv;
       walk.at_raster(p, it, &base, &c0, &nv);
-      load_rows<C, WAVES>(kg, base, nv, kdst, wave, lane, rtab + c0);
-      load_rows<C, WAVES>(vg, base, nv, vdst, wave, lane, rtab + c0);
+      const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
+      load_rows<C, WAVES>(kg, base, nv, kdst, wave, lane, rtab + c0, real);
+      load_rows<C, WAVES>(vg, base, nv, vdst, wave, lane, rtab + c0, real);
     } else {
       int row0, nv;
       walk.at(it, &row0, &nv);
@@ -269,6 +271,7 @@ bwd_dq_kernel(const AttnParams p, const BwdParams b) {
     wait_vm_all();
     __syncthreads();
     if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
+    const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
     f32x4 s[RB][C::kKT], dp[RB][C::kKT];
     mma_rows<C, RB>(s, kcur, koff, qf);    // S^T[key][row] = K Q^T
     mma_rows<C, RB>(dp, vcur, koff, df);   // dP^T[key][row] = V dO^T
@@ -278,9 +281,10 @@ bwd_dq_kernel(const AttnParams p, const BwdParams b) {
       for (int kt = 0; kt < C::kKT; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float pr = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -lse2[rb]));
-          if (nvalid < C::kBN && 16 * kt + 4 * g + r >= nvalid) pr = 0.f;
-          s[rb][kt][r] = pr * (dp[rb][kt][r] - dl[rb]);   // dS^T
+          const int key = 16 * kt + 4 * g + r;
+          const bool off = (nvalid < C::kBN && key >= nvalid) || !((real >> key) & 1ull);
+          const float pr = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -lse2[rb]));
+          s[rb][kt][r] = off ? 0.f : pr * (dp[rb][kt][r] - dl[rb]);   // dS^T
         }
     bf16x8 wf[RB][C::kKP];
     pack_bf16<C, RB>(wf, s);
@@ -298,7 +302,7 @@ bwd_dq_kernel(const AttnParams p, const BwdParams b) {
 // whose window holds the key tile)
 // ---------------------------------------------------------------------------
 
-template <int D, int WAVES, int RB, int BN, bool RASTER>
+template <int D, int WAVES, int RB, int BN, bool RASTER, bool PAD>
 __global__ void __launch_bounds__(WAVES * 64, (WAVES <= 4 ? 2 : 1))
 bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
@@ -345,11 +349,12 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
     } else {
       walk.at(it, &base, &nv);
     }
-    load_rows<C, WAVES>(qg, base, nv, qdst, wave, lane, tab);
-    load_rows<C, WAVES>(dog, base, nv, odst, wave, lane, tab);
+    const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
+    load_rows<C, WAVES>(qg, base, nv, qdst, wave, lane, tab, real);
+    load_rows<C, WAVES>(dog, base, nv, odst, wave, lane, tab, real);
     if (wave == 0) {
-      load_row_values(lseg, base, nv, ldst, lane, tab);
-      load_row_values(delg, base, nv, ddst, lane, tab);
+      load_row_values(lseg, base, nv, ldst, lane, tab, real);
+      load_row_values(delg, base, nv, ddst, lane, tab, real);
     }
   };
   dma(0, qb0, ob0, lb0, db0);
@@ -378,6 +383,7 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
     wait_vm_all();
     __syncthreads();
     if (it + 1 < walk.n_chunks) dma(it + 1, qnxt, onxt, lnxt, dnxt);
+    const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
     f32x4 s[RB][C::kKT];
     mma_rows<C, RB>(s, qcur, koff, kf);    // S[q][key] = Q K^T
     f32x4 lq[C::kKT], dq_[C::kKT];
@@ -392,9 +398,10 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
       for (int kt = 0; kt < C::kKT; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float pr = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -lq[kt][r] * kLog2e));
-          if (nvalid < C::kBN && 16 * kt + 4 * g + r >= nvalid) pr = 0.f;
-          s[rb][kt][r] = pr;                              // P[q][key]
+          const int qrow = 16 * kt + 4 * g + r;
+          const bool off = (nvalid < C::kBN && qrow >= nvalid) || !((real >> qrow) & 1ull);
+          const float pr = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -lq[kt][r] * kLog2e));
+          s[rb][kt][r] = off ? 0.f : pr;                  // P[q][key]
         }
     bf16x8 wf[RB][C::kKP];
     pack_bf16<C, RB>(wf, s);
@@ -406,7 +413,13 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
 #pragma unroll
       for (int kt = 0; kt < C::kKT; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[rb][kt][r] *= dp[rb][kt][r] - dq_[kt][r];   // dS
+        for (int r = 0; r < 4; ++r) {
+          // a masked row may carry garbage lse / D (padding rows of a tile-major
+          // tensor are never written): select, do not multiply
+          const int qrow = 16 * kt + 4 * g + r;
+          const bool off = (nvalid < C::kBN && qrow >= nvalid) || !((real >> qrow) & 1ull);
+          s[rb][kt][r] = off ? 0.f : s[rb][kt][r] * (dp[rb][kt][r] - dq_[kt][r]);   // dS
+        }
     pack_bf16<C, RB>(wf, s);
     mma_tr<C, RB>(dk, qcur, voff, wf);     // dK^T[d][key] += Q^T dS
   };
@@ -543,7 +556,7 @@ void fill_bwd_params(const BwdProblem& pr, int rows_per_item, AttnParams* p, Bwd
   const AttnProblem& a = pr.attn;
   p->q = a.q; p->k = a.k; p->v = a.v; p->out = a.out;
   p->lse = nullptr;
-  p->S = a.g.S;
+  p->S = a.raster ? a.g.S : a.g.S_pad;
   p->heads = a.heads;
   p->dense = 0;
   p->scale_log2 = a.scale * kLog2e;
@@ -551,7 +564,8 @@ void fill_bwd_params(const BwdProblem& pr, int rows_per_item, AttnParams* p, Bwd
   p->unit_rows = a.g.tau;
   p->nt = a.g.nt; p->nh = a.g.nh; p->nw = a.g.nw;
   p->tau = a.g.tau;
-  p->H = a.g.H; p->W = a.g.W;
+  p->T = a.g.T; p->H = a.g.H; p->W = a.g.W;
+  p->pad = a.g.padded;
   p->ct = a.g.ct; p->ch = a.g.ch; p->cw = a.g.cw;
   set_plane_chunks(p);
   for (int h = 0; h < a.heads; ++h)
@@ -586,6 +600,23 @@ unsigned raster_bytes(const AttnProblem& a, bool keys) {
   return (unsigned)run * sizeof(int);
 }
 
+template <int D, int WAVES, int RB, bool KEYS, bool PAD>
+void launch_pass_kernel(const AttnParams& p, const BwdParams& b, unsigned grid, bool raster,
+                        unsigned lds, hipStream_t stream) {
+  using C = Bf16Cfg<D, WAVES, RB, 64>;
+  if constexpr (KEYS) {
+    if (raster)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, WAVES, RB, 64, true, PAD>), dim3(grid), dim3(C::kThreads), lds, stream, p, b);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, WAVES, RB, 64, false, PAD>), dim3(grid), dim3(C::kThreads), 0, stream, p, b);
+  } else {
+    if (raster)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, WAVES, RB, 64, true, PAD>), dim3(grid), dim3(C::kThreads), lds, stream, p, b);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, WAVES, RB, 64, false, PAD>), dim3(grid), dim3(C::kThreads), 0, stream, p, b);
+  }
+}
+
 template <int D, int WAVES, int RB, bool KEYS>
 int launch_bf16_pass(const BwdProblem& pr, hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, RB, 64>;
@@ -595,17 +626,10 @@ int launch_bf16_pass(const BwdProblem& pr, hipStream_t stream) {
   const unsigned grid = (unsigned)p.per_xcd * kXcds;
   const bool raster = pr.attn.raster;
   const unsigned lds = raster ? raster_bytes(pr.attn, KEYS) : 0;
-  if constexpr (KEYS) {
-    if (raster)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, WAVES, RB, 64, true>), dim3(grid), dim3(C::kThreads), lds, stream, p, b);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, WAVES, RB, 64, false>), dim3(grid), dim3(C::kThreads), 0, stream, p, b);
-  } else {
-    if (raster)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, WAVES, RB, 64, true>), dim3(grid), dim3(C::kThreads), lds, stream, p, b);
-    else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, WAVES, RB, 64, false>), dim3(grid), dim3(C::kThreads), 0, stream, p, b);
-  }
+  if (pr.attn.g.padded)
+    launch_pass_kernel<D, WAVES, RB, KEYS, true>(p, b, grid, raster, lds, stream);
+  else
+    launch_pass_kernel<D, WAVES, RB, KEYS, false>(p, b, grid, raster, lds, stream);
   return (int)hipGetLastError();
 }
 
@@ -638,7 +662,7 @@ int launch_f32_bwd(const BwdProblem& pr, hipStream_t stream) {
 template <typename T, int D>
 int launch_delta(const BwdProblem& pr, hipStream_t stream) {
   const AttnProblem& a = pr.attn;
-  const long long rows = (long long)a.B * a.heads * a.g.S;
+  const long long rows = (long long)a.B * a.heads * (a.raster ? a.g.S : a.g.S_pad);
   const long long chunks = rows * (D / (16 / (int)sizeof(T)));
   const unsigned grid = (unsigned)((chunks + 255) / 256);
   hipLaunchKernelGGL((delta_kernel<T, D>), dim3(grid), dim3(256), 0, stream,

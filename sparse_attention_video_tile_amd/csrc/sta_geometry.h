@@ -38,13 +38,19 @@ STA_HD void window_inverse(int j, int n, int omega, int* lo, int* hi) {
   *lo = a <= 0 ? 0 : a + half;
 }
 
+// A volume the tile does not divide is covered by ceil(extent / c) tiles per
+// axis, as if padded up to whole tiles; positions past the volume are not
+// tokens. Tile-major tensors hold n_tiles * tau rows (S_pad), raster tensors
+// S = T * H * W rows.
 struct Geometry {
   int T, H, W;     // tokens per axis
   int ct, ch, cw;  // tile size in tokens
-  int nt, nh, nw;  // tiles per axis
+  int nt, nh, nw;  // tiles per axis (ceil(extent / c))
   int n_tiles;     // nt * nh * nw
   int tau;         // tokens per tile
-  int S;           // tokens in the volume
+  int S;           // tokens in the volume (rows of a raster tensor)
+  int S_pad;       // n_tiles * tau (rows of a tile-major tensor)
+  int padded;      // S_pad != S
 };
 
 }  // namespace sta

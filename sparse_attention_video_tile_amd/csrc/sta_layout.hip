@@ -47,7 +47,7 @@ struct ReorderParams {
   long long tasks;   // BH * n_tiles: one (head, tile) per wavefront
   int tile_chunks;   // tau * row_chunks: 16-byte chunks in one tile
   int row_chunks;    // 16-byte chunks per token row
-  int S, H, W;
+  int S, S_pad, T, H, W;  // raster rows, tile-major rows, volume
   int ct, ch, cw, nh, nw, n_tiles, tau;
   FastDiv run_div;   // by row_chunks * cw: chunk -> run
   FastDiv ch_div;    // by ch: run -> (lt, lh)
@@ -57,7 +57,10 @@ struct ReorderParams {
 
 // One wavefront moves one tile of one (batch, head). Chunk e of the tile in
 // tile-major order (contiguous) belongs to run e / run_chunks; a run is the
-// cw tokens that share (t, y), contiguous in raster order too.
+// cw tokens that share (t, y), contiguous in raster order too. A tile that
+// reaches past the volume (tile grid padded up to whole tiles) takes a slower
+// loop that checks every row: padded rows are written as zeros in tile-major
+// order and skipped when restoring.
 __global__ void __launch_bounds__(kReorderThreads) reorder_kernel(const ReorderParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -68,11 +71,12 @@ __global__ void __launch_bounds__(kReorderThreads) reorder_kernel(const ReorderP
   const int iw = tile % p.nw;
   const int ih = (tile / p.nw) % p.nh;
   const int it = tile / (p.nw * p.nh);
-  const long long head_chunk = bh * p.S * (long long)p.row_chunks;
+  const long long raster_head = bh * p.S * (long long)p.row_chunks;
+  const long long tiled_head = bh * p.S_pad * (long long)p.row_chunks;
   // Raster chunk offset of the tile's first run, and per-(lt, lh) strides.
   const long long raster0 =
-      head_chunk + (((long long)it * p.ct * p.H + ih * p.ch) * p.W + iw * p.cw) * p.row_chunks;
-  const long long tiled0 = head_chunk + (long long)tile * p.tile_chunks;
+      raster_head + (((long long)it * p.ct * p.H + ih * p.ch) * p.W + iw * p.cw) * p.row_chunks;
+  const long long tiled0 = tiled_head + (long long)tile * p.tile_chunks;
   const long long lt_stride = (long long)p.H * p.W * p.row_chunks;
   const long long lh_stride = (long long)p.W * p.row_chunks;
 
@@ -86,6 +90,23 @@ __global__ void __launch_bounds__(kReorderThreads) reorder_kernel(const ReorderP
 
   const u32x4* __restrict__ src = p.src;
   u32x4* __restrict__ dst = p.dst;
+  if ((it + 1) * p.ct > p.T || (ih + 1) * p.ch > p.H || (iw + 1) * p.cw > p.W) {
+    // edge tile: check each row against the volume
+    for (int e = lane; e < p.tile_chunks; e += 64) {
+      const uint32_t run = p.run_div.div((uint32_t)e);
+      const int c = e - (int)run * p.run_chunks;
+      const uint32_t lt = p.ch_div.div(run);
+      const int lh = (int)run - (int)lt * p.ch;
+      const int lw = c / p.row_chunks;
+      const bool real = it * p.ct + (int)lt < p.T && ih * p.ch + lh < p.H && iw * p.cw + lw < p.W;
+      if (p.to_tiles) {
+        dst[tiled0 + e] = real ? src[raster0 + lt * lt_stride + lh * lh_stride + c] : u32x4{0u, 0u, 0u, 0u};
+      } else if (real) {
+        dst[raster0 + lt * lt_stride + lh * lh_stride + c] = src[tiled0 + e];
+      }
+    }
+    return;
+  }
   int e0 = 0;
   for (; e0 + 64 * kUnroll <= p.tile_chunks; e0 += 64 * kUnroll) {
     u32x4 buf[kUnroll];
@@ -168,7 +189,7 @@ int launch_reorder(const void* src, void* dst, int BH, int row_bytes, const Geom
   p.row_chunks = row_bytes / 16;
   p.tile_chunks = g.tau * p.row_chunks;
   p.run_chunks = p.row_chunks * g.cw;
-  p.S = g.S; p.H = g.H; p.W = g.W;
+  p.S = g.S; p.S_pad = g.S_pad; p.T = g.T; p.H = g.H; p.W = g.W;
   p.ct = g.ct; p.ch = g.ch; p.cw = g.cw; p.nh = g.nh; p.nw = g.nw;
   p.n_tiles = g.n_tiles; p.tau = g.tau;
   p.run_div = FastDiv::make((uint32_t)p.run_chunks);

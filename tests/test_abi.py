@@ -46,8 +46,8 @@ def i3(*v):
 def test_reorder_rejects_bad_arguments(lib):
     t = i3(6, 8, 8)
     assert lib.sta_reorder_tiles(None, FAKE, 1, 1, 128, 30, 48, 80, t, 0, None) == -1
-    assert lib.sta_reorder_tiles(FAKE, FAKE * 4, 1, 1, 128, 31, 48, 80, t, 0, None) == -1
-    assert "does not divide" in binding.last_error()
+    assert lib.sta_reorder_tiles(FAKE, FAKE * 4, 1, 1, 128, 30, 48, 80, i3(0, 8, 8), 0, None) == -1
+    assert "tile" in binding.last_error()
     assert lib.sta_reorder_tiles(FAKE, FAKE * 4, 0, 1, 128, 30, 48, 80, t, 0, None) == -1
     assert lib.sta_reorder_tiles(FAKE, FAKE * 4, 1, 1, 128, 30, 48, 80, t, 7, None) == -1
     assert lib.sta_reorder_tiles(FAKE, FAKE * 4, 1, 1, 4, 30, 48, 80, t, 0, None) == -2
@@ -76,7 +76,8 @@ def test_forward_rejects_bad_arguments(lib):
     assert call(args(win=i3(36, 24, 24))) == -1      # larger than the volume
     assert "window" in binding.last_error()
     assert call(args(win=i3(0, 24, 24))) == -1
-    assert call(args(tile=i3(7, 8, 8))) == -1
+    assert call(args(tile=i3(7, 8, 8))) == -1        # the window is not whole tiles of 7
+    assert call(args(win=i3(42, 24, 24), T=31)) == -1  # 7 tiles on a padded grid of 6
     assert call(args(scale=0.0)) == -1
     assert call(args(scale=float("nan"))) == -1
     assert call(args(scale=float("inf"))) == -1
