@@ -223,3 +223,18 @@ def test_window_recall_rejects_bad_arguments(lib):
     assert call(d=32) == -2
     assert call(ws=FAKE * 2000 + 64) == -1                              # workspace overlaps k
     assert "overlap" in binding.last_error()
+
+
+def test_float32_attention_on_a_padded_grid_is_refused(lib):
+    """Volume 5x6x7 with tile 2x4x4 is covered by a padded grid; float32
+    attention refuses it before any launch, bf16 takes it (not launched here)."""
+    t, w = i3(2, 4, 4), i3(4, 4, 4)
+    rc = lib.sta_forward(FAKE, FAKE * 100, FAKE * 200, FAKE * 300, 1, 1, 64, 5, 6, 7, t, w, 0.1, 1, None)
+    assert rc == -2 and "float32" in binding.last_error()
+    rc = lib.sta_forward_raster(FAKE, FAKE * 100, FAKE * 200, FAKE * 300, 1, 1, 64, 5, 6, 7, t, w, 0.1, 1, None)
+    assert rc == -2
+    a = backward_args(T=5, H=6, W=7, tile=t, win=w, d=64, dt=1)
+    assert call_backward(lib, a) == -2
+    # a window larger than the padded grid is still invalid
+    assert lib.sta_forward(FAKE, FAKE * 100, FAKE * 200, FAKE * 300, 1, 1, 64, 5, 6, 7, t,
+                           i3(8, 4, 4), 0.1, 0, None) == -1
