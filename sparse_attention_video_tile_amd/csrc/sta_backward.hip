@@ -270,11 +270,13 @@ bwd_dq_kernel(const AttnParams p, const BwdParams b) {
     walk.at(it, &row0, &nvalid);
     wait_vm_all();
     __syncthreads();
-    if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
     const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
     f32x4 s[RB][C::kKT], dp[RB][C::kKT];
     mma_rows<C, RB>(s, kcur, koff, qf);    // S^T[key][row] = K Q^T
     mma_rows<C, RB>(dp, vcur, koff, df);   // dP^T[key][row] = V dO^T
+    // next chunk's loads after the row-wise reads (their LDS writes then
+    // land during the VALU work)
+    if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -382,10 +384,10 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
     walk.at(it, &row0, &nvalid);
     wait_vm_all();
     __syncthreads();
-    if (it + 1 < walk.n_chunks) dma(it + 1, qnxt, onxt, lnxt, dnxt);
     const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
     f32x4 s[RB][C::kKT];
     mma_rows<C, RB>(s, qcur, koff, kf);    // S[q][key] = Q K^T
+    if (it + 1 < walk.n_chunks) dma(it + 1, qnxt, onxt, lnxt, dnxt);
     f32x4 lq[C::kKT], dq_[C::kKT];
 #pragma unroll
     for (int kt = 0; kt < C::kKT; ++kt) {
