@@ -80,3 +80,39 @@ def test_full_size_raster_equals_three_call_path(w):
     b = binding.sliding_tile_attention(q, k, v, w.tile, inp.windows, fused=False)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_more_than_2_31_elements_per_tensor():
+    """B = 4, 48 heads at 30x48x80, d = 128: 2.83e9 elements per tensor, past
+    what 32-bit element offsets reach. Rows of the last (batch, head) -- the
+    largest offsets -- and of the first are checked against the oracle; the
+    raster kernel and the tile-major path agree on the last head."""
+    vol, tile, win = (30, 48, 80), (6, 8, 8), (18, 24, 24)
+    B, heads, d = 4, 48, 128
+    S = vol[0] * vol[1] * vol[2]
+    assert B * heads * S * d > 2 ** 31
+    print(f"[case] large: B={B} heads={heads} S={S} d={d}", flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(123)
+    shape = (B, heads) + vol + (d,)
+    q, k, v = (torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+               for _ in range(3))
+    out = binding.sta_forward_raster(q, k, v, tile, [win])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    n = oracle.tile_grid(vol, tile)
+    scale = default_scale(d)
+    for b, h in ((0, 0), (B - 1, heads - 1)):
+        qh, kh, vh = (x[b:b + 1, h:h + 1].float().cpu().numpy() for x in (q, k, v))
+        tiles = [0, n[0] * n[1] * n[2] - 1, int(rng.integers(0, n[0] * n[1] * n[2]))]
+        rows = np.concatenate([oracle.tile_tokens(vol, tile, t)[rng.choice(384, 8, replace=False)] for t in tiles])
+        ref = oracle.sta_attention_rows(qh, kh, vh, tile, win, scale, 0, 0, rows)
+        got = out[b, h].float().cpu().numpy().reshape(-1, d)[rows]
+        assert_close(got, ref, "bf16", f"large b={b} h={h}")
+    # the tile-major path on the last (batch, head) alone gives the same rows
+    last = [x[B - 1:B, heads - 1:heads].contiguous() for x in (q, k, v)]
+    ref_last = binding.sliding_tile_attention(*last, tile, [win], fused=False)
+    torch.cuda.synchronize()
+    assert torch.equal(ref_last[0, 0], out[B - 1, heads - 1])
+    del q, k, v, out
+    torch.cuda.empty_cache()
