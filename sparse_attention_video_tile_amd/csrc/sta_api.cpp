@@ -230,6 +230,15 @@ int check_raster_runs(const sta::Geometry& g, int heads, const uint16_t (*omega)
                 "raster order: a window run has %lld keys (limit %d); reorder to tile-major order "
                 "and use the tile-major entry point",
                 run, sta::kMaxRasterRun);
+  // The kernels address the keys of a run as 32-bit byte offsets from its
+  // first key: one tile-row of frames, c_t * H * W tokens of at most 256
+  // bytes, must stay below 2 GB.
+  const long long span = (long long)g.ct * g.H * g.W * 256;
+  if (span >= (1LL << 31))
+    return fail(STA_ERR_UNSUPPORTED,
+                "raster order: c_t * H * W = %lld tokens exceeds the raster addressing range; "
+                "reorder to tile-major order and use the tile-major entry point",
+                (long long)g.ct * g.H * g.W);
   return STA_OK;
 }
 

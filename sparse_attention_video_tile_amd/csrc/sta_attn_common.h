@@ -291,6 +291,26 @@ struct Bf16Cfg {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
+// LDS DMA of BYTES (4 or 16) per lane: base + voff (bytes, this lane's) into
+// LDS at dst + BYTES * lane. base and dst are wave-uniform; callers pass the
+// base row through readfirstlane so that the compiler knows it (else it loops
+// over the lanes to build the resource). The load goes through a buffer
+// resource based at the chunk, so the per-lane offsets stay small (below
+// 2 GB, which the host checks) whatever the tensor size. The buffer form, not
+// the global one: with a global LDS-DMA load in a loop the compiler can no
+// longer count LDS reads in order and waits for all of them at every use,
+// which defeats issuing operand reads ahead.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void* base, int voff, void* dst) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+  static_assert(BYTES == 4 || BYTES == 16, "LDS DMA of 4 or 16 bytes per lane");
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, voff, 0, 0, 0);
+}
+
 // Physical byte offset of 16-byte chunk `c` of key row `row` in a K/V buffer.
 // Chunks are XOR-swizzled by the row so that the operand fetches of the MFMA
 // loops hit distinct LDS banks: with 256-byte rows every row starts at bank 0
@@ -332,10 +352,10 @@ __device__ __forceinline__ void load_rows(const bf16_t* src, int kv_row0, int nv
     // kv_row0. Raster order: kv_row0 is the run's first raster token and
     // rtab (already offset to the chunk) gives each key's raster offset.
     const int key = min(row, nvalid - 1);
-    int src_row = rtab ? kv_row0 + rtab[key] : kv_row0 + key;
-    if (!((real >> key) & 1ull)) src_row = kv_row0;
-    const long long off = (long long)src_row * (C::kRowBytes / 2) + c * 8;
-    __builtin_amdgcn_global_load_lds(src + off, (lds_void*)(buf + blk * 1024), 16, 0, 0);
+    int rel = rtab ? rtab[key] : key;
+    if (!((real >> key) & 1ull)) rel = 0;
+    lds_dma<16>(src + (long long)__builtin_amdgcn_readfirstlane(kv_row0) * (C::kRowBytes / 2),
+                rel * C::kRowBytes + c * 16, buf + blk * 1024);
   }
 }
 
@@ -369,8 +389,8 @@ __device__ __forceinline__ void load_rows_plane(const bf16_t* src, int chunk_row
     const int row = blk * C::kRowsPerBlock + lane / C::kCPR;
     const int pos = lane % C::kCPR;
     const int c = pos ^ ((swz<C::kCPR>(row, 0) >> 4) & (C::kCPR - 1));
-    const long long off = (long long)(chunk_row0 + lane_row[b]) * (C::kRowBytes / 2) + c * 8;
-    __builtin_amdgcn_global_load_lds(src + off, (lds_void*)(buf + blk * 1024), 16, 0, 0);
+    lds_dma<16>(src + (long long)__builtin_amdgcn_readfirstlane(chunk_row0) * (C::kRowBytes / 2),
+                lane_row[b] * C::kRowBytes + c * 16, buf + blk * 1024);
   }
 }
 

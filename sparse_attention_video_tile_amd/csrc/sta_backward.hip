@@ -193,9 +193,9 @@ __device__ __forceinline__ void store_rows(const f32x4 (&acc)[RB][C::kDB], bf16_
 __device__ __forceinline__ void load_row_values(const float* src, int row0, int nvalid, float* buf,
                                                 int lane, const int* rtab, unsigned long long real) {
   const int key = min(lane, nvalid - 1);
-  int src_row = rtab ? row0 + rtab[key] : row0 + key;
-  if (!((real >> key) & 1ull)) src_row = row0;
-  __builtin_amdgcn_global_load_lds(src + src_row, (lds_void*)buf, 4, 0, 0);
+  int rel = rtab ? rtab[key] : key;
+  if (!((real >> key) & 1ull)) rel = 0;
+  lds_dma<4>(src + __builtin_amdgcn_readfirstlane(row0), rel * 4, buf);
 }
 
 // ---------------------------------------------------------------------------
