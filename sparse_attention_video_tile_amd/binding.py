@@ -357,9 +357,13 @@ def raster_run_fits(tile: Sequence[int], window, heads: int, volume: Optional[Se
                     backward: bool = False) -> bool:
     """Whether every window run (omega_w * tau keys) -- and, for the backward
     (which needs the volume), every transposed run -- is within what the
-    raster-order kernels accept."""
+    raster-order kernels accept, and (when the volume is given) whether one
+    tile-row of frames, c_t * H * W tokens, is within their 32-bit byte
+    addressing of a run."""
     ws = _windows_per_head(window, heads)
     tau = int(tile[0]) * int(tile[1]) * int(tile[2])
+    if volume is not None and int(tile[0]) * int(volume[1]) * int(volume[2]) * 256 >= 2 ** 31:
+        return False
     for h in range(heads):
         om = ws[3 * h + 2] // int(tile[2])
         if om * tau > STA_MAX_RASTER_RUN:
@@ -514,7 +518,7 @@ def sliding_tile_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ti
     to raster order. Both give the same values."""
     if q.dim() != 6:
         raise ValueError("q, k, v must be (B, heads, T, H, W, d)")
-    if fused and raster_run_fits(tile, window, q.shape[1]):
+    if fused and raster_run_fits(tile, window, q.shape[1], q.shape[2:5]):
         return sta_forward_raster(q, k, v, tile, window, scale)
     volume = tuple(q.shape[2:5])
     qt, kt, vt = (sta_reorder_tiles(x, tile) for x in (q, k, v))

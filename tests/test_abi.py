@@ -196,6 +196,18 @@ def test_raster_run_fits_matches_library_limit():
     assert not binding.raster_run_fits((1, 1, 4096), [(1, 1, 8192)], 1, (1, 1, 16384), backward=True)
 
 
+def test_raster_frames_beyond_32bit_run_addressing_are_refused(lib):
+    """One tile-row of frames (c_t * H * W tokens of up to 256 bytes) must fit
+    the kernels' 32-bit offsets within a run: 2904 x 2904 frames do not, and
+    the fused helper routes such volumes to the tile-major path."""
+    t, w = i3(1, 8, 8), i3(1, 8, 8)
+    big = [(k + 1) << 40 for k in range(4)]
+    rc = lib.sta_forward_raster(big[0], big[1], big[2], big[3], 1, 1, 64, 1, 2904, 2904, t, w, 0.1, 0, None)
+    assert rc == -2 and "addressing" in binding.last_error()
+    assert not binding.raster_run_fits((1, 8, 8), [(1, 8, 8)], 1, (1, 2904, 2904))
+    assert binding.raster_run_fits((1, 8, 8), [(1, 8, 8)], 1, (1, 2896, 2896))
+
+
 def test_backward_raster_limit_counts_transposed_runs(lib):
     a = backward_args(order=1, T=1, H=1, W=16384, tile=i3(1, 1, 4096), win=i3(1, 1, 8192), d=64)
     assert call_backward(lib, a) == -2
