@@ -173,7 +173,10 @@ int sta_forward(const void* q, const void* k, const void* v, void* out, int B, i
  *   out:     device, same shape, raster order, written. No overlap with inputs.
  * Other arguments and rules as sta_forward. Additionally each head's window run
  * omega_w * tau (keys that are consecutive in tile-major order) must be at most
- * 8192 keys, else STA_ERR_UNSUPPORTED (reorder and call sta_forward instead).
+ * 8192 keys, and one tile-row of frames, c_t * H * W tokens, must span less
+ * than 2^31 bytes at 256 bytes a token (the kernels address a run's keys with
+ * 32-bit offsets), else STA_ERR_UNSUPPORTED (reorder and call sta_forward
+ * instead).
  */
 int sta_forward_raster(const void* q, const void* k, const void* v, void* out, int B, int heads,
                        int head_dim, int T, int H, int W, const int* tile, const int* window,
@@ -215,7 +218,8 @@ int sta_forward_lse(const void* q, const void* k, const void* v, void* out, floa
  * rounded to bfloat16. Each gradient element is computed by one work item
  * (no atomics): results are deterministic. With order = STA_RASTER the
  * window runs and their transposes (the longest interval of query tiles
- * along w times tau) must be at most 8192 tokens, else STA_ERR_UNSUPPORTED.
+ * along w times tau) must be at most 8192 tokens and c_t * H * W tokens must
+ * span less than 2^31 bytes at 256 bytes a token, else STA_ERR_UNSUPPORTED.
  * Other arguments and rules as sta_forward.
  */
 int sta_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
