@@ -99,6 +99,9 @@ __device__ __forceinline__ void softmax_max(WaveState<C, RB>& w, f32x4 (&sc)[RB]
           for (int rb = 0; rb < RB; ++rb) sc[rb][kt][r] = -INFINITY;
       }
   }
+  // The test needs no cross-lane reduction: a row's max exceeds m + 8 exactly
+  // when the max of one of its four lanes does, and the decision is taken for
+  // the whole wave anyway. Only when it fires is each row's max gathered.
   float mx[RB];
   bool grow = false;
 #pragma unroll
@@ -107,14 +110,14 @@ __device__ __forceinline__ void softmax_max(WaveState<C, RB>& w, f32x4 (&sc)[RB]
 #pragma unroll
     for (int kt = 0; kt < C::kKT; ++kt)
       a = fmaxf(a, fmaxf(fmaxf(sc[rb][kt][0], sc[rb][kt][1]), fmaxf(sc[rb][kt][2], sc[rb][kt][3])));
-    mx[rb] = row_max4(a) * scale_log2;
+    mx[rb] = a * scale_log2;
     grow |= mx[rb] > w.m[rb] + 8.0f;
   }
   if (__any(grow)) {
     keep_branch();
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float m_new = fmaxf(w.m[rb], mx[rb]);
+      const float m_new = fmaxf(w.m[rb], row_max4(mx[rb]));
       const float alpha = __builtin_amdgcn_exp2f(w.m[rb] - m_new);
       w.m[rb] = m_new;
       w.lsum[rb] *= alpha;
