@@ -259,11 +259,15 @@ __device__ __forceinline__ void store_out(WaveState<C, RB>& w, bf16_t* og, float
 
 // Flash loop: every wave runs QK^T, softmax and PV of a chunk in turn; the
 // next chunk's K and V stream into the other LDS buffer meanwhile (issued
-// after QK^T).
+// after QK^T). In both MFMA phases the operand reads run two fragment steps
+// ahead of their MFMAs.
 // RASTER: q, k, v, out are in raster token order (the permutation to and from
 // tile-major order is folded into the addressing): query rows map through
 // tile_row_raster, and every key of a window run through a table of raster
-// offsets built in dynamic LDS at the start (all runs of a work item share it).
+// offsets built in dynamic LDS at the start (all runs of a work item share
+// it). PLANE (raster, unpadded, tiles whose c_h * c_w plane holds whole
+// 64-key chunks): each chunk is BN / c_w rows of c_w consecutive raster
+// tokens, addressed by arithmetic, and no table is needed.
 // LSE_ONLY: only the row log-sum-exp is wanted (window scoring); V is neither
 // loaded nor multiplied and no output is written.
 template <int D, int WAVES, int RB, int BN, bool DENSE, bool RASTER, bool LSE_ONLY = false,
