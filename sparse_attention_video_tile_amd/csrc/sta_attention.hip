@@ -344,8 +344,10 @@ attn_bf16_kernel(const AttnParams p) {
     // (measured: 2 % faster than issuing right after the barrier).
     if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
     softmax_chunk<C, RB>(w, nvalid, chunk_real_keys<PAD && !DENSE>(p, walk, it, lane), p.scale_log2, g);
+    // No fence before PV: the scheduler starts the PV MFMAs of the first row
+    // block while the exponentials of the others are still being issued (the
+    // same wave issuing both is what lets them run side by side).
     if constexpr (!LSE_ONLY) {
-      __builtin_amdgcn_sched_barrier(0);
       pv_chunk<C, RB>(w, vcur, l16, g);
       sched_reads_ahead<RB, C::kKP * C::kDB, 2, kReadAhead>();
     }
