@@ -83,6 +83,22 @@ __device__ __forceinline__ void qk_chunk(WaveState<C, RB>& w, const char* kbuf, 
   qk_into<C, RB>(w, w.s, kbuf, l16, g);
 }
 
+// Moves each row's reference max to the larger of it and the row's maximum
+// (mx: this lane's maximum in log2 units; the row's four lanes are combined
+// here) and rescales O and the row sum to match.
+template <class C, int RB>
+__device__ __forceinline__ void rescale_to(WaveState<C, RB>& w, const float (&mx)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float m_new = fmaxf(w.m[rb], row_max4(mx[rb]));
+    const float alpha = __builtin_amdgcn_exp2f(w.m[rb] - m_new);
+    w.m[rb] = m_new;
+    w.lsum[rb] *= alpha;
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) w.o[rb][db] *= alpha;
+  }
+}
+
 template <class C, int RB>
 __device__ __forceinline__ void softmax_max(WaveState<C, RB>& w, f32x4 (&sc)[RB][C::kKT],
                                             int nvalid, unsigned long long real, float scale_log2,
@@ -115,15 +131,7 @@ __device__ __forceinline__ void softmax_max(WaveState<C, RB>& w, f32x4 (&sc)[RB]
   }
   if (__any(grow)) {
     keep_branch();
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float m_new = fmaxf(w.m[rb], row_max4(mx[rb]));
-      const float alpha = __builtin_amdgcn_exp2f(w.m[rb] - m_new);
-      w.m[rb] = m_new;
-      w.lsum[rb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::kDB; ++db) w.o[rb][db] *= alpha;
-    }
+    rescale_to<C, RB>(w, mx);
   }
 }
 
@@ -214,6 +222,85 @@ __device__ __forceinline__ void sched_reads_ahead() {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Chunks with every key real: the softmax during QK^T
+// ---------------------------------------------------------------------------
+// A wave overlaps VALU work only with its own MFMAs, so the probabilities of
+// score tile kt (and their row sums) are issued between the QK^T MFMAs of
+// tile kt + 1, against the reference max m as it stands. No chunk maximum is
+// taken: every probability is at most its lane's sum over the chunk, so a
+// lane sum within 2^8 keeps every probability within 2^8, the same bound the
+// lazy rescale keeps. A larger (or infinite) sum, which the first chunk
+// always gives (m = -inf), sends the chunk down a rare branch that computes
+// its scores again from LDS, moves m to the exact row maximum, rescales O and
+// the row sums, and redoes the probabilities.
+
+// S^T of score tile kt (keys 16*kt ..) for every row block.
+template <class C, int RB>
+__device__ __forceinline__ void qk_tile(WaveState<C, RB>& w, int kt, const char* kbuf) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) w.s[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int dk = 0; dk < C::kDK; ++dk) {
+    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbuf + w.koff[dk] + 16 * kt * C::kRowBytes);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      w.s[rb][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, w.qf[rb][dk], w.s[rb][kt], 0, 0, 0);
+  }
+}
+
+// Probabilities of score tile kt against the reference max, rounded to bf16
+// into their slots of the PV operand (tile kt is half kt % 2 of key step kt / 2).
+template <class C, int RB>
+__device__ __forceinline__ void exp_tile(WaveState<C, RB>& w, int kt, float scale_log2) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float e[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(w.s[rb][kt][r], scale_log2, -w.m[rb]));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w.pf[rb][kt / 2][4 * (kt % 2) + r] = static_cast<bf16_t>(e[r]);
+  }
+}
+
+// Lane sums of the chunk's bf16 probabilities (the values that multiply V).
+template <class C, int RB>
+__device__ __forceinline__ void chunk_sums(const WaveState<C, RB>& w, float (&lc)[RB]) {
+  const bf16x2 ones = {static_cast<bf16_t>(1.0f), static_cast<bf16_t>(1.0f)};
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float ls = 0.f;
+#pragma unroll
+    for (int kp = 0; kp < C::kKP; ++kp)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {w.pf[rb][kp][2 * e], w.pf[rb][kp][2 * e + 1]};
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);
+      }
+    lc[rb] = ls;
+  }
+}
+
+// Issue order of the QK^T phase: operand reads two steps ahead; from tile 1
+// on, two VALU instructions (the previous tile's probabilities and sums)
+// after each MFMA. Measured on the headline shape: two per MFMA 2-2.5 %
+// faster than the plain order, three or four per MFMA slower.
+template <int RB, int KT, int DK>
+__device__ __forceinline__ void sched_qk_softmax() {
+  constexpr int steps = KT * DK;
+#pragma unroll
+  for (int st = 0; st < kReadAhead && st < steps; ++st) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+  for (int st = 0; st < steps; ++st) {
+    if (st + kReadAhead < steps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int m = 0; m < RB; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (st >= DK) __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);   // VALU and transcendental
+    }
+  }
+}
+
 template <class C, int RB>
 __device__ __forceinline__ void load_q_init(WaveState<C, RB>& w, const bf16_t* qg,
                                             const RowMap<C, RB>& rm, int l16, int g) {
@@ -270,8 +357,11 @@ __device__ __forceinline__ void store_out(WaveState<C, RB>& w, bf16_t* og, float
 // tokens, addressed by arithmetic, and no table is needed.
 // LSE_ONLY: only the row log-sum-exp is wanted (window scoring); V is neither
 // loaded nor multiplied and no output is written.
+// FULL: every chunk of every work item has BN real keys (no ragged run end,
+// no padding): only the spread-out softmax is compiled in; otherwise only the
+// masked path (two paths in one kernel would not fit the register file).
 template <int D, int WAVES, int RB, int BN, bool DENSE, bool RASTER, bool LSE_ONLY = false,
-          bool PAD = false, bool PLANE = false>
+          bool PAD = false, bool PLANE = false, bool FULL = false>
 __global__ void __launch_bounds__(WAVES * 64, (WAVES <= 4 ? 2 : 1))
 attn_bf16_kernel(const AttnParams p) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
@@ -334,22 +424,72 @@ attn_bf16_kernel(const AttnParams p) {
                         __attribute__((always_inline)) {
     int row0, nvalid;
     walk.at(it, &row0, &nvalid);
+    const unsigned long long real = chunk_real_keys<PAD && !DENSE>(p, walk, it, lane);
     wait_vm_all();     // this wave's loads of chunk `it` have landed in LDS
     __syncthreads();   // ... and every wave's; chunk it-1's buffers are free
-    qk_chunk<C, RB>(w, kcur, l16, g);
-    sched_reads_ahead<RB, C::kKT * C::kDK, 1, kReadAhead>();
-    __builtin_amdgcn_sched_barrier(0);
-    // The next chunk's loads go out after QK^T, so their LDS writes land
-    // during the softmax (few LDS reads) rather than beside the K reads
-    // (measured: 2 % faster than issuing right after the barrier).
-    if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
-    softmax_chunk<C, RB>(w, nvalid, chunk_real_keys<PAD && !DENSE>(p, walk, it, lane), p.scale_log2, g);
-    // No fence before PV: the scheduler starts the PV MFMAs of the first row
-    // block while the exponentials of the others are still being issued (the
-    // same wave issuing both is what lets them run side by side).
-    if constexpr (!LSE_ONLY) {
-      pv_chunk<C, RB>(w, vcur, l16, g);
-      sched_reads_ahead<RB, C::kKP * C::kDB, 2, kReadAhead>();
+    if constexpr (FULL) {
+#pragma unroll
+      for (int kt = 0; kt < C::kKT; ++kt) {
+        qk_tile<C, RB>(w, kt, kcur);
+        if (kt > 0) exp_tile<C, RB>(w, kt - 1, p.scale_log2);
+      }
+      exp_tile<C, RB>(w, C::kKT - 1, p.scale_log2);
+      float lc[RB];
+      chunk_sums<C, RB>(w, lc);
+      // Keep the probabilities and sums here, beside the MFMAs: the compiler
+      // would otherwise move them past the branch of the loads below.
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int kp = 0; kp < C::kKP; ++kp) asm volatile("" : "+v"(w.pf[rb][kp]));
+        asm volatile("" : "+v"(lc[rb]));
+      }
+      sched_qk_softmax<RB, C::kKT, C::kDK>();
+      __builtin_amdgcn_sched_barrier(0);
+      if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
+      bool grow = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) grow |= !(lc[rb] <= 256.0f);   // also an infinite sum
+      if (__any(grow)) {
+        keep_branch();
+        qk_chunk<C, RB>(w, kcur, l16, g);
+        float mx[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          float a = -INFINITY;
+#pragma unroll
+          for (int kt = 0; kt < C::kKT; ++kt)
+            a = fmaxf(a, fmaxf(fmaxf(w.s[rb][kt][0], w.s[rb][kt][1]), fmaxf(w.s[rb][kt][2], w.s[rb][kt][3])));
+          mx[rb] = a * p.scale_log2;
+        }
+        rescale_to<C, RB>(w, mx);
+#pragma unroll
+        for (int kt = 0; kt < C::kKT; ++kt) exp_tile<C, RB>(w, kt, p.scale_log2);
+        chunk_sums<C, RB>(w, lc);
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) w.lsum[rb] += lc[rb];
+      if constexpr (!LSE_ONLY) {
+        pv_chunk<C, RB>(w, vcur, l16, g);
+        sched_reads_ahead<RB, C::kKP * C::kDB, 2, kReadAhead>();
+      }
+    } else {
+      // Chunks that may hold masked keys (a ragged run end, padding positions).
+      qk_chunk<C, RB>(w, kcur, l16, g);
+      sched_reads_ahead<RB, C::kKT * C::kDK, 1, kReadAhead>();
+      __builtin_amdgcn_sched_barrier(0);
+      // The next chunk's loads go out after QK^T, so their LDS writes land
+      // during the softmax (few LDS reads) rather than beside the K reads
+      // (measured: 2 % faster than issuing right after the barrier).
+      if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
+      softmax_chunk<C, RB>(w, nvalid, real, p.scale_log2, g);
+      // No fence before PV: the scheduler starts the PV MFMAs of the first
+      // row block while the exponentials of the others are still being
+      // issued (the same wave issuing both is what lets them run side by side).
+      if constexpr (!LSE_ONLY) {
+        pv_chunk<C, RB>(w, vcur, l16, g);
+        sched_reads_ahead<RB, C::kKP * C::kDB, 2, kReadAhead>();
+      }
     }
   };
   for (int it = 0; it < walk.n_chunks; it += 2) {
@@ -505,32 +645,50 @@ unsigned raster_table_bytes(const AttnProblem& pr) {
   return (unsigned)run * sizeof(int);
 }
 
-template <int D, int WAVES, int RB, int BN, bool PAD>
+// FULL implies !PAD; plane chunks imply FULL (whole 64-key chunks per tile).
+template <int D, int WAVES, int RB, int BN, bool PAD, bool FULL>
 void launch_sparse(const AttnProblem& pr, const AttnParams& p, unsigned grid, unsigned table,
                    hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
-  const bool plane = !PAD && BN == 64 && p.plane_cpt > 0;
+  const bool plane = FULL && BN == 64 && p.plane_cpt > 0;
   if (pr.lse_only) {
-    if (pr.raster && plane)
-      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, true, false, true>),
-                         dim3(grid), dim3(C::kThreads), 0, stream, p);
-    else if (pr.raster)
-      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, true, PAD>), dim3(grid),
-                         dim3(C::kThreads), table, stream, p);
+    if constexpr (FULL) {
+      if (pr.raster && plane) {
+        hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, true, false, true, true>),
+                           dim3(grid), dim3(C::kThreads), 0, stream, p);
+        return;
+      }
+    }
+    if (pr.raster)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, true, PAD, false, FULL>),
+                         dim3(grid), dim3(C::kThreads), table, stream, p);
     else
-      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false, true, PAD>), dim3(grid),
-                         dim3(C::kThreads), 0, stream, p);
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false, true, PAD, false, FULL>),
+                         dim3(grid), dim3(C::kThreads), 0, stream, p);
   } else {
-    if (pr.raster && plane)
-      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, false, false, true>),
-                         dim3(grid), dim3(C::kThreads), 0, stream, p);
-    else if (pr.raster)
-      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, false, PAD>), dim3(grid),
-                         dim3(C::kThreads), table, stream, p);
+    if constexpr (FULL) {
+      if (pr.raster && plane) {
+        hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, false, false, true, true>),
+                           dim3(grid), dim3(C::kThreads), 0, stream, p);
+        return;
+      }
+    }
+    if (pr.raster)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, false, PAD, false, FULL>),
+                         dim3(grid), dim3(C::kThreads), table, stream, p);
     else
-      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false, false, PAD>), dim3(grid),
-                         dim3(C::kThreads), 0, stream, p);
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false, false, PAD, false, FULL>),
+                         dim3(grid), dim3(C::kThreads), 0, stream, p);
   }
+}
+
+// Whether every chunk of every work item holds BN keys that are all tokens.
+bool chunks_full(const AttnProblem& pr, int bn) {
+  if (pr.dense) return pr.g.S % bn == 0;
+  if (pr.g.padded) return false;
+  for (int h = 0; h < pr.heads; ++h)
+    if ((pr.omega[h][2] * pr.g.tau) % bn != 0) return false;
+  return true;
 }
 
 template <int D, int WAVES, int RB, int BN>
@@ -540,18 +698,27 @@ int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
   fill_params(pr, C::kRows, &p);
   const unsigned grid = (unsigned)p.per_xcd * kXcds;
   // plane chunks address K/V by arithmetic and need no offset table
-  const unsigned table = (BN == 64 && p.plane_cpt > 0) ? 0 : raster_table_bytes(pr);
+  const bool full = chunks_full(pr, BN);
+  const unsigned table = (full && BN == 64 && p.plane_cpt > 0) ? 0 : raster_table_bytes(pr);
   if (pr.dense) {
-    if (pr.lse_only)
+    if (pr.lse_only && full)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false, true, false, false, true>),
+                         dim3(grid), dim3(C::kThreads), 0, stream, p);
+    else if (pr.lse_only)
       hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false, true>), dim3(grid),
                          dim3(C::kThreads), 0, stream, p);
+    else if (full)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false, false, false, false, true>),
+                         dim3(grid), dim3(C::kThreads), 0, stream, p);
     else
       hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false>), dim3(grid),
                          dim3(C::kThreads), 0, stream, p);
   } else if (pr.g.padded) {
-    launch_sparse<D, WAVES, RB, BN, true>(pr, p, grid, table, stream);
+    launch_sparse<D, WAVES, RB, BN, true, false>(pr, p, grid, table, stream);
+  } else if (full) {
+    launch_sparse<D, WAVES, RB, BN, false, true>(pr, p, grid, table, stream);
   } else {
-    launch_sparse<D, WAVES, RB, BN, false>(pr, p, grid, table, stream);
+    launch_sparse<D, WAVES, RB, BN, false, false>(pr, p, grid, table, stream);
   }
   return (int)hipGetLastError();
 }

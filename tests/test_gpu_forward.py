@@ -172,6 +172,57 @@ def test_large_logits_are_stable():
     assert_close(got, ref, "bf16", w.name)
 
 
+def _tile_grid(volume, tile):
+    """Tile coordinates (t, h, w) of every raster token, each (T, H, W)."""
+    t, h, w = np.meshgrid(*(np.arange(n) // c for n, c in zip(volume, tile)), indexing="ij")
+    return t, h, w
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["raster", "tile_major"])
+def test_key_scales_jumping_between_tiles(fused):
+    """Key magnitudes that change by up to 13x from tile to tile: scores jump
+    by orders of magnitude (in log2 units, far past the lazy bound of 8) in the
+    middle of every window walk, in both directions. Every chunk is full, so
+    the walk takes the path whose reference max moves only when a lane's
+    chunk sum exceeds 2^8."""
+    w = workloads.small_case((12, 16, 16), (4, 4, 4), [(8, 8, 8), (12, 16, 16)], seed=17,
+                             name="key_scale_jumps")
+    print(f"[case] forward {w.name} fused={fused}", flush=True)
+    inp = workloads.make_inputs(w)
+    t, h, x = _tile_grid(w.volume, w.tile)
+    factor = 1.0 + 3.0 * ((t * 7 + h * 3 + x) % 5)
+    inp.k = workloads.round_to_bf16(inp.k * factor[None, None, :, :, :, None])
+    got = run_sta(inp, fused=fused)
+    ref = oracle.sta_attention(inp.q, inp.k, inp.v, w.tile, inp.windows, default_scale(w.head_dim))
+    assert np.isfinite(got).all()
+    assert_close(got, ref, "bf16", w.name)
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["raster", "tile_major"])
+def test_many_moderate_scores_move_the_reference_max(fused):
+    """Half the key tiles score about 5 (log2 units) above the others: a
+    chunk of them gives probabilities near 2^5 against a max set by the low
+    tiles, far below the single-probability bound 2^8, but lane sums of 16
+    such probabilities pass 2^8, so the rescale must be triggered by the sum."""
+    d = 128
+    w = workloads.small_case((8, 16, 16), (4, 4, 4), [(8, 8, 12)], head_dim=d, seed=23,
+                             name="moderate_scores")
+    print(f"[case] forward {w.name} fused={fused}", flush=True)
+    inp = workloads.make_inputs(w)
+    scale = default_scale(d)
+    alpha = 5.0 / (scale * math.log2(math.e))
+    e0 = np.zeros(d, dtype=np.float32)
+    e0[0] = 1.0
+    t, h, x = _tile_grid(w.volume, w.tile)
+    high = ((t + h + x) % 2).astype(np.float32)
+    inp.q = workloads.round_to_bf16(alpha * e0 + 0.05 * inp.q)
+    inp.k = workloads.round_to_bf16(high[None, None, :, :, :, None] * e0 + 0.05 * inp.k)
+    got = run_sta(inp, scale, fused=fused)
+    ref = oracle.sta_attention(inp.q, inp.k, inp.v, w.tile, inp.windows, scale)
+    assert np.isfinite(got).all()
+    assert_close(got, ref, "bf16", w.name)
+
+
 def test_invalid_inputs_raise_before_launch():
     q = torch.zeros((1, 1, 384, 128), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
