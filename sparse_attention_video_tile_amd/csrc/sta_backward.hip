@@ -198,11 +198,29 @@ __device__ __forceinline__ void load_row_values(const float* src, int row0, int 
   lds_dma<4>(src + __builtin_amdgcn_readfirstlane(row0), rel * 4, buf);
 }
 
+// Operand reads of an MFMA phase issued AHEAD steps before the MFMAs that use
+// them (each step: DS reads, then RB MFMAs); VALU work from an earlier phase
+// may fill VPM instructions after each MFMA.
+template <int RB, int STEPS, int DS, int AHEAD, int VPM>
+__device__ __forceinline__ void sched_phase() {
+#pragma unroll
+  for (int st = 0; st < AHEAD && st < STEPS; ++st) __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    if (st + AHEAD < STEPS) __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
+#pragma unroll
+    for (int m = 0; m < RB; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (VPM > 0) __builtin_amdgcn_sched_group_barrier(0x402, VPM, 0);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dq kernel (own rows: queries; streamed: K and V of the window)
 // ---------------------------------------------------------------------------
 
-template <int D, int WAVES, int RB, int BN, bool RASTER, bool PAD>
+template <int D, int WAVES, int RB, int BN, bool RASTER, bool PAD, bool FULL>
 __global__ void __launch_bounds__(WAVES * 64, (WAVES <= 4 ? 2 : 1))
 bwd_dq_kernel(const AttnParams p, const BwdParams b) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
@@ -273,9 +291,19 @@ bwd_dq_kernel(const AttnParams p, const BwdParams b) {
     const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
     f32x4 s[RB][C::kKT], dp[RB][C::kKT];
     mma_rows<C, RB>(s, kcur, koff, qf);    // S^T[key][row] = K Q^T
+    sched_phase<RB, C::kKT * C::kDK, 1, 2, 0>();
+    // P^T while dP^T = V dO^T runs
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kt = 0; kt < C::kKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s[rb][kt][r] = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -lse2[rb]));
     mma_rows<C, RB>(dp, vcur, koff, df);   // dP^T[key][row] = V dO^T
-    // next chunk's loads after the row-wise reads (their LDS writes then
-    // land during the VALU work)
+    sched_phase<RB, C::kKT * C::kDK, 1, 2, 3>();
+    __builtin_amdgcn_sched_barrier(0);
+    // next chunk's loads after the row-wise reads
     if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -284,13 +312,13 @@ bwd_dq_kernel(const AttnParams p, const BwdParams b) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = 16 * kt + 4 * g + r;
-          const bool off = (nvalid < C::kBN && key >= nvalid) || !((real >> key) & 1ull);
-          const float pr = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -lse2[rb]));
-          s[rb][kt][r] = off ? 0.f : pr * (dp[rb][kt][r] - dl[rb]);   // dS^T
+          const bool off = !FULL && ((nvalid < C::kBN && key >= nvalid) || !((real >> key) & 1ull));
+          s[rb][kt][r] = off ? 0.f : s[rb][kt][r] * (dp[rb][kt][r] - dl[rb]);   // dS^T
         }
     bf16x8 wf[RB][C::kKP];
     pack_bf16<C, RB>(wf, s);
     mma_tr<C, RB>(acc, kcur, voff, wf);    // dQ^T[d][row] += K^T dS^T
+    sched_phase<RB, C::kKP * C::kDB, 2, 2, 0>();
   };
   for (int it = 0; it < walk.n_chunks; it += 2) {
     chunk_step(kb0, vb0, kb1, vb1, it);
@@ -304,7 +332,7 @@ bwd_dq_kernel(const AttnParams p, const BwdParams b) {
 // whose window holds the key tile)
 // ---------------------------------------------------------------------------
 
-template <int D, int WAVES, int RB, int BN, bool RASTER, bool PAD>
+template <int D, int WAVES, int RB, int BN, bool RASTER, bool PAD, bool FULL>
 __global__ void __launch_bounds__(WAVES * 64, (WAVES <= 4 ? 2 : 1))
 bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
@@ -387,6 +415,8 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
     const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
     f32x4 s[RB][C::kKT];
     mma_rows<C, RB>(s, qcur, koff, kf);    // S[q][key] = Q K^T
+    sched_phase<RB, C::kKT * C::kDK, 1, 2, 0>();
+    __builtin_amdgcn_sched_barrier(0);
     if (it + 1 < walk.n_chunks) dma(it + 1, qnxt, onxt, lnxt, dnxt);
     f32x4 lq[C::kKT], dq_[C::kKT];
 #pragma unroll
@@ -394,6 +424,7 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
       lq[kt] = *reinterpret_cast<const f32x4*>(lcur + 16 * kt + 4 * g);
       dq_[kt] = *reinterpret_cast<const f32x4*>(dcur + 16 * kt + 4 * g);
     }
+    // P while dP = dO V^T runs
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -401,15 +432,16 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int qrow = 16 * kt + 4 * g + r;
-          const bool off = (nvalid < C::kBN && qrow >= nvalid) || !((real >> qrow) & 1ull);
+          const bool off = !FULL && ((nvalid < C::kBN && qrow >= nvalid) || !((real >> qrow) & 1ull));
           const float pr = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -lq[kt][r] * kLog2e));
           s[rb][kt][r] = off ? 0.f : pr;                  // P[q][key]
         }
     bf16x8 wf[RB][C::kKP];
     pack_bf16<C, RB>(wf, s);
-    mma_tr<C, RB>(dv, ocur, voff, wf);     // dV^T[d][key] += dO^T P
     f32x4 dp[RB][C::kKT];
     mma_rows<C, RB>(dp, ocur, koff, vf);   // dP[q][key] = dO V^T
+    sched_phase<RB, C::kKT * C::kDK, 1, 2, 3>();
+    // dS while dV^T += dO^T P runs
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -419,11 +451,15 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
           // a masked row may carry garbage lse / D (padding rows of a tile-major
           // tensor are never written): select, do not multiply
           const int qrow = 16 * kt + 4 * g + r;
-          const bool off = (nvalid < C::kBN && qrow >= nvalid) || !((real >> qrow) & 1ull);
+          const bool off = !FULL && ((nvalid < C::kBN && qrow >= nvalid) || !((real >> qrow) & 1ull));
           s[rb][kt][r] = off ? 0.f : s[rb][kt][r] * (dp[rb][kt][r] - dq_[kt][r]);   // dS
         }
-    pack_bf16<C, RB>(wf, s);
-    mma_tr<C, RB>(dk, qcur, voff, wf);     // dK^T[d][key] += Q^T dS
+    bf16x8 wd[RB][C::kKP];
+    pack_bf16<C, RB>(wd, s);
+    mma_tr<C, RB>(dv, ocur, voff, wf);     // dV^T[d][key] += dO^T P
+    sched_phase<RB, C::kKP * C::kDB, 2, 2, 3>();
+    mma_tr<C, RB>(dk, qcur, voff, wd);     // dK^T[d][key] += Q^T dS
+    sched_phase<RB, C::kKP * C::kDB, 2, 2, 0>();
   };
   for (int it = 0; it < walk.n_chunks; it += 2) {
     chunk_step(qb0, ob0, lb0, db0, qb1, ob1, lb1, db1, it);
@@ -602,20 +638,20 @@ unsigned raster_bytes(const AttnProblem& a, bool keys) {
   return (unsigned)run * sizeof(int);
 }
 
-template <int D, int WAVES, int RB, bool KEYS, bool PAD>
+template <int D, int WAVES, int RB, bool KEYS, bool PAD, bool FULL>
 void launch_pass_kernel(const AttnParams& p, const BwdParams& b, unsigned grid, bool raster,
                         unsigned lds, hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, RB, 64>;
   if constexpr (KEYS) {
     if (raster)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, WAVES, RB, 64, true, PAD>), dim3(grid), dim3(C::kThreads), lds, stream, p, b);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, WAVES, RB, 64, true, PAD, FULL>), dim3(grid), dim3(C::kThreads), lds, stream, p, b);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, WAVES, RB, 64, false, PAD>), dim3(grid), dim3(C::kThreads), 0, stream, p, b);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, WAVES, RB, 64, false, PAD, FULL>), dim3(grid), dim3(C::kThreads), 0, stream, p, b);
   } else {
     if (raster)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, WAVES, RB, 64, true, PAD>), dim3(grid), dim3(C::kThreads), lds, stream, p, b);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, WAVES, RB, 64, true, PAD, FULL>), dim3(grid), dim3(C::kThreads), lds, stream, p, b);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, WAVES, RB, 64, false, PAD>), dim3(grid), dim3(C::kThreads), 0, stream, p, b);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, WAVES, RB, 64, false, PAD, FULL>), dim3(grid), dim3(C::kThreads), 0, stream, p, b);
   }
 }
 
@@ -628,10 +664,14 @@ int launch_bf16_pass(const BwdProblem& pr, hipStream_t stream) {
   const unsigned grid = (unsigned)p.per_xcd * kXcds;
   const bool raster = pr.attn.raster;
   const unsigned lds = raster ? raster_bytes(pr.attn, KEYS) : 0;
+  // Whole 64-row chunks everywhere (every run is a whole number of tiles):
+  // no chunk needs masking.
   if (pr.attn.g.padded)
-    launch_pass_kernel<D, WAVES, RB, KEYS, true>(p, b, grid, raster, lds, stream);
+    launch_pass_kernel<D, WAVES, RB, KEYS, true, false>(p, b, grid, raster, lds, stream);
+  else if (pr.attn.g.tau % 64 == 0)
+    launch_pass_kernel<D, WAVES, RB, KEYS, false, true>(p, b, grid, raster, lds, stream);
   else
-    launch_pass_kernel<D, WAVES, RB, KEYS, false>(p, b, grid, raster, lds, stream);
+    launch_pass_kernel<D, WAVES, RB, KEYS, false, false>(p, b, grid, raster, lds, stream);
   return (int)hipGetLastError();
 }
 
