@@ -251,6 +251,19 @@ __device__ __forceinline__ void qk_tile(WaveState<C, RB>& w, int kt, const char*
 
 // Probabilities of score tile kt against the reference max, rounded to bf16
 // into their slots of the PV operand (tile kt is half kt % 2 of key step kt / 2).
+// Log-sum-exp only: the probabilities are summed in fp32 and never rounded.
+template <class C, int RB>
+__device__ __forceinline__ void exp_sum_tile(WaveState<C, RB>& w, int kt, float scale_log2,
+                                             float (&lc)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float e[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(w.s[rb][kt][r], scale_log2, -w.m[rb]));
+    lc[rb] += (e[0] + e[1]) + (e[2] + e[3]);
+  }
+}
+
 template <class C, int RB>
 __device__ __forceinline__ void exp_tile(WaveState<C, RB>& w, int kt, float scale_log2) {
 #pragma unroll
@@ -281,18 +294,20 @@ __device__ __forceinline__ void chunk_sums(const WaveState<C, RB>& w, float (&lc
   }
 }
 
-// Issue order of the QK^T phase: operand reads two steps ahead; from tile 1
-// on, two VALU instructions (the previous tile's probabilities and sums)
+// Issue order of the QK^T phase: operand reads three steps ahead; from tile
+// 1 on, two VALU instructions (the previous tile's probabilities and sums)
 // after each MFMA. Measured on the headline shape: two per MFMA 2-2.5 %
-// faster than the plain order, three or four per MFMA slower.
+// faster than the plain order, three or four per MFMA slower; reading three
+// steps ahead rather than two another 1.7 % (four: less).
+constexpr int kQkReadAhead = 3;
 template <int RB, int KT, int DK>
 __device__ __forceinline__ void sched_qk_softmax() {
   constexpr int steps = KT * DK;
 #pragma unroll
-  for (int st = 0; st < kReadAhead && st < steps; ++st) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  for (int st = 0; st < kQkReadAhead && st < steps; ++st) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
   for (int st = 0; st < steps; ++st) {
-    if (st + kReadAhead < steps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (st + kQkReadAhead < steps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
     for (int m = 0; m < RB; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -428,20 +443,33 @@ attn_bf16_kernel(const AttnParams p) {
     wait_vm_all();     // this wave's loads of chunk `it` have landed in LDS
     __syncthreads();   // ... and every wave's; chunk it-1's buffers are free
     if constexpr (FULL) {
-#pragma unroll
-      for (int kt = 0; kt < C::kKT; ++kt) {
-        qk_tile<C, RB>(w, kt, kcur);
-        if (kt > 0) exp_tile<C, RB>(w, kt - 1, p.scale_log2);
-      }
-      exp_tile<C, RB>(w, C::kKT - 1, p.scale_log2);
       float lc[RB];
-      chunk_sums<C, RB>(w, lc);
+      if constexpr (LSE_ONLY) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) lc[rb] = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < C::kKT; ++kt) {
+          qk_tile<C, RB>(w, kt, kcur);
+          if (kt > 0) exp_sum_tile<C, RB>(w, kt - 1, p.scale_log2, lc);
+        }
+        exp_sum_tile<C, RB>(w, C::kKT - 1, p.scale_log2, lc);
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < C::kKT; ++kt) {
+          qk_tile<C, RB>(w, kt, kcur);
+          if (kt > 0) exp_tile<C, RB>(w, kt - 1, p.scale_log2);
+        }
+        exp_tile<C, RB>(w, C::kKT - 1, p.scale_log2);
+        chunk_sums<C, RB>(w, lc);
+      }
       // Keep the probabilities and sums here, beside the MFMAs: the compiler
       // would otherwise move them past the branch of the loads below.
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
+        if constexpr (!LSE_ONLY) {
 #pragma unroll
-        for (int kp = 0; kp < C::kKP; ++kp) asm volatile("" : "+v"(w.pf[rb][kp]));
+          for (int kp = 0; kp < C::kKP; ++kp) asm volatile("" : "+v"(w.pf[rb][kp]));
+        }
         asm volatile("" : "+v"(lc[rb]));
       }
       sched_qk_softmax<RB, C::kKT, C::kDK>();
@@ -463,9 +491,16 @@ attn_bf16_kernel(const AttnParams p) {
           mx[rb] = a * p.scale_log2;
         }
         rescale_to<C, RB>(w, mx);
+        if constexpr (LSE_ONLY) {
 #pragma unroll
-        for (int kt = 0; kt < C::kKT; ++kt) exp_tile<C, RB>(w, kt, p.scale_log2);
-        chunk_sums<C, RB>(w, lc);
+          for (int rb = 0; rb < RB; ++rb) lc[rb] = 0.f;
+#pragma unroll
+          for (int kt = 0; kt < C::kKT; ++kt) exp_sum_tile<C, RB>(w, kt, p.scale_log2, lc);
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < C::kKT; ++kt) exp_tile<C, RB>(w, kt, p.scale_log2);
+          chunk_sums<C, RB>(w, lc);
+        }
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) w.lsum[rb] += lc[rb];
