@@ -295,10 +295,12 @@ __device__ __forceinline__ void chunk_sums(const WaveState<C, RB>& w, float (&lc
 }
 
 // Issue order of the QK^T phase: operand reads three steps ahead; from tile
-// 1 on, two VALU instructions (the previous tile's probabilities and sums)
-// after each MFMA. Measured on the headline shape: two per MFMA 2-2.5 %
-// faster than the plain order, three or four per MFMA slower; reading three
-// steps ahead rather than two another 1.7 % (four: less).
+// 1 on, one VALU instruction (of the previous tile's probabilities and sums)
+// after each MFMA, the rest where the scheduler puts them. Measured on the
+// headline shape against the plain order: with reads two steps ahead, two
+// per MFMA 2-2.5 % faster, three or four slower; reads three steps ahead
+// another 1.7 % (four: less); then one per MFMA 1.3 % faster than two, none
+// 2 % slower.
 constexpr int kQkReadAhead = 3;
 template <int RB, int KT, int DK>
 __device__ __forceinline__ void sched_qk_softmax() {
@@ -311,7 +313,7 @@ __device__ __forceinline__ void sched_qk_softmax() {
 #pragma unroll
     for (int m = 0; m < RB; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (st >= DK) __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);   // VALU and transcendental
+      if (st >= DK) __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);   // VALU and transcendental
     }
   }
 }
