@@ -239,7 +239,9 @@ int sta_backward(const void* q, const void* k, const void* v, const void* out, c
  * section, recall of local windows across prompts).
  * Computed as the mean of exp(lse_c(i) - lse_full(i)) from the two row
  * log-sum-exps (the attention kernels in a log-sum-exp-only mode: no V, no
- * output), then a deterministic double-precision reduction per (b, h).
+ * output; with bf16 inputs this mode sums the probabilities in float32
+ * without rounding them to bfloat16, as nothing multiplies them), then a
+ * deterministic double-precision reduction per (b, h).
  *   q, k:        device [B][heads][S][head_dim], token order `order`, read.
  *   recall:      device float [B][heads][n_candidates], written.
  *   workspace:   device float [2][B][heads][S], caller-owned scratch.
