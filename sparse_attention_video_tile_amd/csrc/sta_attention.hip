@@ -295,14 +295,15 @@ __device__ __forceinline__ void chunk_sums(const WaveState<C, RB>& w, float (&lc
 }
 
 // Issue order of the QK^T phase: operand reads three steps ahead; from tile
-// 1 on, one VALU instruction (of the previous tile's probabilities and sums)
-// after each MFMA, the rest where the scheduler puts them. Measured on the
-// headline shape against the plain order: with reads two steps ahead, two
-// per MFMA 2-2.5 % faster, three or four slower; reads three steps ahead
-// another 1.7 % (four: less); then one per MFMA 1.3 % faster than two, none
-// 2 % slower.
+// 1 on, VPM VALU instructions (of the previous tile's probabilities and
+// sums) after each MFMA, the rest where the scheduler puts them. Measured on
+// the headline shape against the plain order: with reads two steps ahead,
+// two per MFMA 2-2.5 % faster, three or four slower; reads three steps ahead
+// another 1.7 % (four: less). Then the kernel that addresses plane chunks
+// by arithmetic is 1.3 % faster with one per MFMA than with two (none: 2 %
+// slower), while the tile-major kernel is 2 % slower with one than with two.
 constexpr int kQkReadAhead = 3;
-template <int RB, int KT, int DK>
+template <int RB, int KT, int DK, int VPM>
 __device__ __forceinline__ void sched_qk_softmax() {
   constexpr int steps = KT * DK;
 #pragma unroll
@@ -313,7 +314,7 @@ __device__ __forceinline__ void sched_qk_softmax() {
 #pragma unroll
     for (int m = 0; m < RB; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (st >= DK) __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);   // VALU and transcendental
+      if (st >= DK) __builtin_amdgcn_sched_group_barrier(0x402, VPM, 0);   // VALU and transcendental
     }
   }
 }
@@ -474,7 +475,7 @@ attn_bf16_kernel(const AttnParams p) {
         }
         asm volatile("" : "+v"(lc[rb]));
       }
-      sched_qk_softmax<RB, C::kKT, C::kDK>();
+      sched_qk_softmax<RB, C::kKT, C::kDK, plane ? 1 : 2>();
       __builtin_amdgcn_sched_barrier(0);
       if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
       bool grow = false;
