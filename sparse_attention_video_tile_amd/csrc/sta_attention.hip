@@ -230,10 +230,11 @@ __device__ __forceinline__ void sched_reads_ahead() {
 // tile kt + 1, against the reference max m as it stands. No chunk maximum is
 // taken: every probability is at most its lane's sum over the chunk, so a
 // lane sum within 2^8 keeps every probability within 2^8, the same bound the
-// lazy rescale keeps. A larger (or infinite) sum, which the first chunk
-// always gives (m = -inf), sends the chunk down a rare branch that computes
-// its scores again from LDS, moves m to the exact row maximum, rescales O and
-// the row sums, and redoes the probabilities.
+// lazy rescale keeps. A larger (or infinite) sum sends the chunk down a rare
+// branch that computes its scores again from LDS, moves m to the exact row
+// maximum, rescales O and the row sums, and redoes the probabilities. The
+// first chunk of a work item (m = -inf, which would always take that branch)
+// runs the max-first order of the masked path instead.
 
 // S^T of score tile kt (keys 16*kt ..) for every row block.
 template <class C, int RB>
@@ -318,6 +319,11 @@ __device__ __forceinline__ void sched_qk_softmax() {
     }
   }
 }
+
+template <bool B>
+struct FirstChunk {
+  static constexpr bool value = B;
+};
 
 template <class C, int RB>
 __device__ __forceinline__ void load_q_init(WaveState<C, RB>& w, const bf16_t* qg,
@@ -438,14 +444,14 @@ attn_bf16_kernel(const AttnParams p) {
   WaveState<C, RB> w;
   load_q_init<C, RB>(w, qg, map_rows<C, RB, RASTER>(p, t, wave, l16), l16, g);
 
-  auto chunk_step = [&](const char* kcur, const char* vcur, char* knxt, char* vnxt, int it)
+  auto chunk_step = [&](auto first, const char* kcur, const char* vcur, char* knxt, char* vnxt, int it)
                         __attribute__((always_inline)) {
     int row0, nvalid;
     walk.at(it, &row0, &nvalid);
     const unsigned long long real = chunk_real_keys<PAD && !DENSE>(p, walk, it, lane);
     wait_vm_all();     // this wave's loads of chunk `it` have landed in LDS
     __syncthreads();   // ... and every wave's; chunk it-1's buffers are free
-    if constexpr (FULL) {
+    if constexpr (FULL && !decltype(first)::value) {
       float lc[RB];
       if constexpr (LSE_ONLY) {
 #pragma unroll
@@ -530,9 +536,19 @@ attn_bf16_kernel(const AttnParams p) {
       }
     }
   };
-  for (int it = 0; it < walk.n_chunks; it += 2) {
-    chunk_step(kb0, vb0, kb1, vb1, it);
-    if (it + 1 < walk.n_chunks) chunk_step(kb1, vb1, kb0, vb0, it + 1);
+  if constexpr (FULL) {
+    // The first chunk sets the reference max: the max-first order, which the
+    // sum test would otherwise send down its rare branch every time.
+    chunk_step(FirstChunk<true>{}, kb0, vb0, kb1, vb1, 0);
+    for (int it = 1; it < walk.n_chunks; it += 2) {
+      chunk_step(FirstChunk<false>{}, kb1, vb1, kb0, vb0, it);
+      if (it + 1 < walk.n_chunks) chunk_step(FirstChunk<false>{}, kb0, vb0, kb1, vb1, it + 1);
+    }
+  } else {
+    for (int it = 0; it < walk.n_chunks; it += 2) {
+      chunk_step(FirstChunk<false>{}, kb0, vb0, kb1, vb1, it);
+      if (it + 1 < walk.n_chunks) chunk_step(FirstChunk<false>{}, kb1, vb1, kb0, vb0, it + 1);
+    }
   }
   // The row map is built again rather than kept in registers across the loop.
   store_out<C, RB>(w, LSE_ONLY ? nullptr : og, p.lse ? p.lse + t.head_base / D : nullptr,
