@@ -200,7 +200,9 @@ __device__ __forceinline__ void load_row_values(const float* src, int row0, int 
 
 // Operand reads of an MFMA phase issued AHEAD steps before the MFMAs that use
 // them (each step: DS reads, then RB MFMAs); VALU work from an earlier phase
-// may fill VPM instructions after each MFMA.
+// may fill VPM instructions after each MFMA. Measured at the headline shape:
+// three steps ahead for the row-wise reads and two for the transposing ones,
+// three VALU instructions per MFMA where there is VALU work to place.
 template <int RB, int STEPS, int DS, int AHEAD, int VPM>
 __device__ __forceinline__ void sched_phase() {
 #pragma unroll
@@ -291,7 +293,7 @@ bwd_dq_kernel(const AttnParams p, const BwdParams b) {
     const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
     f32x4 s[RB][C::kKT], dp[RB][C::kKT];
     mma_rows<C, RB>(s, kcur, koff, qf);    // S^T[key][row] = K Q^T
-    sched_phase<RB, C::kKT * C::kDK, 1, 2, 0>();
+    sched_phase<RB, C::kKT * C::kDK, 1, 3, 0>();
     // P^T while dP^T = V dO^T runs
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -301,7 +303,7 @@ bwd_dq_kernel(const AttnParams p, const BwdParams b) {
         for (int r = 0; r < 4; ++r)
           s[rb][kt][r] = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -lse2[rb]));
     mma_rows<C, RB>(dp, vcur, koff, df);   // dP^T[key][row] = V dO^T
-    sched_phase<RB, C::kKT * C::kDK, 1, 2, 3>();
+    sched_phase<RB, C::kKT * C::kDK, 1, 3, 3>();
     __builtin_amdgcn_sched_barrier(0);
     // next chunk's loads after the row-wise reads
     if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
@@ -415,7 +417,7 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
     const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
     f32x4 s[RB][C::kKT];
     mma_rows<C, RB>(s, qcur, koff, kf);    // S[q][key] = Q K^T
-    sched_phase<RB, C::kKT * C::kDK, 1, 2, 0>();
+    sched_phase<RB, C::kKT * C::kDK, 1, 3, 0>();
     __builtin_amdgcn_sched_barrier(0);
     if (it + 1 < walk.n_chunks) dma(it + 1, qnxt, onxt, lnxt, dnxt);
     f32x4 lq[C::kKT], dq_[C::kKT];
@@ -440,7 +442,7 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
     pack_bf16<C, RB>(wf, s);
     f32x4 dp[RB][C::kKT];
     mma_rows<C, RB>(dp, ocur, koff, vf);   // dP[q][key] = dO V^T
-    sched_phase<RB, C::kKT * C::kDK, 1, 2, 3>();
+    sched_phase<RB, C::kKT * C::kDK, 1, 3, 3>();
     // dS while dV^T += dO^T P runs
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
