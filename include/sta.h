@@ -198,6 +198,29 @@ int sta_forward_lse(const void* q, const void* k, const void* v, void* out, floa
                     const int* window, float scale, int dtype, int order, void* stream);
 
 /*
+ * STA forward with fp8 queries and keys. The pages mention FP8 quantization
+ * inside a sparse attention kernel (dianyo ICML2025 blog, Sparse VideoGen,
+ * "Observation & Proposed Method"); here it applies to the score product:
+ *     O_i = softmax(scale * (q_descale Q8_i) (k_descale K8_J)^T) V_J,
+ * with Q8, K8 the values of the fp8 codes, window rule as sta_forward.
+ *   q8, k8:  device uint8 [B][heads][S][128], OCP 8-bit floating point E4M3
+ *            codes (bias 7, no infinities, 0x7F / 0xFF NaN, largest 448),
+ *            read. The caller quantizes.
+ *   v:       device bf16 [B][heads][S][128], read.
+ *   out:     device bf16, same shape, written. No overlap with inputs.
+ *   q_descale, k_descale: finite, > 0; per tensor. scale * q_descale *
+ *            k_descale must be finite and > 0.
+ *   order:   sta_order of q8, k8, v and out (tile-major or raster, with the
+ *            rules of sta_forward and sta_forward_raster).
+ * head_dim must be 128 (else STA_ERR_UNSUPPORTED). The fp8 products are exact
+ * and summed in float32; probabilities and output are rounded to bfloat16 as
+ * in sta_forward.
+ */
+int sta_forward_fp8(const void* q8, const void* k8, const void* v, void* out, int B, int heads,
+                    int head_dim, int T, int H, int W, const int* tile, const int* window,
+                    float scale, float q_descale, float k_descale, int order, void* stream);
+
+/*
  * STA backward: gradients of sum(dout * O) with respect to q, k and v, for
  * training a model with a fixed STA window (the fine-tuning of the pages:
  * podcast transcript, the answer on fine-tuning; atlas.scime.ai summary,

@@ -12,3 +12,4 @@ from .sta_backward_oracle import (  # noqa: F401
     sta_lse,
     window_recall,
 )
+from .sta_fp8_oracle import e4m3_decode, sta_attention_fp8, sta_attention_fp8_rows  # noqa: F401

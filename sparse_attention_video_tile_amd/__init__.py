@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     sta_backward,
     sta_forward,
     sta_forward_lse,
+    sta_forward_fp8,
     sta_forward_raster,
     sta_full_attention,
     sta_kv_pair_count,

@@ -36,6 +36,7 @@ EXPORTS = (
     "sta_forward",
     "sta_forward_raster",
     "sta_forward_lse",
+    "sta_forward_fp8",
     "sta_backward",
     "sta_window_recall",
     "sta_full_attention",
@@ -83,6 +84,10 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.sta_forward_lse.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int,
                                     c_int, c_int, c_int, c_int, int3, int3, c_float, c_int, c_int,
                                     c_void_p]
+    lib.sta_forward_fp8.restype = c_int
+    lib.sta_forward_fp8.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
+                                    c_int, c_int, c_int, int3, int3, c_float, c_float, c_float,
+                                    c_int, c_void_p]
     lib.sta_backward.restype = c_int
     lib.sta_backward.argtypes = [c_void_p] * 10 + [c_int, c_int, c_int, c_int, c_int, c_int, int3,
                                                    int3, c_float, c_int, c_int, c_void_p]
@@ -420,6 +425,41 @@ def sta_forward_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tile: Seq
                                  _dtype_code(q), order, _stream(dev))
     _check(rc, "sta_forward_lse")
     return out, lse
+
+
+_FP8_DTYPES = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+
+
+def sta_forward_fp8(q8: torch.Tensor, k8: torch.Tensor, v: torch.Tensor, tile: Sequence[int], window,
+                    q_descale: float, k_descale: float, scale: Optional[float] = None,
+                    volume: Optional[Sequence[int]] = None,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """STA forward with fp8 (OCP E4M3) q8, k8 (torch.uint8 codes or
+    torch.float8_e4m3fn), per-tensor descales and bf16 v; returns bf16 out.
+    Raster (B, heads, T, H, W, 128) tensors, or tile-major (B, heads, S, 128)
+    ones with `volume`."""
+    lib = load_library()
+    if q8.shape != k8.shape or q8.shape != v.shape:
+        raise ValueError("q8, k8, v must share a shape")
+    if q8.dtype not in _FP8_DTYPES or k8.dtype not in _FP8_DTYPES:
+        raise TypeError("q8 and k8 must be torch.uint8 codes or torch.float8_e4m3fn")
+    if v.dtype != torch.bfloat16:
+        raise TypeError("v must be torch.bfloat16")
+    B, heads, d, (T, H, W), order = _order_shapes(v, volume, tile)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(v)
+    elif out.shape != v.shape or out.dtype != v.dtype:
+        raise ValueError("out must match v")
+    dev = _require_gpu(q8, k8, v, out)
+    with torch.cuda.device(dev):
+        rc = lib.sta_forward_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(), B, heads,
+                                 d, T, H, W, _int_array(tile),
+                                 _int_array(_windows_per_head(window, heads)), float(scale),
+                                 float(q_descale), float(k_descale), order, _stream(dev))
+    _check(rc, "sta_forward_fp8")
+    return out
 
 
 def sta_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,

@@ -156,7 +156,8 @@ int attention_common(sta::AttnProblem& p, void* stream) {
   if (BH > (1LL << 24)) return fail(STA_ERR_INVALID_ARG, "B*heads=%lld is too large", BH);
   const int rows = p.dense || p.raster ? p.g.S : p.g.S_pad;
   const size_t bytes = (size_t)BH * rows * p.head_dim * es;
-  if (overlaps(p.out, bytes, p.q, bytes) || overlaps(p.out, bytes, p.k, bytes) ||
+  const size_t qk_bytes = p.qk_fp8 ? (size_t)BH * rows * p.head_dim : bytes;
+  if (overlaps(p.out, bytes, p.q, qk_bytes) || overlaps(p.out, bytes, p.k, qk_bytes) ||
       overlaps(p.out, bytes, p.v, bytes))
     return fail(STA_ERR_INVALID_ARG, "output overlaps an input");
   rc = sta::launch_attention(p, stream);
@@ -244,7 +245,8 @@ int check_raster_runs(const sta::Geometry& g, int heads, const uint16_t (*omega)
 
 int forward_common(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                    int heads, int head_dim, int T, int H, int W, const int* tile,
-                   const int* window, float scale, int dtype, void* stream, bool raster);
+                   const int* window, float scale, int dtype, void* stream, bool raster,
+                   bool qk_fp8 = false);
 
 }  // namespace
 
@@ -295,7 +297,8 @@ namespace {
 
 int forward_common(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                    int heads, int head_dim, int T, int H, int W, const int* tile,
-                   const int* window, float scale, int dtype, void* stream, bool raster) {
+                   const int* window, float scale, int dtype, void* stream, bool raster,
+                   bool qk_fp8) {
   if (heads <= 0 || heads > STA_MAX_HEADS)
     return fail(STA_ERR_INVALID_ARG, "heads=%d must be in [1, %d]", heads, STA_MAX_HEADS);
   static thread_local sta::AttnProblem p;
@@ -304,6 +307,7 @@ int forward_common(const void* q, const void* k, const void* v, void* out, float
   p.dense = false;
   p.raster = raster;
   p.lse_only = false;
+  p.qk_fp8 = qk_fp8;
   int rc = check_volume(T, H, W, tile, &p.g);
   if (rc) return rc;
   if ((rc = check_windows(p.g, heads, window, p.omega))) return rc;
@@ -348,6 +352,7 @@ int backward_common(const void* q, const void* k, const void* v, const void* out
   p.dense = false;
   p.raster = order == STA_RASTER;
   p.lse_only = false;
+  p.qk_fp8 = false;
   if ((rc = check_volume(T, H, W, tile, &p.g))) return rc;
   if ((rc = check_windows(p.g, heads, window, p.omega))) return rc;
   if ((rc = check_f32_padding(p.g, dtype))) return rc;
@@ -411,6 +416,24 @@ int sta_forward_lse(const void* q, const void* k, const void* v, void* out, floa
                         dtype, stream, order == STA_RASTER);
 }
 
+int sta_forward_fp8(const void* q8, const void* k8, const void* v, void* out, int B, int heads,
+                    int head_dim, int T, int H, int W, const int* tile, const int* window,
+                    float scale, float q_descale, float k_descale, int order, void* stream) {
+  if (order != STA_TILE_MAJOR && order != STA_RASTER)
+    return fail(STA_ERR_INVALID_ARG, "unknown token order %d", order);
+  if (!(q_descale > 0.0f) || !isfinite(q_descale) || !(k_descale > 0.0f) || !isfinite(k_descale))
+    return fail(STA_ERR_INVALID_ARG, "descales %g, %g must be finite and positive",
+                (double)q_descale, (double)k_descale);
+  if (head_dim != 128)
+    return fail(STA_ERR_UNSUPPORTED, "head_dim %d: the fp8 kernels need 128", head_dim);
+  const float folded = scale * q_descale * k_descale;
+  if (!(scale > 0.0f) || !isfinite(scale) || !(folded > 0.0f) || !isfinite(folded))
+    return fail(STA_ERR_INVALID_ARG, "scale %g times the descales must be finite and positive",
+                (double)scale);
+  return forward_common(q8, k8, v, out, nullptr, B, heads, head_dim, T, H, W, tile, window, folded,
+                        STA_BF16, stream, order == STA_RASTER, true);
+}
+
 int sta_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int heads,
                  int head_dim, int T, int H, int W, const int* tile, const int* window,
@@ -466,14 +489,14 @@ int sta_window_recall(const void* q, const void* k, float* recall, float* worksp
   // full-attention lse (token order does not matter for all-keys attention)
   dense.q = q; dense.k = k; dense.v = k; dense.out = nullptr; dense.lse = lse_full;
   dense.B = B; dense.heads = heads; dense.head_dim = head_dim; dense.dtype = dtype; dense.scale = scale;
-  dense.dense = true; dense.raster = false; dense.lse_only = true;
+  dense.dense = true; dense.raster = false; dense.lse_only = true; dense.qk_fp8 = false;
   memset(&dense.g, 0, sizeof(dense.g));
   dense.g.S = win.g.S;
   rc = sta::launch_attention(dense, stream);
   if (rc) return rc < 0 ? fail(rc, "no kernel for dtype %d with head_dim %d", dtype, head_dim) : launched(rc);
   win.q = q; win.k = k; win.v = k; win.out = nullptr; win.lse = lse_win;
   win.B = B; win.heads = heads; win.head_dim = head_dim; win.dtype = dtype; win.scale = scale;
-  win.dense = false; win.raster = order == STA_RASTER; win.lse_only = true;
+  win.dense = false; win.raster = order == STA_RASTER; win.lse_only = true; win.qk_fp8 = false;
   for (int c = 0; c < n_candidates; ++c) {
     for (int h = 0; h < heads; ++h) {
       win.omega[h][0] = (uint16_t)(candidates[3 * c] / win.g.ct);
@@ -496,6 +519,7 @@ int sta_full_attention(const void* q, const void* k, const void* v, void* out, i
   memset(&p.g, 0, sizeof(p.g));
   p.raster = false;
   p.lse_only = false;
+  p.qk_fp8 = false;
   p.lse = nullptr;
   p.q = q; p.k = k; p.v = v; p.out = out;
   p.B = B; p.heads = heads; p.head_dim = head_dim; p.dtype = dtype; p.scale = scale;

@@ -32,14 +32,15 @@ namespace {
 // probabilities, and the lane's byte offsets into a K/V buffer.
 template <class C, int RB>
 struct WaveState {
-  bf16x8 qf[RB][C::kDK];
+  typename C::QFrag qf[RB][C::kDK];
   f32x4 o[RB][C::kDB];
   float m[RB], lsum[RB];
   f32x4 s[RB][C::kKT];
   bf16x8 pf[RB][C::kKP];
-  // K operand: row 16*kt + l16, chunk 4*dk + g; the swizzled offset is
-  // koff[dk] + 16*kt*row_bytes because the row's low 4 bits are l16.
-  int koff[C::kDK];
+  // K operand: row 16*kt + l16, chunk 4*dk + g (fp8: chunks 8*dk + 2g and
+  // 8*dk + 2g + 1, in koff[2dk] and koff[2dk + 1]); the swizzled offset is
+  // koff[.] + 16*kt*row_bytes because the row's low 4 bits are l16.
+  int koff[C::kKOffs];
   // V operand (transposing read): row 32*kp + 4g + l16/4 (+16 for the upper
   // half), element column 16*db + 4*(l16 % 4); offset voff[db] + rows*row_bytes.
   int voff[C::kDB];
@@ -47,14 +48,45 @@ struct WaveState {
 
 template <class C, int RB>
 __device__ __forceinline__ void lane_offsets(WaveState<C, RB>& w, int l16, int g) {
+  if constexpr (C::kQK8) {
 #pragma unroll
-  for (int dk = 0; dk < C::kDK; ++dk) w.koff[dk] = swz<C::kCPR>(l16, 4 * dk + g);
+    for (int i = 0; i < C::kKOffs; ++i)
+      w.koff[i] = swz<C::KGeom::kCPR>(l16, 8 * (i / 2) + 2 * g + (i % 2));
+  } else {
+#pragma unroll
+    for (int dk = 0; dk < C::kDK; ++dk) w.koff[dk] = swz<C::kCPR>(l16, 4 * dk + g);
+  }
   const int s4 = l16 >> 2, sq = l16 & 3;
   const int vrow = 4 * g + s4;  // row within its 16-row group (< 16)
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) {
     const int col = 16 * db + 4 * sq;
     w.voff[db] = swz<C::kCPR>(vrow, col >> 3) + (col & 7) * 2;
+  }
+}
+
+// One k-step dk of score tile kt for every row block: sc[.][kt] += K Q^T.
+// fp8: a lane's 32 bytes of K are chunks 2g and 2g + 1 of the step's 128
+// dimensions, the same dimensions (in the same byte order) as its 32 bytes
+// of Q, so the MFMA pairs them whatever order it sums the products in. The
+// zero format and scale operands select e4m3 for both and no scaling.
+template <class C, int RB>
+__device__ __forceinline__ void qk_step(WaveState<C, RB>& w, f32x4 (&sc)[RB][C::kKT], int kt,
+                                        int dk, const char* kbuf) {
+  if constexpr (C::kQK8) {
+    const char* rows = kbuf + 16 * kt * C::KGeom::kRowBytes;
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(rows + w.koff[2 * dk]);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(rows + w.koff[2 * dk + 1]);
+    const i32x8 kf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      sc[rb][kt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, w.qf[rb][dk], sc[rb][kt],
+                                                                    0, 0, 0, 0, 0, 0);
+  } else {
+    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbuf + w.koff[dk] + 16 * kt * C::kRowBytes);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      sc[rb][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, w.qf[rb][dk], sc[rb][kt], 0, 0, 0);
   }
 }
 
@@ -68,13 +100,7 @@ __device__ __forceinline__ void qk_into(WaveState<C, RB>& w, f32x4 (&sc)[RB][C::
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) sc[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dk = 0; dk < C::kDK; ++dk) {
-      const bf16x8 kf =
-          *reinterpret_cast<const bf16x8*>(kbuf + w.koff[dk] + 16 * kt * C::kRowBytes);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        sc[rb][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, w.qf[rb][dk], sc[rb][kt], 0, 0, 0);
-    }
+    for (int dk = 0; dk < C::kDK; ++dk) qk_step<C, RB>(w, sc, kt, dk, kbuf);
   }
 }
 
@@ -242,12 +268,7 @@ __device__ __forceinline__ void qk_tile(WaveState<C, RB>& w, int kt, const char*
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) w.s[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int dk = 0; dk < C::kDK; ++dk) {
-    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbuf + w.koff[dk] + 16 * kt * C::kRowBytes);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      w.s[rb][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, w.qf[rb][dk], w.s[rb][kt], 0, 0, 0);
-  }
+  for (int dk = 0; dk < C::kDK; ++dk) qk_step<C, RB>(w, w.s, kt, dk, kbuf);
 }
 
 // Probabilities of score tile kt against the reference max, rounded to bf16
@@ -303,15 +324,16 @@ __device__ __forceinline__ void chunk_sums(const WaveState<C, RB>& w, float (&lc
 // another 1.7 % (four: less). Then the kernel that addresses plane chunks
 // by arithmetic is 1.3 % faster with one per MFMA than with two (none: 2 %
 // slower), while the tile-major kernel is 2 % slower with one than with two.
+// RPS: LDS reads per fragment step (2 for fp8 K).
 constexpr int kQkReadAhead = 3;
-template <int RB, int KT, int DK, int VPM>
+template <int RB, int KT, int DK, int VPM, int RPS = 1>
 __device__ __forceinline__ void sched_qk_softmax() {
   constexpr int steps = KT * DK;
 #pragma unroll
-  for (int st = 0; st < kQkReadAhead && st < steps; ++st) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  for (int st = 0; st < kQkReadAhead && st < steps; ++st) __builtin_amdgcn_sched_group_barrier(0x100, RPS, 0);
 #pragma unroll
   for (int st = 0; st < steps; ++st) {
-    if (st + kQkReadAhead < steps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (st + kQkReadAhead < steps) __builtin_amdgcn_sched_group_barrier(0x100, RPS, 0);
 #pragma unroll
     for (int m = 0; m < RB; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -325,18 +347,30 @@ struct FirstChunk {
   static constexpr bool value = B;
 };
 
+// Q rows into registers: bf16, dimensions 32*dk + 8g .. +8 of the lane's row;
+// fp8, dimensions 128*dk + 32g .. +32 (the bytes the K reads pair them with).
 template <class C, int RB>
-__device__ __forceinline__ void load_q_init(WaveState<C, RB>& w, const bf16_t* qg,
+__device__ __forceinline__ void load_q_init(WaveState<C, RB>& w, const void* qg,
                                             const RowMap<C, RB>& rm, int l16, int g) {
   lane_offsets<C, RB>(w, l16, g);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const bf16_t* src = qg + (long long)rm.tok[rb] * C::kD + 8 * g;
+    if constexpr (C::kQK8) {
+      const char* src = static_cast<const char*>(qg) + (long long)rm.tok[rb] * C::kD + 32 * g;
 #pragma unroll
-    for (int dk = 0; dk < C::kDK; ++dk) {
-      bf16x8 x = *reinterpret_cast<const bf16x8*>(src + 32 * dk);
-      if (!rm.ok[rb]) x = bf16x8{};
-      w.qf[rb][dk] = x;
+      for (int dk = 0; dk < C::kDK; ++dk) {
+        i32x8 x = *reinterpret_cast<const i32x8*>(src + 128 * dk);
+        if (!rm.ok[rb]) x = i32x8{};
+        w.qf[rb][dk] = x;
+      }
+    } else {
+      const bf16_t* src = static_cast<const bf16_t*>(qg) + (long long)rm.tok[rb] * C::kD + 8 * g;
+#pragma unroll
+      for (int dk = 0; dk < C::kDK; ++dk) {
+        bf16x8 x = *reinterpret_cast<const bf16x8*>(src + 32 * dk);
+        if (!rm.ok[rb]) x = bf16x8{};
+        w.qf[rb][dk] = x;
+      }
     }
     w.m[rb] = -INFINITY;
     w.lsum[rb] = 0.f;
@@ -384,18 +418,20 @@ __device__ __forceinline__ void store_out(WaveState<C, RB>& w, bf16_t* og, float
 // FULL: every chunk of every work item has BN real keys (no ragged run end,
 // no padding): only the spread-out softmax is compiled in; otherwise only the
 // masked path (two paths in one kernel would not fit the register file).
+// QK8: q and k are fp8 e4m3 (their scales folded into p.scale_log2).
 template <int D, int WAVES, int RB, int BN, bool DENSE, bool RASTER, bool LSE_ONLY = false,
-          bool PAD = false, bool PLANE = false, bool FULL = false>
+          bool PAD = false, bool PLANE = false, bool FULL = false, bool QK8 = false>
 __global__ void __launch_bounds__(WAVES * 64, (WAVES <= 4 ? 2 : 1))
 attn_bf16_kernel(const AttnParams p) {
-  using C = Bf16Cfg<D, WAVES, RB, BN>;
+  using C = Bf16Cfg<D, WAVES, RB, BN, QK8>;
+  using KG = typename C::KGeom;
   // K and V buffers of two chunks. They are separate objects and the loop
   // selects them statically, so the compiler can tell the chunk being read
   // apart from the one the LDS DMA is filling and does not wait for the
   // prefetch before reading.
-  __shared__ __attribute__((aligned(1024))) char kb0[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char kb0[KG::kChunkBytes];
   __shared__ __attribute__((aligned(1024))) char vb0[C::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char kb1[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char kb1[KG::kChunkBytes];
   __shared__ __attribute__((aligned(1024))) char vb1[C::kChunkBytes];
   // Raster offsets of one window run (RASTER only), sized at launch.
   extern __shared__ int rtab[];
@@ -403,8 +439,9 @@ attn_bf16_kernel(const AttnParams p) {
   const int task = logical_task(p);
   if (task >= p.n_tasks) return;
   const Task t = decode_task<C::kRows>(p, task, D);
-  const bf16_t* qg = static_cast<const bf16_t*>(p.q) + t.head_base;
-  const bf16_t* kg = static_cast<const bf16_t*>(p.k) + t.head_base;
+  constexpr int kQkBytes = QK8 ? 1 : 2;   // bytes per element of q and k
+  const char* qg = static_cast<const char*>(p.q) + t.head_base * kQkBytes;
+  const char* kg = static_cast<const char*>(p.k) + t.head_base * kQkBytes;
   const bf16_t* vg = static_cast<const bf16_t*>(p.v) + t.head_base;
   bf16_t* og = static_cast<bf16_t*>(p.out) + t.head_base;
 
@@ -416,8 +453,10 @@ attn_bf16_kernel(const AttnParams p) {
   // Plane chunks: raster rows by arithmetic (no table); else the table.
   constexpr bool plane = RASTER && PLANE && BN == 64;
   int lane_row[(C::kBlocks + WAVES - 1) / WAVES];
+  int lane_row_k[(KG::kBlocks + WAVES - 1) / WAVES];   // fp8 K rows (QK8 only)
   if constexpr (plane) {
     plane_lane_rows<C, WAVES>(p, wave, lane, lane_row);
+    if constexpr (QK8) plane_lane_rows<KG, WAVES>(p, wave, lane, lane_row_k);
   } else if (RASTER) {
     for (int e = threadIdx.x; e < walk.run_len; e += C::kThreads) rtab[e] = run_offset_raster(p, e);
     __syncthreads();
@@ -425,18 +464,21 @@ attn_bf16_kernel(const AttnParams p) {
   auto dma = [&](int it, char* kdst, char* vdst) __attribute__((always_inline)) {
     if constexpr (plane) {
       const int row0 = walk.at_plane(p, it);
-      load_rows_plane<C, WAVES>(kg, row0, lane_row, kdst, wave, lane);
+      if constexpr (QK8)
+        load_rows_plane<KG, WAVES>(kg, row0, lane_row_k, kdst, wave, lane);
+      else
+        load_rows_plane<C, WAVES>(kg, row0, lane_row, kdst, wave, lane);
       if (!LSE_ONLY) load_rows_plane<C, WAVES>(vg, row0, lane_row, vdst, wave, lane);
     } else if (RASTER) {
       int base, c0, nv;
       walk.at_raster(p, it, &base, &c0, &nv);
       const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
-      load_rows<C, WAVES>(kg, base, nv, kdst, wave, lane, rtab + c0, real);
+      load_rows<KG, WAVES>(kg, base, nv, kdst, wave, lane, rtab + c0, real);
       if (!LSE_ONLY) load_rows<C, WAVES>(vg, base, nv, vdst, wave, lane, rtab + c0, real);
     } else {
       int row0, nv;
       walk.at(it, &row0, &nv);
-      load_rows<C, WAVES>(kg, row0, nv, kdst, wave, lane);
+      load_rows<KG, WAVES>(kg, row0, nv, kdst, wave, lane);
       if (!LSE_ONLY) load_rows<C, WAVES>(vg, row0, nv, vdst, wave, lane);
     }
   };
@@ -481,7 +523,8 @@ attn_bf16_kernel(const AttnParams p) {
         }
         asm volatile("" : "+v"(lc[rb]));
       }
-      sched_qk_softmax<RB, C::kKT, C::kDK, plane ? 1 : 2>();
+      // fp8: one MFMA per tile and row block, twice as long as a bf16 one.
+      sched_qk_softmax<RB, C::kKT, C::kDK, (plane ? 1 : 2) * (QK8 ? 2 : 1), QK8 ? 2 : 1>();
       __builtin_amdgcn_sched_barrier(0);
       if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
       bool grow = false;
@@ -520,7 +563,7 @@ attn_bf16_kernel(const AttnParams p) {
     } else {
       // Chunks that may hold masked keys (a ragged run end, padding positions).
       qk_chunk<C, RB>(w, kcur, l16, g);
-      sched_reads_ahead<RB, C::kKT * C::kDK, 1, kReadAhead>();
+      sched_reads_ahead<RB, C::kKT * C::kDK, QK8 ? 2 : 1, kReadAhead>();
       __builtin_amdgcn_sched_barrier(0);
       // The next chunk's loads go out after QK^T, so their LDS writes land
       // during the softmax (few LDS reads) rather than beside the K reads
@@ -700,12 +743,23 @@ unsigned raster_table_bytes(const AttnProblem& pr) {
 }
 
 // FULL implies !PAD; plane chunks imply FULL (whole 64-key chunks per tile).
-template <int D, int WAVES, int RB, int BN, bool PAD, bool FULL>
+// QK8 (fp8 q and k) has no log-sum-exp-only form; the host never asks for one.
+template <int D, int WAVES, int RB, int BN, bool PAD, bool FULL, bool QK8>
 void launch_sparse(const AttnProblem& pr, const AttnParams& p, unsigned grid, unsigned table,
                    hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
   const bool plane = FULL && BN == 64 && p.plane_cpt > 0;
-  if (pr.lse_only) {
+  if constexpr (QK8) {
+    if (pr.raster && plane)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, false, false, true, true, true>),
+                         dim3(grid), dim3(C::kThreads), 0, stream, p);
+    else if (pr.raster)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, false, PAD, false, FULL, true>),
+                         dim3(grid), dim3(C::kThreads), table, stream, p);
+    else
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false, false, PAD, false, FULL, true>),
+                         dim3(grid), dim3(C::kThreads), 0, stream, p);
+  } else if (pr.lse_only) {
     if constexpr (FULL) {
       if (pr.raster && plane) {
         hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, true, false, true, true>),
@@ -745,7 +799,7 @@ bool chunks_full(const AttnProblem& pr, int bn) {
   return true;
 }
 
-template <int D, int WAVES, int RB, int BN>
+template <int D, int WAVES, int RB, int BN, bool QK8>
 int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
   AttnParams p;
@@ -754,6 +808,16 @@ int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
   // plane chunks address K/V by arithmetic and need no offset table
   const bool full = chunks_full(pr, BN);
   const unsigned table = (full && BN == 64 && p.plane_cpt > 0) ? 0 : raster_table_bytes(pr);
+  if constexpr (QK8) {
+    if (pr.dense || pr.lse_only) return STA_ERR_UNSUPPORTED;
+    if (pr.g.padded)
+      launch_sparse<D, WAVES, RB, BN, true, false, true>(pr, p, grid, table, stream);
+    else if (full)
+      launch_sparse<D, WAVES, RB, BN, false, true, true>(pr, p, grid, table, stream);
+    else
+      launch_sparse<D, WAVES, RB, BN, false, false, true>(pr, p, grid, table, stream);
+    return (int)hipGetLastError();
+  }
   if (pr.dense) {
     if (pr.lse_only && full)
       hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false, true, false, false, true>),
@@ -768,11 +832,11 @@ int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
       hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false>), dim3(grid),
                          dim3(C::kThreads), 0, stream, p);
   } else if (pr.g.padded) {
-    launch_sparse<D, WAVES, RB, BN, true, false>(pr, p, grid, table, stream);
+    launch_sparse<D, WAVES, RB, BN, true, false, false>(pr, p, grid, table, stream);
   } else if (full) {
-    launch_sparse<D, WAVES, RB, BN, false, true>(pr, p, grid, table, stream);
+    launch_sparse<D, WAVES, RB, BN, false, true, false>(pr, p, grid, table, stream);
   } else {
-    launch_sparse<D, WAVES, RB, BN, false, false>(pr, p, grid, table, stream);
+    launch_sparse<D, WAVES, RB, BN, false, false, false>(pr, p, grid, table, stream);
   }
   return (int)hipGetLastError();
 }
@@ -790,7 +854,7 @@ int launch_f32(const AttnProblem& pr, hipStream_t stream) {
 }
 
 // Rows per bf16 work item: a whole 384-token tile when it fits, else 64 or 128.
-template <int D>
+template <int D, bool QK8 = false>
 int dispatch_bf16(const AttnProblem& pr, hipStream_t stream) {
   const int unit_rows = pr.dense ? pr.g.S : pr.g.tau;
 #ifndef STA_CFG_WAVES
@@ -803,9 +867,10 @@ int dispatch_bf16(const AttnProblem& pr, hipStream_t stream) {
 #define STA_CFG_BN 64
 #endif
   constexpr int kBigRows = STA_CFG_WAVES * 16 * STA_CFG_RB;
-  if (unit_rows % kBigRows == 0) return launch_bf16<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN>(pr, stream);
-  if (unit_rows <= 64) return launch_bf16<D, 4, 1, 64>(pr, stream);
-  return launch_bf16<D, 4, 2, 64>(pr, stream);
+  if (unit_rows % kBigRows == 0)
+    return launch_bf16<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN, QK8>(pr, stream);
+  if (unit_rows <= 64) return launch_bf16<D, 4, 1, 64, QK8>(pr, stream);
+  return launch_bf16<D, 4, 2, 64, QK8>(pr, stream);
 }
 
 }  // namespace
@@ -815,6 +880,10 @@ int launch_attention(const AttnProblem& pr, void* stream_ptr) {
   const long long units = pr.dense ? 1 : pr.g.n_tiles;
   const long long tasks_upper = (long long)pr.B * pr.heads * units * (pr.dense ? pr.g.S : pr.g.tau);
   if (tasks_upper > (1LL << 31) - 1) return (int)hipErrorInvalidValue;
+  if (pr.qk_fp8) {
+    if (pr.dtype == STA_BF16 && pr.head_dim == 128) return dispatch_bf16<128, true>(pr, stream);
+    return STA_ERR_UNSUPPORTED;
+  }
   if (pr.dtype == STA_BF16) {
     if (pr.head_dim == 128) return dispatch_bf16<128>(pr, stream);
     if (pr.head_dim == 64) return dispatch_bf16<64>(pr, stream);

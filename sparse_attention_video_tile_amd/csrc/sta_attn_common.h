@@ -9,6 +9,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "sta_kernels.h"
 
 namespace sta {
@@ -19,6 +21,8 @@ typedef bf16_t bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16_t bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16_t bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -269,14 +273,20 @@ __device__ __forceinline__ float wave_xor_sum(float x, int mask) {
 // bf16 kernel
 // ---------------------------------------------------------------------------
 
-template <int D, int WAVES, int RB, int BN>
+// QK8: Q and K are fp8 (OCP e4m3), one byte an element; S^T = K Q^T then
+// takes one v_mfma_f32_16x16x128_f8f6f4 per 128 dimensions, and V, P and O
+// stay bf16. KGeom is the K buffer's geometry (its rows are half as long).
+template <int D, int WAVES, int RB, int BN, bool QK8 = false>
 struct Bf16Cfg {
   static constexpr int kD = D;
   static constexpr int kBN = BN;
   static constexpr int kThreads = WAVES * 64;
   static constexpr int kRowsWave = 16 * RB;
   static constexpr int kRows = WAVES * kRowsWave;
-  static constexpr int kDK = D / 32;            // k-steps of S^T = K Q^T
+  static constexpr bool kQK8 = QK8;
+  static constexpr int kDK = QK8 ? D / 128 : D / 32;   // k-steps of S^T = K Q^T
+  static constexpr int kKOffs = QK8 ? 2 * kDK : kDK;    // 16-byte K reads per score tile
+  using QFrag = typename std::conditional<QK8, i32x8, bf16x8>::type;
   static constexpr int kDB = D / 16;            // 16-row blocks of O^T
   static constexpr int kKT = BN / 16;           // 16-key score tiles per chunk
   static constexpr int kKP = BN / 32;           // 32-key steps of O^T += V^T P^T
@@ -286,6 +296,14 @@ struct Bf16Cfg {
   static constexpr int kBlocks = kChunkBytes / 1024;       // 1 KB LDS-DMA blocks per chunk
   static constexpr int kRowsPerBlock = 1024 / kRowBytes;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert(!QK8 || D % 128 == 0, "fp8 scores need whole 128-dim steps");
+  struct KGeom {
+    static constexpr int kRowBytes = QK8 ? D : 2 * D;
+    static constexpr int kCPR = kRowBytes / 16;
+    static constexpr int kChunkBytes = BN * kRowBytes;
+    static constexpr int kBlocks = kChunkBytes / 1024;
+    static constexpr int kRowsPerBlock = 1024 / kRowBytes;
+  };
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -332,7 +350,7 @@ __device__ __forceinline__ int swz(int row, int c) {
 // clear are padding positions: they load row kv_row0 instead (the run's first
 // key, always a token) and are masked later.
 template <class C, int WAVES>
-__device__ __forceinline__ void load_rows(const bf16_t* src, int kv_row0, int nvalid, char* buf,
+__device__ __forceinline__ void load_rows(const void* src, int kv_row0, int nvalid, char* buf,
                                           int wave, int lane, const int* rtab = nullptr,
                                           unsigned long long real = ~0ull) {
   constexpr int kIter = (C::kBlocks + WAVES - 1) / WAVES;
@@ -349,7 +367,8 @@ __device__ __forceinline__ void load_rows(const bf16_t* src, int kv_row0, int nv
     const int key = min(row, nvalid - 1);
     int rel = rtab ? rtab[key] : key;
     if (!((real >> key) & 1ull)) rel = 0;
-    lds_dma<16>(src + (long long)__builtin_amdgcn_readfirstlane(kv_row0) * (C::kRowBytes / 2),
+    lds_dma<16>(static_cast<const char*>(src) +
+                    (long long)__builtin_amdgcn_readfirstlane(kv_row0) * C::kRowBytes,
                 rel * C::kRowBytes + c * 16, buf + blk * 1024);
   }
 }
@@ -373,7 +392,7 @@ __device__ __forceinline__ void plane_lane_rows(const AttnParams& p, int wave, i
 }
 
 template <class C, int WAVES>
-__device__ __forceinline__ void load_rows_plane(const bf16_t* src, int chunk_row0,
+__device__ __forceinline__ void load_rows_plane(const void* src, int chunk_row0,
                                                 const int (&lane_row)[(C::kBlocks + WAVES - 1) / WAVES],
                                                 char* buf, int wave, int lane) {
   constexpr int kIter = (C::kBlocks + WAVES - 1) / WAVES;
@@ -384,7 +403,8 @@ __device__ __forceinline__ void load_rows_plane(const bf16_t* src, int chunk_row
     const int row = blk * C::kRowsPerBlock + lane / C::kCPR;
     const int pos = lane % C::kCPR;
     const int c = pos ^ ((swz<C::kCPR>(row, 0) >> 4) & (C::kCPR - 1));
-    lds_dma<16>(src + (long long)__builtin_amdgcn_readfirstlane(chunk_row0) * (C::kRowBytes / 2),
+    lds_dma<16>(static_cast<const char*>(src) +
+                    (long long)__builtin_amdgcn_readfirstlane(chunk_row0) * C::kRowBytes,
                 lane_row[b] * C::kRowBytes + c * 16, buf + blk * 1024);
   }
 }

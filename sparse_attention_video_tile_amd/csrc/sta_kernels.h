@@ -27,6 +27,7 @@ struct AttnProblem {
   bool dense;      // true: every query attends to all S keys
   bool raster;     // STA only: q, k, v, out in raster order (else tile-major)
   bool lse_only;   // write lse only (out and v are not touched)
+  bool qk_fp8;     // q and k are fp8 e4m3 (v and out keep dtype, which is bf16)
   Geometry g;      // for dense problems only g.S is used
   // Window per head in tiles (sparse problems only).
   uint16_t omega[STA_MAX_HEADS][3];

@@ -86,3 +86,16 @@ def assert_grad_close(got, ref, dtype: str, what: str = ""):
         assert e["rel_l2"] <= GRAD_F32_REL_L2, (what, e)
         assert e["max_abs_rel_to_max"] <= GRAD_F32_MAX_REL, (what, e)
     return e
+
+
+# fp8 inputs (OCP E4M3 codes for q and k). The caller quantizes; here torch's
+# own cast does it, after dividing by a power-of-two descale chosen so the
+# largest magnitude stays below the format's 448 (no overflow to NaN).
+def e4m3_descale(x: np.ndarray) -> float:
+    amax = float(np.abs(np.asarray(x, dtype=np.float64)).max())
+    return 2.0 ** math.ceil(math.log2(max(amax, 1e-30) / 448.0))
+
+
+def e4m3_codes(x: np.ndarray, descale: float) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.float64) / descale))
+    return t.to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()

@@ -1,0 +1,154 @@
+"""GPU: STA forward with fp8 (OCP E4M3) queries and keys against the float64
+oracle on the same codes, in both token orders, on small seeded workloads
+(several tiles, ragged runs, a padded tile grid, per-head windows) and on
+sampled rows of the 30x48x80 workload in the launch configuration of the
+raster-order kernel; plus agreement with the bf16 kernel on the decoded values
+(every E4M3 value times a power-of-two descale is a bf16 value)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_video_tile_amd import binding, workloads
+from tests.parity_util import (assert_close, default_scale, e4m3_codes, e4m3_descale, errors,
+                               to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, volume, tile, windows per head
+    ("hunyuan_tiles_2x2x3", (12, 16, 24), (6, 8, 8), [(6, 8, 8), (12, 16, 24), (6, 16, 8)]),
+    ("tile64_3x4x4_w333", (12, 16, 16), (4, 4, 4), [(12, 12, 12), (4, 4, 4)]),
+    ("tile48_ragged_runs", (9, 8, 12), (3, 4, 4), [(6, 4, 8), (9, 8, 12)]),
+    ("tile128", (8, 8, 16), (4, 4, 8), [(4, 8, 8), (8, 4, 16)]),
+    ("tile8_tiny", (4, 4, 6), (2, 2, 2), [(2, 2, 2), (4, 4, 6), (4, 2, 4)]),
+    ("one_tile_volume", (6, 8, 8), (6, 8, 8), [(6, 8, 8)]),
+    ("image_2d_tile8x8", (1, 32, 48), (1, 8, 8), [(1, 24, 24), (1, 32, 48), (1, 8, 16)]),
+    ("padded_tile96", (7, 12, 20), (3, 4, 8), [(6, 8, 16), (9, 12, 24)]),
+    ("padded_tile384", (13, 17, 19), (6, 8, 8), [(18, 24, 24)]),
+]
+
+
+def fp8_inputs(inp):
+    qd, kd = e4m3_descale(inp.q), e4m3_descale(inp.k)
+    return e4m3_codes(inp.q, qd), e4m3_codes(inp.k, kd), qd, kd
+
+
+def run_fp8(w, inp, q8, k8, qd, kd, order):
+    """fp8 forward through the C ABI -> raster numpy output."""
+    v = inp.v
+    if order == "tile_major":
+        q8, k8 = (oracle.to_tile_major(x, w.tile) for x in (q8, k8))
+        v = oracle.to_tile_major(v, w.tile)
+    q8g, k8g = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (q8, k8))
+    vg = to_gpu(v, "bf16")
+    vol = w.volume if order == "tile_major" else None
+    out = binding.sta_forward_fp8(q8g, k8g, vg, w.tile, inp.windows, qd, kd, volume=vol)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    if order == "tile_major":
+        got = oracle.from_tile_major(got, w.volume, w.tile)
+    return got
+
+
+@pytest.mark.parametrize("order", ["raster", "tile_major"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_fp8_forward_matches_oracle(case, order):
+    name, volume, tile, windows = case
+    w = workloads.small_case(volume, tile, windows, head_dim=128, dtype="bf16", seed=17, name=name)
+    print(f"[case] fp8 forward {order} {w}", flush=True)
+    inp = workloads.make_inputs(w)
+    q8, k8, qd, kd = fp8_inputs(inp)
+    got = run_fp8(w, inp, q8, k8, qd, kd, order)
+    ref = oracle.sta_attention_fp8(q8, k8, inp.v, tile, inp.windows, default_scale(128), qd, kd)
+    assert_close(got, ref, "bf16", f"fp8 {name} {order}")
+
+
+@pytest.mark.parametrize("case", CASES[:3], ids=lambda c: c[0])
+def test_fp8_kernel_agrees_with_bf16_kernel_on_decoded_values(case):
+    """Both kernels form exact products of the same values and sum them in
+    float32; only the summation order and the rounding of a few probabilities
+    to bf16 may differ."""
+    name, volume, tile, windows = case
+    w = workloads.small_case(volume, tile, windows, head_dim=128, dtype="bf16", seed=23, name=name)
+    print(f"[case] fp8 vs bf16 kernel {w}", flush=True)
+    inp = workloads.make_inputs(w)
+    q8, k8, qd, kd = fp8_inputs(inp)
+    got = run_fp8(w, inp, q8, k8, qd, kd, "raster")
+    qb = to_gpu(oracle.e4m3_decode(q8) * qd, "bf16")
+    kb = to_gpu(oracle.e4m3_decode(k8) * kd, "bf16")
+    out = binding.sliding_tile_attention(qb, kb, to_gpu(inp.v, "bf16"), tile, inp.windows)
+    torch.cuda.synchronize()
+    e = errors(got, out.float().cpu().numpy())
+    print(f"[parity] fp8 vs bf16 kernel {name} {e}", flush=True)
+    assert e["rel_l2"] <= 2e-3 and e["max_abs"] <= 1e-2, e
+
+
+def test_fp8_large_scores_stay_stable():
+    """Scores far from zero (the reference max moves often): the kernel keeps
+    the same softmax as the oracle."""
+    w = workloads.small_case((12, 16, 24), (6, 8, 8), [(6, 16, 16), (12, 16, 24)], head_dim=128,
+                             dtype="bf16", seed=29, name="fp8_large")
+    inp = workloads.make_inputs(w)
+    q8, k8, qd, kd = fp8_inputs(inp)
+    scale = 4.0
+    print(f"[case] fp8 large scores scale={scale}", flush=True)
+    q8g, k8g = (torch.from_numpy(x).cuda() for x in (q8, k8))
+    out = binding.sta_forward_fp8(q8g, k8g, to_gpu(inp.v, "bf16"), w.tile, inp.windows, qd, kd,
+                                  scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.sta_attention_fp8(q8, k8, inp.v, w.tile, inp.windows, scale, qd, kd)
+    assert_close(out.float().cpu().numpy(), ref, "bf16", "fp8 large scores")
+
+
+def test_fp8_full_size_sampled_rows():
+    w = workloads.STA_18_24_24
+    print(f"[case] fp8 full size {w.name}: generating inputs", flush=True)
+    inp = workloads.make_inputs(w)
+    q8, k8, qd, kd = fp8_inputs(inp)
+    q8g, k8g = (torch.from_numpy(x).cuda() for x in (q8, k8))
+    print(f"[case] fp8 full size {w.name}: running the raster kernel", flush=True)
+    out = binding.sta_forward_fp8(q8g, k8g, to_gpu(inp.v, "bf16"), w.tile, inp.windows, qd, kd)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().reshape(w.B, w.heads, -1, w.head_dim)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(w.seed)
+    n = oracle.tile_grid(w.volume, w.tile)
+    n_tiles = n[0] * n[1] * n[2]
+    interior = ((n[0] // 2) * n[1] + n[1] // 2) * n[2] + n[2] // 2
+    tiles = sorted({0, n_tiles - 1, interior, int(rng.integers(0, n_tiles))})
+    gots, refs = [], []
+    for h in sorted({0, w.heads - 1, int(rng.integers(0, w.heads))}):
+        rows = np.concatenate([rng.choice(oracle.tile_tokens(w.volume, w.tile, t), 8, replace=False)
+                               for t in tiles])
+        window = tuple(int(x) for x in inp.windows[h])
+        ref = oracle.sta_attention_fp8_rows(q8, k8, inp.v, w.tile, window, default_scale(128),
+                                            qd, kd, 0, h, rows)
+        gots.append(got[0, h, rows])
+        refs.append(ref)
+    assert_close(np.concatenate(gots), np.concatenate(refs), "bf16", "fp8 full size samples")
+
+
+def test_fp8_invalid_inputs_raise():
+    w = workloads.small_case((4, 8, 8), (2, 4, 4), [(4, 8, 8)], head_dim=128, dtype="bf16", seed=1,
+                             name="fp8_args")
+    inp = workloads.make_inputs(w)
+    q8, k8, qd, kd = fp8_inputs(inp)
+    q8g, k8g = (torch.from_numpy(x).cuda() for x in (q8, k8))
+    v = to_gpu(inp.v, "bf16")
+    for bad in (0.0, -1.0, math.inf, math.nan):
+        with pytest.raises(ValueError):
+            binding.sta_forward_fp8(q8g, k8g, v, w.tile, inp.windows, bad, kd)
+    w64 = workloads.small_case((4, 8, 8), (2, 4, 4), [(4, 8, 8)], head_dim=64, dtype="bf16", seed=1,
+                               name="fp8_d64")
+    i64 = workloads.make_inputs(w64)
+    with pytest.raises(Exception):
+        binding.sta_forward_fp8(torch.zeros(i64.q.shape, dtype=torch.uint8, device="cuda"),
+                                torch.zeros(i64.q.shape, dtype=torch.uint8, device="cuda"),
+                                to_gpu(i64.v, "bf16"), w64.tile, i64.windows, 1.0, 1.0)
+    with pytest.raises(TypeError):
+        binding.sta_forward_fp8(q8g.float(), k8g, v, w.tile, inp.windows, qd, kd)
+    torch.cuda.synchronize()
