@@ -20,6 +20,9 @@ Printed as one JSON line. Besides the contract fields it carries
                 permutation kernels' achieved HBM bandwidth;
   backward      sta_forward_lse + sta_backward at the same shape;
   recall        sta_window_recall over five candidate windows at the same shape;
+  fp8_qk        sta_forward_fp8 (e4m3 q and k, bf16 v) at the same shape, against
+                the mixed peak of its two products (QK^T at the fp8 MFMA peak,
+                PV at the bf16 one);
   other_workloads  the fused kernel on the other named workloads.
 """
 
@@ -39,6 +42,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
+# Half the counted work (QK^T) at the fp8 peak, half (PV) at the bf16 peak.
+FP8_QK_PEAK_TFLOPS = 1.0 / (0.5 / FP8_PEAK_TFLOPS + 0.5 / BF16_PEAK_TFLOPS)
 F32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector, published
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 METRIC = "STA fwd effective TFLOP/s + MFMA util, 30x48x80 latent, w=(18,24,24), 1 GPU"
@@ -178,6 +184,30 @@ def time_recall(w, args, torch, binding, workloads, q, k, stream, ev):
             "candidates": cands, "mean_recall_on_iid_inputs": mean}
 
 
+def time_fp8(w, args, torch, binding, q, k, v, out, windows, flops, stream, ev):
+    """sta_forward_fp8 on the headline raster tensors: q and k quantized to
+    e4m3 with power-of-two per-tensor descales before the timed region."""
+    codes = []
+    for x in (q, k):
+        amax = float(x.float().abs().max())
+        descale = 2.0 ** math.ceil(math.log2(max(amax, 1e-30) / 448.0))
+        codes.append(((x.float() / descale).to(torch.float8_e4m3fn).view(torch.uint8), descale))
+    (q8, qd), (k8, kd) = codes
+    binding.sta_forward_fp8(q8, k8, v, w.tile, windows, qd, kd, out=out)  # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(args.fp8_reps):
+        binding.sta_forward_fp8(q8, k8, v, w.tile, windows, qd, kd, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.fp8_reps
+    tf = flops / (ms * 1e-3) / 1e12
+    del q8, k8
+    return {"ms": ms, "tflops": tf, "peak": FP8_QK_PEAK_TFLOPS, "frac_of_peak": tf / FP8_QK_PEAK_TFLOPS,
+            "frac_of_bf16_peak": tf / BF16_PEAK_TFLOPS, "kernel": "attn_bf16_kernel, QK8 (raster order)"}
+
+
 def other_workloads(main_w, args, torch, binding, workloads, q, k, v, out, stream, ev):
     """The fused kernel on every other named workload: average launch time,
     effective TFLOP/s and fraction of peak. Workloads of the headline shape
@@ -232,6 +262,8 @@ def main(argv=None):
                     help="STA backward launches to time at the headline workload (0: skip)")
     ap.add_argument("--recall-reps", type=int, default=2,
                     help="window-recall scoring runs to time at the headline shape (0: skip)")
+    ap.add_argument("--fp8-reps", type=int, default=3,
+                    help="sta_forward_fp8 launches to time (0: skip)")
     ap.add_argument("--config-reps", type=int, default=3,
                     help="launches per other named workload to time (0: skip)")
     ap.add_argument("--copy-reference", action="store_true",
@@ -360,6 +392,10 @@ def main(argv=None):
     if args.recall_reps > 0 and fused:
         recall = time_recall(w, args, torch, binding, workloads, q, k, stream, ev)
 
+    fp8 = None
+    if args.fp8_reps > 0 and fused and w.dtype == "bf16" and w.head_dim == 128:
+        fp8 = time_fp8(w, args, torch, binding, q, k, v, out, windows, flops, stream, ev)
+
     others = None
     if args.config_reps > 0:
         others = other_workloads(w, args, torch, binding, workloads, q, k, v, out, stream, ev)
@@ -404,6 +440,7 @@ def main(argv=None):
         "three_call": three,
         "backward": backward,
         "recall": recall,
+        "fp8_qk": fp8,
         "other_workloads": others,
     }
     print(json.dumps(result), flush=True)

@@ -81,16 +81,19 @@ def role(name: str) -> str:
         return "STA backward, D = rowsum(dO * O)"
     if "attn_bf16_kernel" in name:
         a = _targs(name)
-        # <D, WAVES, RB, BN, DENSE, RASTER, LSE_ONLY, PAD, PLANE>
+        # <D, WAVES, RB, BN, DENSE, RASTER, LSE_ONLY, PAD, PLANE, FULL, QK8>
         dense, raster = a[4] == "true", a[5] == "true"
         lse_only = len(a) > 6 and a[6] == "true"
         pad = len(a) > 7 and a[7] == "true"
+        qk8 = len(a) > 10 and a[10] == "true"
         what = "dense comparator" if dense else (
             "STA forward, raster order (fused path)" if raster else "STA forward, tile-major (three-call path)")
         if lse_only:
             what += ", log-sum-exp only (recall)"
         if pad:
             what += ", padded grid"
+        if qk8:
+            what += ", fp8 q and k"
         return what
     if "attn_f32_kernel" in name:
         return "STA forward, float32"
@@ -146,7 +149,8 @@ def main(argv=None) -> int:
          "bench.py defaults: 3 warm-up + 20 timed steps of the fused path (one raster-order STA launch), "
          "then 1 + 3 steps of the three-call path (reorder q, k, v; tile-major STA; restore), "
          "1 + 2 dense-comparator launches, 1 + 3 forward-with-lse and backward passes at the same "
-         "shape, then 1 + 3 launches on each other named workload (the same kernels).\n",
+         "shape, 1 + 2 window-recall passes, 1 + 3 launches of the fp8 q/k forward, then 1 + 3 "
+         "launches on each other named workload (the same kernels).\n",
          "| kernel | role | calls | average (ms) | min (ms) | max (ms) | share |",
          "|---|---|---|---|---|---|---|"]
     for r in rows:
@@ -160,11 +164,12 @@ def main(argv=None) -> int:
     timed = None
     tpath = os.path.join(run, "trace", "bench_kernel_trace.csv")
     if os.path.exists(tpath):
-        want = "true>" if cfg.get("path", "fused") == "fused" else "false, false>"
+        fused = cfg.get("path", "fused") == "fused"
         disp = sorted((int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
                       for r in csv.DictReader(open(tpath))
-                      if "attn_bf16_kernel" in r["Kernel_Name"] and want in r["Kernel_Name"]
-                      and "true, false>" not in r["Kernel_Name"])
+                      if "attn_bf16_kernel" in r["Kernel_Name"] and (
+                          is_headline(r["Kernel_Name"]) if fused else
+                          role(r["Kernel_Name"]) == "STA forward, tile-major (three-call path)"))
         w0, ns = bench["warmup"], bench["steps"]
         if len(disp) >= w0 + ns:
             sel = [d for _, d in disp[w0:w0 + ns]]
@@ -231,6 +236,8 @@ def main(argv=None) -> int:
         r = role(n)
         if "reorder" in n:
             alg = f"{tensor / 1e9:.3f} + {tensor / 1e9:.3f}"
+        elif r.endswith("fp8 q and k"):   # q and k at one byte an element
+            alg = f"{2 * tensor / 1e9:.3f} + {tensor / 1e9:.3f}"
         elif r.startswith(("STA forward, raster", "STA forward, tile-major", "dense comparator")) and "only" not in r:
             alg = f"{3 * tensor / 1e9:.3f} + {tensor / 1e9:.3f}"
         else:
