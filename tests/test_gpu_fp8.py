@@ -104,6 +104,55 @@ def test_fp8_large_scores_stay_stable():
     assert_close(out.float().cpu().numpy(), ref, "bf16", "fp8 large scores")
 
 
+def _tile_grid(volume, tile):
+    """Tile coordinates (t, h, w) of every raster token, each (T, H, W)."""
+    t, h, w = np.meshgrid(*(np.arange(n) // c for n, c in zip(volume, tile)), indexing="ij")
+    return t, h, w
+
+
+@pytest.mark.parametrize("order", ["raster", "tile_major"])
+def test_fp8_key_scales_jumping_between_tiles(order):
+    """Key magnitudes that change by up to 13x from tile to tile (full 64-key
+    chunks, so the kernel that moves its reference max only on a lane-sum
+    test): scores jump far past the lazy bound in both directions."""
+    w = workloads.small_case((12, 16, 16), (4, 4, 4), [(8, 8, 8), (12, 16, 16)], head_dim=128,
+                             dtype="bf16", seed=17, name="fp8_key_scale_jumps")
+    print(f"[case] fp8 {w.name} {order}", flush=True)
+    inp = workloads.make_inputs(w)
+    t, h, x = _tile_grid(w.volume, w.tile)
+    inp.k = inp.k * (1.0 + 3.0 * ((t * 7 + h * 3 + x) % 5))[None, None, :, :, :, None]
+    q8, k8, qd, kd = fp8_inputs(inp)
+    got = run_fp8(w, inp, q8, k8, qd, kd, order)
+    ref = oracle.sta_attention_fp8(q8, k8, inp.v, w.tile, inp.windows, default_scale(128), qd, kd)
+    assert np.isfinite(got).all()
+    assert_close(got, ref, "bf16", f"{w.name} {order}")
+
+
+@pytest.mark.parametrize("order", ["raster", "tile_major"])
+def test_fp8_many_moderate_scores_move_the_reference_max(order):
+    """Half the key tiles score about 5 (log2 units) above the others: single
+    probabilities stay near 2^5, but lane sums of 16 of them pass 2^8, so the
+    rescale has to come from the sum test."""
+    d = 128
+    w = workloads.small_case((8, 16, 16), (4, 4, 4), [(8, 8, 12)], head_dim=d, dtype="bf16",
+                             seed=23, name="fp8_moderate_scores")
+    print(f"[case] fp8 {w.name} {order}", flush=True)
+    inp = workloads.make_inputs(w)
+    scale = default_scale(d)
+    alpha = 5.0 / (scale * math.log2(math.e))
+    e0 = np.zeros(d, dtype=np.float32)
+    e0[0] = 1.0
+    t, h, x = _tile_grid(w.volume, w.tile)
+    high = ((t + h + x) % 2).astype(np.float32)
+    inp.q = alpha * e0 + 0.05 * inp.q
+    inp.k = high[None, None, :, :, :, None] * e0 + 0.05 * inp.k
+    q8, k8, qd, kd = fp8_inputs(inp)
+    got = run_fp8(w, inp, q8, k8, qd, kd, order)
+    ref = oracle.sta_attention_fp8(q8, k8, inp.v, w.tile, inp.windows, scale, qd, kd)
+    assert np.isfinite(got).all()
+    assert_close(got, ref, "bf16", f"{w.name} {order}")
+
+
 def test_fp8_full_size_sampled_rows():
     w = workloads.STA_18_24_24
     print(f"[case] fp8 full size {w.name}: generating inputs", flush=True)
