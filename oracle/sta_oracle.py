@@ -296,18 +296,6 @@ def full_attention(q, k, v, scale) -> np.ndarray:
     return out.reshape(shape)
 
 
-def full_attention_rows(q, k, v, scale, b: int, h: int, query_rows) -> np.ndarray:
-    """Plain softmax attention for selected query rows; q, k, v: (B, heads, S, d)."""
-    d = q.shape[-1]
-    qf = np.asarray(q[b, h], dtype=np.float64).reshape(-1, d)[np.asarray(query_rows)]
-    kf = np.asarray(k[b, h], dtype=np.float64).reshape(-1, d)
-    vf = np.asarray(v[b, h], dtype=np.float64).reshape(-1, d)
-    s = scale * (qf @ kf.T)
-    m = s.max(axis=1, keepdims=True)
-    p = np.exp(s - m)
-    return (p @ vf) / p.sum(axis=1, keepdims=True)
-
-
 # ----------------------------------------------------------------------------
 # Token order
 # ----------------------------------------------------------------------------

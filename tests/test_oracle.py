@@ -303,10 +303,52 @@ def test_large_logits_stay_finite():
 
 
 def test_rows_match_full_output():
-    w = workloads.TINY_F32
-    inp = workloads.make_inputs(w.with_(heads=1, windows=w.windows[:1]))
+    """The row-subset entry point (used by the sampled full-size checks) picks
+    the right batch entry, head and window: it equals the matching rows of the
+    whole output for every (b, h) of a B = 2, three-head draw with a different
+    window per head."""
+    w = workloads.small_case((6, 8, 12), (2, 4, 4), [(2, 4, 4), (6, 8, 12), (4, 4, 8)],
+                             head_dim=16, dtype="f32", B=2, seed=5, name="rows")
+    inp = workloads.make_inputs(w)
     scale = 1 / math.sqrt(w.head_dim)
     full = oracle.sta_attention(inp.q, inp.k, inp.v, w.tile, inp.windows, scale)
-    rows = np.array([0, 17, 300, 3071])
-    part = oracle.sta_attention_rows(inp.q, inp.k, inp.v, w.tile, tuple(inp.windows[0]), scale, 0, 0, rows)
-    np.testing.assert_allclose(part, full[0, 0].reshape(-1, w.head_dim)[rows], rtol=1e-12, atol=1e-14)
+    rows = np.array([0, 17, 300, 575])
+    for b in range(w.B):
+        for h in range(w.heads):
+            part = oracle.sta_attention_rows(inp.q, inp.k, inp.v, w.tile, tuple(inp.windows[h]),
+                                             scale, b, h, rows)
+            np.testing.assert_allclose(part, full[b, h].reshape(-1, w.head_dim)[rows],
+                                       rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize(
+    "volume,tile,windows",
+    [
+        # the pages' geometry, with the other named windows and an even one
+        ((30, 48, 80), (6, 8, 8), [(18, 24, 24), (30, 40, 40), (30, 24, 24), (12, 16, 16)]),
+        ((12, 16, 16), (4, 4, 4), [(12, 12, 12), (4, 8, 4)]),
+        # a padded tile grid (the volume is not whole tiles)
+        ((5, 6, 7), (2, 4, 4), [(4, 4, 4), (2, 8, 8), (6, 8, 8)]),
+        ((11, 9, 13), (4, 4, 12), [(8, 8, 12), (12, 12, 24)]),
+    ],
+)
+def test_kv_tile_lists_equal_brute_force_listing(volume, tile, windows):
+    """List contents, not only their counts: per head and query tile, the key
+    tiles of the nearest-centre window (brute_start, a definition independent
+    of the oracle's clamp) enumerated by nested loops in raster order of tile
+    coordinates, then -1 fill. A listing taken from the wrong axis of the
+    selection (the transposed relation, which differs under clamping) fails."""
+    lists, counts = oracle.kv_tile_lists(volume, tile, np.array(windows))
+    n = [-(-e // c) for e, c in zip(volume, tile)]
+    assert lists.shape[:2] == (len(windows), n[0] * n[1] * n[2])
+    for h, win in enumerate(windows):
+        om = [win[a] // tile[a] for a in range(3)]
+        for i, qc in enumerate(itertools.product(range(n[0]), range(n[1]), range(n[2]))):
+            st = [brute_start(qc[a], n[a], om[a]) for a in range(3)]
+            want = [(t * n[1] + y) * n[2] + x
+                    for t in range(st[0], st[0] + om[0])
+                    for y in range(st[1], st[1] + om[1])
+                    for x in range(st[2], st[2] + om[2])]
+            assert counts[h, i] == len(want), (h, i)
+            assert list(lists[h, i, :counts[h, i]]) == want, (h, i)
+            assert (lists[h, i, counts[h, i]:] == -1).all()

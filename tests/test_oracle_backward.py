@@ -101,17 +101,22 @@ def test_gradient_invariants(window):
 
 
 def test_row_subsets_match_full_backward():
+    """The row-subset gradients (used by the sampled full-size checks) equal
+    the matching rows of the whole backward for every (b, h) of a B = 2,
+    two-head draw with a different window per head."""
     vol, tile = (6, 4, 6), (2, 2, 2)
-    window = (4, 2, 4)
-    shape = (1, 1) + vol + (8,)
+    windows = [(4, 2, 4), (2, 4, 6)]
+    shape = (2, 2) + vol + (8,)
     q, k, v, dout = draw(shape, 11)
-    dq, dk, dv = oracle.sta_backward(q, k, v, dout, tile, [window], 0.3)
+    dq, dk, dv = oracle.sta_backward(q, k, v, dout, tile, windows, 0.3)
     rows = np.array([0, 5, 17, 40, 77, 143])
-    gq = oracle.sta_backward_query_rows(q, k, v, dout, tile, window, 0.3, 0, 0, rows)
-    gk, gv = oracle.sta_backward_key_rows(q, k, v, dout, tile, window, 0.3, 0, 0, rows)
-    np.testing.assert_allclose(gq, dq.reshape(-1, 8)[rows], rtol=1e-12, atol=1e-13)
-    np.testing.assert_allclose(gk, dk.reshape(-1, 8)[rows], rtol=1e-12, atol=1e-13)
-    np.testing.assert_allclose(gv, dv.reshape(-1, 8)[rows], rtol=1e-12, atol=1e-13)
+    for b in range(2):
+        for h in range(2):
+            gq = oracle.sta_backward_query_rows(q, k, v, dout, tile, windows[h], 0.3, b, h, rows)
+            gk, gv = oracle.sta_backward_key_rows(q, k, v, dout, tile, windows[h], 0.3, b, h, rows)
+            np.testing.assert_allclose(gq, dq[b, h].reshape(-1, 8)[rows], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(gk, dk[b, h].reshape(-1, 8)[rows], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(gv, dv[b, h].reshape(-1, 8)[rows], rtol=1e-12, atol=1e-13)
 
 
 def test_lse_whole_volume_is_library_logsumexp():

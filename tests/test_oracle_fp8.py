@@ -100,3 +100,24 @@ def test_whole_volume_window_equals_library_attention():
     lib = torch.nn.functional.scaled_dot_product_attention(
         qt.reshape(sh), kt.reshape(sh), vt.reshape(sh), scale=s).numpy()
     assert np.allclose(out.reshape(sh), lib, rtol=0, atol=1e-12)
+
+
+def test_row_subsets_match_whole_fp8_output():
+    """The row-subset fp8 entry point (the checker of the sampled full-size
+    fp8 test) slices one (b, h) before decoding; it must give the matching rows
+    of the whole output for every (b, h) of a B = 2, three-head draw with a
+    different window per head, descales included."""
+    w = workloads.small_case((4, 8, 8), (2, 4, 4), [(4, 8, 8), (2, 4, 4), (2, 8, 4)], head_dim=128,
+                             dtype="bf16", B=2, seed=13, name="fp8_rows_pin")
+    inp = workloads.make_inputs(w)
+    qd, kd = e4m3_descale(inp.q), e4m3_descale(inp.k)
+    q8, k8 = e4m3_codes(inp.q, qd), e4m3_codes(inp.k, kd)
+    s = 1.0 / math.sqrt(128)
+    full = oracle.sta_attention_fp8(q8, k8, inp.v, w.tile, inp.windows, s, qd, kd)
+    rows = np.array([0, 9, 63, 130, 255])
+    for b in range(w.B):
+        for h in range(w.heads):
+            part = oracle.sta_attention_fp8_rows(q8, k8, inp.v, w.tile, tuple(inp.windows[h]), s,
+                                                 qd, kd, b, h, rows)
+            np.testing.assert_allclose(part, full[b, h].reshape(-1, 128)[rows], rtol=1e-12,
+                                       atol=1e-14)
