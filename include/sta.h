@@ -96,8 +96,13 @@ int sta_reorder_tiles(const void* x_raster, void* x_tiled, int B, int heads, int
                       int T, int H, int W, const int* tile, int dtype, void* stream);
 
 /*
- * Inverse of sta_reorder_tiles: tile-major back to raster order (bit-exact).
- * Same arguments, with the roles of input and output swapped.
+ * Inverse of sta_reorder_tiles: tile-major back to raster order (bit-exact),
+ * so that the attention output returns to the token order of the model's
+ * other layers (the pages' layout transformation: tokens are grouped into
+ * contiguous tiles for the kernel and grouped back afterwards -- podcast
+ * transcript, the answer on what a tile is; dianyo ICML2025 blog, Sparse
+ * VideoGen, layout transformation). Padding rows of a tile-major input are
+ * skipped. Same arguments, with the roles of input and output swapped.
  */
 int sta_restore_order(const void* x_tiled, void* x_raster, int B, int heads, int head_dim,
                       int T, int H, int W, const int* tile, int dtype, void* stream);
@@ -137,8 +142,22 @@ int sta_q_tiles(int* q_list, int* q_count, int heads, int T, int H, int W, const
                 const int* window, int max_q, void* stream);
 
 /*
+ * Length of the longest tile list, for sizing the list buffers of
+ * sta_kv_tiles (transposed = 0: the largest window, max_h prod_a omega_a) and
+ * sta_q_tiles (transposed = 1: the most query tiles whose windows hold one
+ * key tile). Host only; enqueues nothing. Arguments as sta_kv_tiles. Returns
+ * the length (>= 1) or a negative sta_status.
+ */
+int sta_tile_list_len(int heads, int T, int H, int W, const int* tile, const int* window,
+                      int transposed);
+
+/*
  * Number of computed (query tile, key tile) pairs summed over heads, for one
- * batch entry: sum_h N_t * prod_a omega_a. Host only; enqueues nothing.
+ * batch entry: sum_h N_t * prod_a omega_a. This is the count of dense blocks
+ * that STA computes instead of the N_t^2 blocks of full attention (atlas
+ * summary, "Key results": the 91 % sparsity at w = (18,24,24) is
+ * 1 - 27 / 300 of these pairs), and the effective TFLOP/s of the kernels are
+ * counted from it. Host only; enqueues nothing.
  * Returns a negative sta_status on invalid arguments.
  */
 long long sta_kv_pair_count(int heads, int T, int H, int W, const int* tile, const int* window);
@@ -288,7 +307,12 @@ int sta_window_recall(const void* q, const void* k, float* recall, float* worksp
 int sta_full_attention(const void* q, const void* k, const void* v, void* out, int B, int heads,
                        int head_dim, int S, float scale, int dtype, void* stream);
 
-/* Message for the last non-OK status on this thread ("" if none). */
+/*
+ * Message for the last non-OK status on this thread ("" if none). The pages
+ * describe no interface; this is the error channel of the C boundary through
+ * which the attention of the pages' video models is replaced (podcast
+ * transcript, the opening answers on swapping full 3D attention for STA).
+ */
 const char* sta_last_error(void);
 
 #ifdef __cplusplus

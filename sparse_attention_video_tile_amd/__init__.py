@@ -9,7 +9,6 @@ from .binding import (  # noqa: F401
     StaError,
     last_error,
     load_library,
-    raster_run_fits,
     sliding_tile_attention,
     sta_attention,
     sta_backward,
@@ -23,6 +22,7 @@ from .binding import (  # noqa: F401
     sta_q_tiles,
     sta_reorder_tiles,
     sta_restore_order,
+    sta_tile_list_len,
     sta_window_recall,
     tile_major_rows,
 )

@@ -21,10 +21,8 @@ LIB_PATH = os.path.join(_PKG, "libsta.so")
 STA_OK, STA_ERR_INVALID_ARG, STA_ERR_UNSUPPORTED, STA_ERR_HIP = 0, -1, -2, -3
 STA_BF16, STA_F32 = 0, 1
 STA_MAX_HEADS = 256
-ABI_VERSION = 3
+ABI_VERSION = 4
 STA_TILE_MAJOR, STA_RASTER = 0, 1
-# Longest window run (omega_w * tau keys) sta_forward_raster accepts.
-STA_MAX_RASTER_RUN = 8192
 
 EXPORTS = (
     "sta_abi_version",
@@ -32,6 +30,7 @@ EXPORTS = (
     "sta_restore_order",
     "sta_kv_tiles",
     "sta_q_tiles",
+    "sta_tile_list_len",
     "sta_kv_pair_count",
     "sta_forward",
     "sta_forward_raster",
@@ -91,6 +90,8 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.sta_backward.restype = c_int
     lib.sta_backward.argtypes = [c_void_p] * 10 + [c_int, c_int, c_int, c_int, c_int, c_int, int3,
                                                    int3, c_float, c_int, c_int, c_void_p]
+    lib.sta_tile_list_len.restype = c_int
+    lib.sta_tile_list_len.argtypes = [c_int, c_int, c_int, c_int, int3, int3, c_int]
     lib.sta_kv_pair_count.restype = ctypes.c_longlong
     lib.sta_kv_pair_count.argtypes = [c_int, c_int, c_int, c_int, int3, int3]
     for name in ("sta_forward", "sta_forward_raster"):
@@ -229,22 +230,26 @@ def sta_kv_pair_count(heads: int, volume: Sequence[int], tile: Sequence[int], wi
     return int(n)
 
 
+def sta_tile_list_len(heads: int, volume: Sequence[int], tile: Sequence[int], window,
+                      transposed: bool = False) -> int:
+    """Longest list of sta_kv_tiles (transposed=False) or sta_q_tiles
+    (transposed=True), computed by the library (host only)."""
+    lib = load_library()
+    T, H, W = (int(a) for a in volume)
+    n = lib.sta_tile_list_len(heads, T, H, W, _int_array(tile),
+                              _int_array(_windows_per_head(window, heads)), int(bool(transposed)))
+    if n < 0:
+        _check(int(n), "sta_tile_list_len")
+    return int(n)
+
+
 def _tile_lists(fn_name: str, heads: int, volume, tile, window, max_len, device, transposed: bool):
     lib = load_library()
     T, H, W = (int(a) for a in volume)
     ws = _windows_per_head(window, heads)
-    n = [-(-int(e) // int(c)) for e, c in zip((T, H, W), tile)]
-    n_tiles = n[0] * n[1] * n[2]
+    n_tiles = tile_major_rows(volume, tile) // (int(tile[0]) * int(tile[1]) * int(tile[2]))
     if max_len is None:
-        max_len = 0
-        for h in range(heads):
-            prod = 1
-            for a in range(3):
-                om = ws[3 * h + a] // int(tile[a])
-                if transposed:  # longest interval of query tiles along this axis
-                    om = max(_inverse_len(j, n[a], om) for j in range(n[a])) if n[a] > 0 else 0
-                prod *= om
-            max_len = max(max_len, prod)
+        max_len = sta_tile_list_len(heads, volume, tile, ws, transposed)
     lists = torch.empty((heads, n_tiles, max_len), dtype=torch.int32, device=device)
     counts = torch.empty((heads, n_tiles), dtype=torch.int32, device=device)
     dev = _require_gpu(lists, counts)
@@ -253,18 +258,6 @@ def _tile_lists(fn_name: str, heads: int, volume, tile, window, max_len, device,
                                    _int_array(tile), _int_array(ws), max_len, _stream(dev))
     _check(rc, fn_name)
     return lists, counts
-
-
-def _inverse_len(j: int, n: int, omega: int) -> int:
-    """Number of query tiles along an axis whose window holds key tile j
-    (for sizing only; the library computes the lists)."""
-    if omega <= 0 or omega > n:
-        return 0
-    half = omega // 2
-    hi = n - 1 if j >= n - omega else j + half
-    a = j - omega + 1
-    lo = 0 if a <= 0 else a + half
-    return hi - lo + 1
 
 
 def sta_kv_tiles(heads: int, volume: Sequence[int], tile: Sequence[int], window,
@@ -356,28 +349,6 @@ def sta_forward_raster(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tile: 
                                     _dtype_code(q), _stream(dev))
     _check(rc, "sta_forward_raster")
     return out
-
-
-def raster_run_fits(tile: Sequence[int], window, heads: int, volume: Optional[Sequence[int]] = None,
-                    backward: bool = False) -> bool:
-    """Whether every window run (omega_w * tau keys) -- and, for the backward
-    (which needs the volume), every transposed run -- is within what the
-    raster-order kernels accept, and (when the volume is given) whether one
-    tile-row of frames, c_t * H * W tokens, is within their 32-bit byte
-    addressing of a run."""
-    ws = _windows_per_head(window, heads)
-    tau = int(tile[0]) * int(tile[1]) * int(tile[2])
-    if volume is not None and int(tile[0]) * int(volume[1]) * int(volume[2]) * 256 >= 2 ** 31:
-        return False
-    for h in range(heads):
-        om = ws[3 * h + 2] // int(tile[2])
-        if om * tau > STA_MAX_RASTER_RUN:
-            return False
-        if backward:
-            nw = -(-int(volume[2]) // int(tile[2]))
-            if max(_inverse_len(j, nw, om) for j in range(nw)) * tau > STA_MAX_RASTER_RUN:
-                return False
-    return True
 
 
 def _order_shapes(q: torch.Tensor, volume, tile):
@@ -553,13 +524,18 @@ def sta_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tile: Seque
 def sliding_tile_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tile: Sequence[int],
                            window, scale: Optional[float] = None, fused: bool = True) -> torch.Tensor:
     """The whole path on raster (B, heads, T, H, W, d) tensors. fused=True runs
-    the single raster-order kernel when the windows allow it; otherwise q, k, v
-    are reordered to tile-major, STA forward runs, and the output is restored
-    to raster order. Both give the same values."""
+    the single raster-order kernel; when the library has no raster-order
+    kernel for the request (it refuses with STA_ERR_UNSUPPORTED, e.g. a window
+    run longer than its offset table) or fused=False, q, k, v are reordered to
+    tile-major, STA forward runs, and the output is restored to raster order.
+    Both give the same values."""
     if q.dim() != 6:
         raise ValueError("q, k, v must be (B, heads, T, H, W, d)")
-    if fused and raster_run_fits(tile, window, q.shape[1], q.shape[2:5]):
-        return sta_forward_raster(q, k, v, tile, window, scale)
+    if fused:
+        try:
+            return sta_forward_raster(q, k, v, tile, window, scale)
+        except NotImplementedError:
+            pass
     volume = tuple(q.shape[2:5])
     qt, kt, vt = (sta_reorder_tiles(x, tile) for x in (q, k, v))
     ot = sta_forward(qt, kt, vt, volume, tile, window, scale)

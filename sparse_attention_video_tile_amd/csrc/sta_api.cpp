@@ -143,6 +143,10 @@ int attention_common(sta::AttnProblem& p, void* stream) {
   if (!p.q || !p.k || !p.v || !p.out) return fail(STA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   int rc = check_heads(p.B, p.heads, p.head_dim);
   if (rc) return rc;
+  // The work plan keeps per-head tables of STA_MAX_HEADS entries (window,
+  // heaviest-first head order), for the dense comparator too.
+  if (p.heads > STA_MAX_HEADS)
+    return fail(STA_ERR_INVALID_ARG, "heads=%d must be in [1, %d]", p.heads, STA_MAX_HEADS);
   const int es = elem_size(p.dtype);
   if (!es) return fail(STA_ERR_INVALID_ARG, "unknown dtype %d", p.dtype);
   if (!(p.scale > 0.0f) || !isfinite(p.scale))
@@ -252,7 +256,7 @@ int forward_common(const void* q, const void* k, const void* v, void* out, float
 
 extern "C" {
 
-int sta_abi_version(void) { return 3; }
+int sta_abi_version(void) { return 4; }
 
 const char* sta_last_error(void) { return g_last_error.c_str(); }
 
@@ -279,6 +283,23 @@ long long sta_kv_pair_count(int heads, int T, int H, int W, const int* tile, con
     pairs += (long long)g.n_tiles * omega[h][0] * omega[h][1] * omega[h][2];
   ok();
   return pairs;
+}
+
+int sta_tile_list_len(int heads, int T, int H, int W, const int* tile, const int* window,
+                      int transposed) {
+  if (heads <= 0 || heads > STA_MAX_HEADS)
+    return fail(STA_ERR_INVALID_ARG, "heads=%d must be in [1, %d]", heads, STA_MAX_HEADS);
+  if (transposed != 0 && transposed != 1)
+    return fail(STA_ERR_INVALID_ARG, "transposed=%d must be 0 or 1", transposed);
+  sta::Geometry g;
+  int rc = check_volume(T, H, W, tile, &g);
+  if (rc) return rc;
+  static thread_local uint16_t omega[STA_MAX_HEADS][3];
+  if ((rc = check_windows(g, heads, window, omega))) return rc;
+  int longest, longest_w;
+  list_extents(g, heads, omega, transposed != 0, &longest, &longest_w);
+  ok();
+  return longest;
 }
 
 int sta_kv_tiles(int* kv_list, int* kv_count, int heads, int T, int H, int W, const int* tile,

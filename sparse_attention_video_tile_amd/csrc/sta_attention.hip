@@ -161,7 +161,7 @@ __device__ __forceinline__ void softmax_max(WaveState<C, RB>& w, f32x4 (&sc)[RB]
   }
 }
 
-template <class C, int RB>
+template <class C, int RB, bool LSE_ONLY>
 __device__ __forceinline__ void softmax_exp(WaveState<C, RB>& w, f32x4 (&sc)[RB][C::kKT],
                                             float scale_log2) {
 #pragma unroll
@@ -171,6 +171,16 @@ __device__ __forceinline__ void softmax_exp(WaveState<C, RB>& w, f32x4 (&sc)[RB]
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         sc[rb][kt][r] = __builtin_amdgcn_exp2f(fmaf(sc[rb][kt][r], scale_log2, -w.m[rb]));
+    if constexpr (LSE_ONLY) {
+      // Nothing multiplies the probabilities: their fp32 values are summed
+      // as they are, never rounded to bf16.
+      float ls = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < C::kKT; ++kt)
+        ls += (sc[rb][kt][0] + sc[rb][kt][1]) + (sc[rb][kt][2] + sc[rb][kt][3]);
+      w.lsum[rb] += ls;
+      continue;
+    }
     // The row sum adds the bf16-rounded probabilities, the same values that
     // multiply V, two per dot instruction.
     float ls = w.lsum[rb];
@@ -198,11 +208,11 @@ __device__ __forceinline__ void softmax_exp(WaveState<C, RB>& w, f32x4 (&sc)[RB]
 // reference max m only moves when a row's chunk max exceeds it by more than 8
 // (then O and the row sum are rescaled); in between, probabilities stay below
 // 2^8, which fp32 sums and bf16 P hold as well as values below 1.
-template <class C, int RB>
+template <class C, int RB, bool LSE_ONLY>
 __device__ __forceinline__ void softmax_chunk(WaveState<C, RB>& w, int nvalid,
                                               unsigned long long real, float scale_log2, int g) {
   softmax_max<C, RB>(w, w.s, nvalid, real, scale_log2, g);
-  softmax_exp<C, RB>(w, w.s, scale_log2);
+  softmax_exp<C, RB, LSE_ONLY>(w, w.s, scale_log2);
 }
 
 // O^T[d][row] += V^T[d][key] P^T[key][row] for one chunk. Slot j of lane group
@@ -475,6 +485,12 @@ attn_bf16_kernel(const AttnParams p) {
       const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
       load_rows<KG, WAVES>(kg, base, nv, kdst, wave, lane, rtab + c0, real);
       if (!LSE_ONLY) load_rows<C, WAVES>(vg, base, nv, vdst, wave, lane, rtab + c0, real);
+    } else if constexpr (PAD) {
+      int row0, kb, nv;
+      walk.at_tile(it, p.tau, &row0, &kb, &nv);
+      const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
+      load_rows<KG, WAVES>(kg, row0, nv, kdst, wave, lane, nullptr, real, kb);
+      if (!LSE_ONLY) load_rows<C, WAVES>(vg, row0, nv, vdst, wave, lane, nullptr, real, kb);
     } else {
       int row0, nv;
       walk.at(it, &row0, &nv);
@@ -569,7 +585,7 @@ attn_bf16_kernel(const AttnParams p) {
       // during the softmax (few LDS reads) rather than beside the K reads
       // (measured: 2 % faster than issuing right after the barrier).
       if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
-      softmax_chunk<C, RB>(w, nvalid, real, p.scale_log2, g);
+      softmax_chunk<C, RB, LSE_ONLY>(w, nvalid, real, p.scale_log2, g);
       // No fence before PV: the scheduler starts the PV MFMAs of the first
       // row block while the exponentials of the others are still being
       // issued (the same wave issuing both is what lets them run side by side).

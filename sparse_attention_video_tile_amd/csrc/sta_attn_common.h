@@ -344,15 +344,18 @@ __device__ __forceinline__ int swz(int row, int c) {
 }
 
 // Issue this wave's share of the direct-to-LDS loads of one K (or V) chunk:
-// key rows kv_row0 .. kv_row0 + BN - 1 of the head (rows past `nvalid` repeat
-// the last valid row; their scores are masked). Each instruction fills one
-// 1 KB block; WAVES wavefronts share the chunk. Keys whose bit in `real` is
-// clear are padding positions: they load row kv_row0 instead (the run's first
-// key, always a token) and are masked later.
+// key rows kv_row0 + key_base .. + BN - 1 of the head (rows past `nvalid`
+// repeat the last valid row; their scores are masked). Each instruction fills
+// one 1 KB block; WAVES wavefronts share the chunk. Keys whose bit in `real`
+// is clear are padding positions: they load row kv_row0 instead, which the
+// caller points at a token (the run's first key in raster order, the first
+// row of the chunk's first tile in tile-major order), so that whatever a
+// caller keeps in the padding rows of a tile-major tensor never reaches the
+// products (a masked key still multiplies its V row by P = 0).
 template <class C, int WAVES>
 __device__ __forceinline__ void load_rows(const void* src, int kv_row0, int nvalid, char* buf,
                                           int wave, int lane, const int* rtab = nullptr,
-                                          unsigned long long real = ~0ull) {
+                                          unsigned long long real = ~0ull, int key_base = 0) {
   constexpr int kIter = (C::kBlocks + WAVES - 1) / WAVES;
 #pragma unroll
   for (int b = 0; b < kIter; ++b) {
@@ -365,7 +368,7 @@ __device__ __forceinline__ void load_rows(const void* src, int kv_row0, int nval
     // kv_row0. Raster order: kv_row0 is the run's first raster token and
     // rtab (already offset to the chunk) gives each key's raster offset.
     const int key = min(row, nvalid - 1);
-    int rel = rtab ? rtab[key] : key;
+    int rel = rtab ? rtab[key] : key_base + key;
     if (!((real >> key) & 1ull)) rel = 0;
     lds_dma<16>(static_cast<const char*>(src) +
                     (long long)__builtin_amdgcn_readfirstlane(kv_row0) * C::kRowBytes,
@@ -467,6 +470,17 @@ struct ChunkWalk {
     const int sub = pp - lt * p.plane_cpp;
     return kv.run_start_raster(run, p.H, p.W, p.ct, p.ch, p.cw) +
            (lt * p.H + sub * (64 / p.cw)) * p.W + tw * p.cw;
+  }
+  // Tile-major order on a padded grid: the first row of the tile the chunk
+  // starts in (a token: every tile starts inside the volume), the chunk's
+  // first key relative to it, and the number of valid keys.
+  __device__ __forceinline__ void at_tile(int it, int tau, int* tile_row0, int* key_base,
+                                          int* nvalid) const {
+    const int run = it / chunks_per_run;
+    const int c0 = (it - run * chunks_per_run) * bn;
+    *key_base = c0 % tau;
+    *tile_row0 = (dense ? 0 : kv.run_start(run)) + c0 - *key_base;
+    *nvalid = min(bn, run_len - c0);
   }
   // Raster order: the run's first raster token, the chunk's first key within
   // the run, and the number of valid keys.

@@ -191,9 +191,10 @@ __device__ __forceinline__ void store_rows(const f32x4 (&acc)[RB][C::kDB], bf16_
 // One float per streamed row of a chunk (lse or D) into LDS with a single
 // direct-to-LDS dword load: lane i fills slot i (BN = 64 rows, one wave).
 __device__ __forceinline__ void load_row_values(const float* src, int row0, int nvalid, float* buf,
-                                                int lane, const int* rtab, unsigned long long real) {
+                                                int lane, const int* rtab, unsigned long long real,
+                                                int key_base) {
   const int key = min(lane, nvalid - 1);
-  int rel = rtab ? rtab[key] : key;
+  int rel = rtab ? rtab[key] : key_base + key;
   if (!((real >> key) & 1ull)) rel = 0;
   lds_dma<4>(src + __builtin_amdgcn_readfirstlane(row0), rel * 4, buf);
 }
@@ -258,6 +259,12 @@ bwd_dq_kernel(const AttnParams p, const BwdParams b) {
       const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
       load_rows<C, WAVES>(kg, base, nv, kdst, wave, lane, rtab + c0, real);
       load_rows<C, WAVES>(vg, base, nv, vdst, wave, lane, rtab + c0, real);
+    } else if constexpr (PAD) {
+      int row0, kb, nv;
+      walk.at_tile(it, p.tau, &row0, &kb, &nv);
+      const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
+      load_rows<C, WAVES>(kg, row0, nv, kdst, wave, lane, nullptr, real, kb);
+      load_rows<C, WAVES>(vg, row0, nv, vdst, wave, lane, nullptr, real, kb);
     } else {
       int row0, nv;
       walk.at(it, &row0, &nv);
@@ -373,20 +380,23 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
   }
   auto dma = [&](int it, char* qdst, char* odst, float* ldst, float* ddst)
                  __attribute__((always_inline)) {
-    int base, c0, nv;
+    int base, c0 = 0, nv;
     const int* tab = nullptr;
     if (RASTER) {
       walk.at_raster(p, it, &base, &c0, &nv);
       tab = rtab + c0;
+    } else if (PAD) {
+      walk.at_tile(it, p.tau, &base, &c0, &nv);   // padding rows load the tile's first row
     } else {
       walk.at(it, &base, &nv);
     }
+    const int kb = RASTER ? 0 : c0;
     const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
-    load_rows<C, WAVES>(qg, base, nv, qdst, wave, lane, tab, real);
-    load_rows<C, WAVES>(dog, base, nv, odst, wave, lane, tab, real);
+    load_rows<C, WAVES>(qg, base, nv, qdst, wave, lane, tab, real, kb);
+    load_rows<C, WAVES>(dog, base, nv, odst, wave, lane, tab, real, kb);
     if (wave == 0) {
-      load_row_values(lseg, base, nv, ldst, lane, tab, real);
-      load_row_values(delg, base, nv, ddst, lane, tab, real);
+      load_row_values(lseg, base, nv, ldst, lane, tab, real, kb);
+      load_row_values(delg, base, nv, ddst, lane, tab, real, kb);
     }
   };
   dma(0, qb0, ob0, lb0, db0);

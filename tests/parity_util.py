@@ -71,6 +71,27 @@ GRAD_F32_MAX_REL = 1e-4
 # values that multiply V), which moves lse by at most log(1 + 2^-9) < 2e-3.
 LSE_BF16_MAX_ABS = 4e-3
 LSE_F32_MAX_ABS = 1e-5
+# Log-sum-exp-only passes (window recall), per row against the float64
+# oracle. Nothing multiplies the probabilities there, so they are summed in
+# fp32 without rounding, in both the dense and the window pass, for bf16 and
+# float32 inputs alike. The error sources, for the small recall workloads
+# (at most 4608 keys, 72 key chunks of 64 per row):
+#   fp32 summation: each lane adds its chunk partials in order, then four lanes
+#     combine: at most (n_chunks + 8) u = 80 * 2^-24 = 4.8e-6 relative;
+#   exp2 argument: scale*log2(e) and the fma are rounded (relative u each) at
+#     |argument| <= 8 above the reference max, and the hardware exp2 is within
+#     about one ulp: well under 1e-6 relative on the probability-weighted sum;
+#   score products: exact (bf16 x bf16, or fp32 in the fp32 kernel), summed in
+#     fp32 over d <= 128 terms: typically a few 1e-7 on the scaled score;
+#   storing lse in fp32: u |lse| < 1e-6 for |lse| < 16.
+# Together under 1e-5; the bound leaves a factor two. Rounding the
+# probabilities to bf16 before summing (the forward's rule, wrong here) moves
+# these rows' lse by 2e-4 .. 1e-3 (tests/test_tolerances.py checks this on the
+# recall workloads), so the bound tells the two apart.
+LSE_FP32_SUM_MAX_ABS = 2e-5
+# recall = mean_i exp(lse_window(i) - lse_full(i)) <= 1: both lse errors, the
+# fp32 exp of the reduction (|argument| < 16, one ulp) and the fp32 result.
+RECALL_MAX_ABS = 2 * LSE_FP32_SUM_MAX_ABS + 4 * 2.0 ** -24
 
 
 def assert_grad_close(got, ref, dtype: str, what: str = ""):

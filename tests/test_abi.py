@@ -94,6 +94,10 @@ def test_full_attention_rejects_bad_arguments(lib):
     assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 1000, 1, 1, 128, 0, 0.1, 0, None) == -1
     assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 1000, 1, 1, 128, 1024, -1.0, 0, None) == -1
     assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 1000, 1, 1, 48, 1024, 0.1, 0, None) == -2
+    # more heads than the work plan's per-head tables hold
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE * 1000, 1, binding.STA_MAX_HEADS + 1, 128, 1024, 0.1, 0,
+             None) == -1
+    assert "heads" in binding.last_error()
 
 
 def test_kv_tiles_rejects_bad_arguments(lib):
@@ -183,17 +187,48 @@ def test_backward_rejects_bad_arguments(lib):
     assert "raster order" in binding.last_error()
 
 
-def test_raster_run_fits_matches_library_limit():
-    assert binding.raster_run_fits((6, 8, 8), [(18, 24, 24)], 1, (30, 48, 80), backward=True)
-    assert binding.raster_run_fits((1, 1, 8), [(1, 1, 8192)], 1, (1, 1, 8192), backward=True)
-    assert not binding.raster_run_fits((1, 1, 8), [(1, 1, 8200)], 1, (1, 1, 8200), backward=True)
-    # transposed runs can be longer than the window: n_w = 4, omega_w = 2 gives
-    # key tile 1 three query tiles
-    assert binding._inverse_len(1, 4, 2) == 3
-    # n_w = 4 tiles of 4096, omega_w = 2: window runs of 8192 fit, the
-    # transposed run of key tile 1 (3 query tiles, 12288 tokens) does not
-    assert binding.raster_run_fits((1, 1, 4096), [(1, 1, 8192)], 1, (1, 1, 16384), backward=False)
-    assert not binding.raster_run_fits((1, 1, 4096), [(1, 1, 8192)], 1, (1, 1, 16384), backward=True)
+def raster_forward_rc(lib, tile, window, volume, d=64):
+    """Return code of sta_forward_raster on never-dereferenced pointers: the
+    host checks decide before any launch."""
+    T, H, W = volume
+    big = [(k + 1) << 40 for k in range(4)]
+    return lib.sta_forward_raster(big[0], big[1], big[2], big[3], 1, 1, d, T, H, W, i3(*tile),
+                                  i3(*window), 0.1, 0, None)
+
+
+def test_raster_run_limit_is_the_library_s(lib):
+    """Window runs of up to 8192 keys take the raster kernel; longer ones are
+    refused with STA_ERR_UNSUPPORTED (the binding's fused path then reorders).
+    The backward counts the transposed runs too: n_w = 4 tiles of 4096 with
+    omega_w = 2 gives key tile 1 three query tiles (12288 keys)."""
+    assert lib.sta_tile_list_len(1, 1, 1, 16384, i3(1, 1, 4096), i3(1, 1, 8192), 1) == 3
+    assert lib.sta_tile_list_len(1, 1, 1, 16384, i3(1, 1, 4096), i3(1, 1, 8192), 0) == 2
+    a = backward_args(order=1, T=1, H=1, W=16384, tile=i3(1, 1, 4096), win=i3(1, 1, 8192), d=64)
+    assert call_backward(lib, a) == -2
+    assert "12288" in binding.last_error()
+    a = backward_args(order=1, T=1, H=1, W=8200, tile=i3(1, 1, 8), win=i3(1, 1, 8200), d=64)
+    assert call_backward(lib, a) == -2
+
+
+def test_tile_list_len_matches_oracle(lib):
+    """The library's longest-list query, which sizes the list buffers, against
+    the oracle's lists (forward and transposed), padded grids included."""
+    for volume, tile, windows in [
+        ((30, 48, 80), (6, 8, 8), [(18, 24, 24)]),
+        ((30, 48, 80), (6, 8, 8), [(18, 24, 24), (30, 40, 40), (30, 48, 80)]),
+        ((5, 6, 7), (2, 4, 4), [(4, 4, 4), (2, 8, 8), (6, 8, 8)]),
+        ((1, 1, 16384), (1, 1, 4096), [(1, 1, 8192)]),
+    ]:
+        kv = oracle.kv_tile_lists(volume, tile, np.array(windows))[1].max()
+        q = oracle.q_tile_lists(volume, tile, windows)[1].max()
+        assert binding.sta_tile_list_len(len(windows), volume, tile, windows) == kv
+        assert binding.sta_tile_list_len(len(windows), volume, tile, windows, transposed=True) == q
+    t, w = i3(6, 8, 8), i3(18, 24, 24)
+    assert lib.sta_tile_list_len(0, 30, 48, 80, t, w, 0) == -1
+    assert lib.sta_tile_list_len(257, 30, 48, 80, t, w, 0) == -1
+    assert lib.sta_tile_list_len(1, 30, 48, 80, t, i3(18, 24, 25), 0) == -1
+    assert lib.sta_tile_list_len(1, 30, 48, 80, t, w, 2) == -1
+    assert lib.sta_tile_list_len(1, 30, 48, 80, None, w, 0) == -1
 
 
 def test_raster_frames_beyond_32bit_run_addressing_are_refused(lib):
@@ -204,14 +239,12 @@ def test_raster_frames_beyond_32bit_run_addressing_are_refused(lib):
     big = [(k + 1) << 40 for k in range(4)]
     rc = lib.sta_forward_raster(big[0], big[1], big[2], big[3], 1, 1, 64, 1, 2904, 2904, t, w, 0.1, 0, None)
     assert rc == -2 and "addressing" in binding.last_error()
-    assert not binding.raster_run_fits((1, 8, 8), [(1, 8, 8)], 1, (1, 2904, 2904))
-    assert binding.raster_run_fits((1, 8, 8), [(1, 8, 8)], 1, (1, 2896, 2896))
-
-
-def test_backward_raster_limit_counts_transposed_runs(lib):
-    a = backward_args(order=1, T=1, H=1, W=16384, tile=i3(1, 1, 4096), win=i3(1, 1, 8192), d=64)
-    assert call_backward(lib, a) == -2
-    assert "12288" in binding.last_error()
+    assert raster_forward_rc(lib, (1, 8, 8), (1, 8, 8), (1, 2904, 2904)) == -2
+    # 2896 x 2896 frames pass the raster checks: with misaligned pointers the
+    # call gets as far as the alignment check (made after them)
+    rc = lib.sta_forward_raster(FAKE + 8, FAKE * 100, FAKE * 200, FAKE * 300, 1, 1, 64, 1, 2896,
+                                2896, t, w, 0.1, 0, None)
+    assert rc == -2 and "aligned" in binding.last_error()
 
 
 def test_window_recall_rejects_bad_arguments(lib):

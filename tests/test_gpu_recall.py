@@ -8,15 +8,16 @@ import torch
 
 import oracle
 from sparse_attention_video_tile_amd import binding, workloads
-from tests.parity_util import default_scale, to_gpu
+from tests.parity_util import LSE_FP32_SUM_MAX_ABS, RECALL_MAX_ABS, default_scale, to_gpu
 
 pytestmark = pytest.mark.gpu
 
-# Both log-sum-exps of the bf16 path sum bf16-rounded probabilities (relative
-# error <= 2^-9 each), so exp(lse_w - lse_full) is within ~4e-3 relative of
-# the exact share, and the share is at most 1.
-RECALL_BF16_ABS = 5e-3
-RECALL_F32_ABS = 1e-5
+# At 30x48x80 (1800 key chunks of 64 per dense row) the whole-volume window's
+# lse comes from the sparse kernel and the full lse from the dense one: the
+# scores are the same fp32 products, the fp32 sums run in different orders,
+# each within (n_chunks + 8) u of the exact sum, so the recall is within
+# 2 * 1808 * 2^-24 = 2.2e-4 of 1.
+RECALL_FULL_SIZE_ABS = 2.5e-4
 
 CASES = [
     ("tiles_6x8x8", (12, 16, 24), (6, 8, 8), [(6, 8, 8), (6, 16, 8), (12, 16, 24)], 2, 128, "bf16"),
@@ -36,16 +37,29 @@ def test_recall_matches_oracle(case, order):
     inp = workloads.make_inputs(w)
     q, k = to_gpu(inp.q, dtype), to_gpu(inp.k, dtype)
     scale = default_scale(d)
+    S = int(np.prod(volume))
+    ws = torch.empty((2, w.B, heads, S), dtype=torch.float32, device="cuda")
     if order == "raster":
-        got = binding.sta_window_recall(q, k, tile, cands, scale)
+        got = binding.sta_window_recall(q, k, tile, cands, scale, workspace=ws)
     else:
         qt, kt = binding.sta_reorder_tiles(q, tile), binding.sta_reorder_tiles(k, tile)
-        got = binding.sta_window_recall(qt, kt, tile, cands, scale, volume=volume)
+        got = binding.sta_window_recall(qt, kt, tile, cands, scale, volume=volume, workspace=ws)
     torch.cuda.synchronize()
     ref = oracle.window_recall(inp.q, inp.k, tile, cands, scale)
     err = np.abs(got.cpu().numpy().astype(np.float64) - ref).max()
     print(f"[parity] {name} {order} recall max_abs {err:.3e} ref {ref.ravel()[:4]}", flush=True)
-    assert err <= (RECALL_BF16_ABS if dtype == "bf16" else RECALL_F32_ABS)
+    assert err <= RECALL_MAX_ABS
+    # The workspace keeps the two row log-sum-exps of the last pass: all keys,
+    # and the last candidate window. Each row against the oracle.
+    lse_ref = [oracle.sta_lse(inp.q, inp.k, tile, [win] * heads, scale) for win in (volume, cands[-1])]
+    for slot, r in enumerate(lse_ref):
+        r = r[..., None]
+        if order == "tile_major":
+            r = oracle.to_tile_major(r, tile)
+        r = r.reshape(w.B, heads, S)
+        lerr = np.abs(ws[slot].cpu().numpy().astype(np.float64) - r).max()
+        print(f"[parity] {name} {order} lse slot {slot} max_abs {lerr:.3e}", flush=True)
+        assert lerr <= LSE_FP32_SUM_MAX_ABS
 
 
 def test_recall_full_size_invariants():
@@ -72,7 +86,7 @@ def test_recall_full_size_invariants():
     torch.cuda.synchronize()
     r, rt = r.cpu().numpy(), rt.cpu().numpy()
     print(f"[parity] full-size recall head 0 {r[0, 0]}", flush=True)
-    assert np.all(r > 0) and np.all(r <= 1 + RECALL_BF16_ABS)
-    assert np.abs(r[..., 2] - 1.0).max() <= RECALL_BF16_ABS
+    assert np.all(r > 0) and np.all(r <= 1 + RECALL_FULL_SIZE_ABS)
+    assert np.abs(r[..., 2] - 1.0).max() <= RECALL_FULL_SIZE_ABS
     assert np.all(r[..., 0] <= r[..., 1] + 1e-6) and np.all(r[..., 1] <= r[..., 2] + 1e-6)
     assert np.abs(r - rt).max() <= 1e-4
