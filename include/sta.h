@@ -270,6 +270,23 @@ int sta_backward(const void* q, const void* k, const void* v, const void* out, c
                  float scale, int dtype, int order, void* stream);
 
 /*
+ * sta_backward without the delta workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). D = rowsum(dO * O) goes to a static
+ * 32 MiB device array that the library carries on every GPU it runs on
+ * (until the process ends): B * heads * rows must be at most 8 Mi (8388608),
+ * else STA_ERR_INVALID_ARG and nothing is enqueued. The call allocates
+ * nothing. Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (other streams, other threads) race and must be serialised by
+ * the caller. Arguments, outputs and results as sta_backward (bit-identical
+ * gradients).
+ */
+int sta_backward_noalloc(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int heads, int head_dim, int T, int H, int W, const int* tile,
+                         const int* window, float scale, int dtype, int order, void* stream);
+
+/*
  * Window recall: for every batch entry b, head h and candidate window c,
  *     recall[b][h][c] = (1/S) sum_i sum_{j in W_c(i)} softmax_j(scale * q_i . k_j)
  * where the softmax runs over ALL S keys (full attention) and W_c(i) is the

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     sliding_tile_attention,
     sta_attention,
     sta_backward,
+    sta_backward_noalloc,
     sta_forward,
     sta_forward_lse,
     sta_forward_fp8,

@@ -37,6 +37,7 @@ EXPORTS = (
     "sta_forward_lse",
     "sta_forward_fp8",
     "sta_backward",
+    "sta_backward_noalloc",
     "sta_window_recall",
     "sta_full_attention",
     "sta_last_error",
@@ -90,6 +91,9 @@ def load_library(path: str = None) -> ctypes.CDLL:
     lib.sta_backward.restype = c_int
     lib.sta_backward.argtypes = [c_void_p] * 10 + [c_int, c_int, c_int, c_int, c_int, c_int, int3,
                                                    int3, c_float, c_int, c_int, c_void_p]
+    lib.sta_backward_noalloc.restype = c_int
+    lib.sta_backward_noalloc.argtypes = [c_void_p] * 9 + [c_int, c_int, c_int, c_int, c_int, c_int, int3,
+                                                          int3, c_float, c_int, c_int, c_void_p]
     lib.sta_tile_list_len.restype = c_int
     lib.sta_tile_list_len.argtypes = [c_int, c_int, c_int, c_int, int3, int3, c_int]
     lib.sta_kv_pair_count.restype = ctypes.c_longlong
@@ -462,6 +466,40 @@ def sta_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
                               _int_array(tile), _int_array(_windows_per_head(window, heads)),
                               float(scale), _dtype_code(q), order, _stream(dev))
     _check(rc, "sta_backward")
+    return dq, dk, dv
+
+
+def sta_backward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                         dout: torch.Tensor, lse: torch.Tensor, tile: Sequence[int], window,
+                         scale: Optional[float] = None, volume: Optional[Sequence[int]] = None,
+                         grads: Optional[Sequence[torch.Tensor]] = None
+                         ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """sta_backward through the library's allocation-free entry point (its D
+    workspace is a static device array; calls that overlap on one GPU race).
+    `grads` may supply the (dq, dk, dv) output tensors."""
+    lib = load_library()
+    for name, x in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if x.shape != q.shape or x.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    B, heads, d, (T, H, W), order = _order_shapes(q, volume, tile)
+    if lse.shape != q.shape[:-1] or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of q's shape without d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    dq, dk, dv = grads
+    for x in grads:
+        if x.shape != q.shape or x.dtype != q.dtype:
+            raise ValueError("gradient outputs must match q in shape and dtype")
+    dev = _require_gpu(q, k, v, out, dout, lse, dq, dk, dv)
+    with torch.cuda.device(dev):
+        rc = lib.sta_backward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                      dv.data_ptr(), B, heads, d, T, H, W, _int_array(tile),
+                                      _int_array(_windows_per_head(window, heads)), float(scale),
+                                      _dtype_code(q), order, _stream(dev))
+    _check(rc, "sta_backward_noalloc")
     return dq, dk, dv
 
 

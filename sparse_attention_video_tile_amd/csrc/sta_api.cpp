@@ -347,12 +347,14 @@ int forward_common(const void* q, const void* k, const void* v, void* out, float
   return attention_common(p, stream);
 }
 
+// use_scratch: D goes to the library's static device scratch (delta is
+// ignored); the problem must fit it.
 int backward_common(const void* q, const void* k, const void* v, const void* out,
                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
                     float* delta, int B, int heads, int head_dim, int T, int H, int W,
                     const int* tile, const int* window, float scale, int dtype, int order,
-                    void* stream) {
-  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !delta)
+                    void* stream, bool use_scratch = false) {
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || (!delta && !use_scratch))
     return fail(STA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (order != STA_TILE_MAJOR && order != STA_RASTER)
     return fail(STA_ERR_INVALID_ARG, "unknown token order %d", order);
@@ -388,19 +390,29 @@ int backward_common(const void* q, const void* k, const void* v, const void* out
   const long long BH = (long long)B * heads;
   if (BH > (1LL << 24)) return fail(STA_ERR_INVALID_ARG, "B*heads=%lld is too large", BH);
   const int rows = p.raster ? p.g.S : p.g.S_pad;
+  if (use_scratch && BH * rows > sta::kNoAllocScratchFloats)
+    return fail(STA_ERR_INVALID_ARG,
+                "B*heads*rows = %lld exceeds the %lld rows of the allocation-free scratch; "
+                "use sta_backward with a caller-owned delta workspace",
+                BH * rows, sta::kNoAllocScratchFloats);
   const size_t tb = (size_t)BH * rows * head_dim * es;
   const size_t rb = (size_t)BH * rows * sizeof(float);
   const void* ins[6] = {q, k, v, out, dout, lse};
   const size_t in_bytes[6] = {tb, tb, tb, tb, tb, rb};
   const void* outs[4] = {dq, dk, dv, delta};
   const size_t out_bytes[4] = {tb, tb, tb, rb};
-  for (int i = 0; i < 4; ++i) {
+  const int n_outs = use_scratch ? 3 : 4;   // the library's own scratch overlaps nothing
+  for (int i = 0; i < n_outs; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j]))
         return fail(STA_ERR_INVALID_ARG, "an output or the delta workspace overlaps an input");
-    for (int j = i + 1; j < 4; ++j)
+    for (int j = i + 1; j < n_outs; ++j)
       if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j]))
         return fail(STA_ERR_INVALID_ARG, "outputs overlap each other or the delta workspace");
+  }
+  if (use_scratch) {   // every check has passed: look up this device's scratch
+    const int e = sta::noalloc_scratch(&delta);
+    if (e) return fail(STA_ERR_HIP, "device scratch lookup failed: %s", sta::hip_error_string(e));
   }
   pb.dout = dout; pb.lse = lse; pb.delta = delta;
   pb.dq = dq; pb.dk = dk; pb.dv = dv;
@@ -461,6 +473,14 @@ int sta_backward(const void* q, const void* k, const void* v, const void* out, c
                  float scale, int dtype, int order, void* stream) {
   return backward_common(q, k, v, out, dout, lse, dq, dk, dv, delta, B, heads, head_dim, T, H, W,
                          tile, window, scale, dtype, order, stream);
+}
+
+int sta_backward_noalloc(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int heads, int head_dim, int T, int H, int W, const int* tile,
+                         const int* window, float scale, int dtype, int order, void* stream) {
+  return backward_common(q, k, v, out, dout, lse, dq, dk, dv, nullptr, B, heads, head_dim, T, H, W,
+                         tile, window, scale, dtype, order, stream, true);
 }
 
 int sta_window_recall(const void* q, const void* k, float* recall, float* workspace, int B,

@@ -65,6 +65,14 @@ int launch_backward(const BwdProblem& p, void* stream);
 int launch_recall_reduce(const float* lse_full, const float* lse_win, float* recall, int BH, int S,
                          int n_cand, int c, void* stream);
 
+// Floats in the device scratch of the allocation-free backward (32 MiB per
+// GPU): the D workspace of up to 8 Mi query rows (B * heads * rows).
+constexpr long long kNoAllocScratchFloats = 8LL << 20;
+
+// The current device's address of that scratch, looked up on the first call
+// on each device. Returns 0 or a hipError_t value.
+int noalloc_scratch(float** ptr);
+
 const char* hip_error_string(int code);
 
 }  // namespace sta

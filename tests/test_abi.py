@@ -283,3 +283,22 @@ def test_float32_attention_on_a_padded_grid_is_refused(lib):
     # a window larger than the padded grid is still invalid
     assert lib.sta_forward(FAKE, FAKE * 100, FAKE * 200, FAKE * 300, 1, 1, 64, 5, 6, 7, t,
                            i3(8, 4, 4), 0.1, 0, None) == -1
+
+
+def call_backward_noalloc(lib, a):
+    return lib.sta_backward_noalloc(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                                    a["dk"], a["dv"], a["B"], a["heads"], a["d"], a["T"], a["H"],
+                                    a["W"], a["tile"], a["win"], a["scale"], a["dt"], a["order"], None)
+
+
+def test_backward_noalloc_refuses_problems_beyond_its_scratch(lib):
+    """The allocation-free backward keeps D in a static scratch of 8 Mi rows:
+    72 heads of 115200 rows fit (the call then fails later, on the fake
+    buffers' overlap), 73 do not, and it says so before anything is enqueued."""
+    for heads, msg in ((73, "scratch"), (72, "overlap")):
+        win = binding._int_array([18, 24, 24] * heads)   # one window per head
+        assert call_backward_noalloc(lib, backward_args(heads=heads, win=win, order=1)) == -1
+        assert msg in binding.last_error()
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert call_backward_noalloc(lib, backward_args(**{name: None})) == -1, name
+    assert call_backward_noalloc(lib, backward_args(order=3)) == -1
