@@ -1,14 +1,20 @@
 """GPU: the four 30x48x80 workloads at full size, in the launch configuration
 the benchmark times (the raster-order kernel). The oracle computes sampled
-query rows one by one (corner, edge and interior tiles of several heads);
-whole-volume STA is also compared element by element with the dense kernel,
-and the raster-order kernel with the reorder + tile-major path."""
+query rows one by one (corner, edge and interior tiles of several heads), and
+every row of one whole head of the (18,24,24) workload and of the mixed
+workload's heaviest head that is not the whole volume (a process pool of the
+oracle over the host's cores); whole-volume STA is also compared element by
+element with the dense kernel, and the raster-order kernel with the reorder +
+tile-major path."""
+
+import time
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
+from oracle import pool
 from sparse_attention_video_tile_amd import binding, workloads
 from tests.parity_util import assert_close, default_scale, to_gpu
 
@@ -38,6 +44,17 @@ def sample_rows(w, windows, rng):
     return out
 
 
+def whole_head(w, windows) -> int:
+    """Head checked row by row: head 0 of a uniform workload; of the mixed one,
+    the head with the largest window that is not the whole volume."""
+    if w.windows is not None:
+        return 0
+    sizes = [int(np.prod(x)) for x in windows]
+    full = int(np.prod(w.volume))
+    return max((i for i in range(len(sizes)) if sizes[i] < full), key=lambda i: (sizes[i], -i))
+
+
+@pytest.mark.timeout(400)   # input draws, then up to a whole head of the oracle on the host
 @pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
 def test_full_size_sampled_rows(w):
     print(f"[case] full size {w.name}: generating inputs", flush=True)
@@ -58,6 +75,24 @@ def test_full_size_sampled_rows(w):
         refs.append(ref)
         assert_close(got[0, h, rows], ref, w.dtype, f"{w.name} head {h} window {window}")
     assert_close(np.concatenate(gots), np.concatenate(refs), w.dtype, f"{w.name} all samples")
+
+    if w is workloads.STA_18_24_24 or w is workloads.MIXED_HEADS:
+        h = whole_head(w, inp.windows)
+        window = tuple(int(x) for x in inp.windows[h])
+        print(f"[case] full size {w.name}: every row of head {h}, window {window}, oracle pool",
+              flush=True)
+        last = [time.perf_counter()]
+
+        def progress(done, total):
+            if time.perf_counter() - last[0] > 10 or done == total:
+                last[0] = time.perf_counter()
+                print(f"[oracle] {done}/{total} query tiles", flush=True)
+
+        jobs = pool.tile_jobs(w.volume, w.tile, [(0, h)])
+        ref, wall, workers = pool.sta_attention_pool(inp.q, inp.k, inp.v, w.tile, inp.windows, scale,
+                                                     jobs, progress=progress)
+        print(f"[oracle] head {h}: {wall:.1f} s on {workers} workers", flush=True)
+        assert_close(got[0, h], ref[(0, h)], w.dtype, f"{w.name} head {h} all {w.seq_len} rows")
 
     if w is workloads.DENSE_WHOLE:
         print(f"[case] full size {w.name}: dense kernel", flush=True)
