@@ -61,6 +61,13 @@ def load_library(path: str = None) -> ctypes.CDLL:
         return _lib
     if path is None:
         path = os.environ.get("STA_LIBRARY", LIB_PATH)
+    _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """Open one build of libsta at `path` and declare its C signatures
+    (uncached: load_library keeps the one the binding uses)."""
     if not os.path.exists(path):
         raise RuntimeError(
             f"libsta.so not found at {path}; build it with "
@@ -111,7 +118,6 @@ def load_library(path: str = None) -> ctypes.CDLL:
                                        c_int, c_int, c_float, c_int, c_void_p]
     if lib.sta_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libsta ABI {lib.sta_abi_version()} != expected {ABI_VERSION}")
-    _lib = lib
     return lib
 
 

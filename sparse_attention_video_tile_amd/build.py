@@ -21,6 +21,12 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsta.so")
+# The same library with the attention kernels built single-buffered (one K/V
+# buffer, loads after every wave has finished a chunk): the reference of the
+# synchronisation audit test. Built beside libsta.so, never loaded by the
+# package itself.
+AUDIT_LIB = os.path.join(PKG, "libsta_audit.so")
+AUDIT_FLAGS = ["-DSTA_AUDIT_SINGLE_BUFFER=1"]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HIP_SOURCES = ["sta_layout.hip", "sta_attention.hip", "sta_backward.hip", "sta_recall.hip",
@@ -72,12 +78,17 @@ def build(verbose: bool = False, extra_hip_flags=()) -> str:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
         jobs.append(["g++", *CXX_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+    audit_obj = os.path.join(BUILD, "sta_attention_audit.hip.o")
+    jobs.append([_hipcc(), *HIPCC_FLAGS, *extra_hip_flags, *AUDIT_FLAGS, *inc, "-c",
+                 os.path.join(CSRC, "sta_attention.hip"), "-o", audit_obj])
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         for f in [ex.submit(_run, j, verbose) for j in jobs]:
             f.result()
-    tmp = LIB + ".tmp"
-    _run([_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    for lib, lib_objs in ((LIB, objs),
+                          (AUDIT_LIB, [audit_obj if o.endswith("sta_attention.hip.o") else o for o in objs])):
+        tmp = lib + ".tmp"
+        _run([_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *lib_objs, "-o", tmp], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -502,8 +502,21 @@ attn_bf16_kernel(const AttnParams p) {
   WaveState<C, RB> w;
   load_q_init<C, RB>(w, qg, map_rows<C, RB, RASTER>(p, t, wave, l16), l16, g);
 
+  // STA_AUDIT_SINGLE_BUFFER (a separate build of this file, used only by the
+  // synchronisation audit): one K/V buffer, whose next chunk is loaded only
+  // after every wave has finished the current one. Same arithmetic in the
+  // same order, so its outputs must equal the double-buffered kernel's bit
+  // for bit; a missing wait in the pipeline would show as a difference.
+#ifdef STA_AUDIT_SINGLE_BUFFER
+  constexpr bool kSingleBuffer = true;
+#else
+  constexpr bool kSingleBuffer = false;
+#endif
   auto chunk_step = [&](auto first, const char* kcur, const char* vcur, char* knxt, char* vnxt, int it)
                         __attribute__((always_inline)) {
+    if constexpr (kSingleBuffer) {
+      kcur = kb0; vcur = vb0; knxt = nullptr; vnxt = nullptr;
+    }
     int row0, nvalid;
     walk.at(it, &row0, &nvalid);
     const unsigned long long real = chunk_real_keys<PAD && !DENSE>(p, walk, it, lane);
@@ -542,7 +555,7 @@ attn_bf16_kernel(const AttnParams p) {
       // fp8: one MFMA per tile and row block, twice as long as a bf16 one.
       sched_qk_softmax<RB, C::kKT, C::kDK, (plane ? 1 : 2) * (QK8 ? 2 : 1), QK8 ? 2 : 1>();
       __builtin_amdgcn_sched_barrier(0);
-      if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
+      if (!kSingleBuffer && it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
       bool grow = false;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) grow |= !(lc[rb] <= 256.0f);   // also an infinite sum
@@ -584,7 +597,7 @@ attn_bf16_kernel(const AttnParams p) {
       // The next chunk's loads go out after QK^T, so their LDS writes land
       // during the softmax (few LDS reads) rather than beside the K reads
       // (measured: 2 % faster than issuing right after the barrier).
-      if (it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
+      if (!kSingleBuffer && it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
       softmax_chunk<C, RB, LSE_ONLY>(w, nvalid, real, p.scale_log2, g);
       // No fence before PV: the scheduler starts the PV MFMAs of the first
       // row block while the exponentials of the others are still being
@@ -593,6 +606,10 @@ attn_bf16_kernel(const AttnParams p) {
         pv_chunk<C, RB>(w, vcur, l16, g);
         sched_reads_ahead<RB, C::kKP * C::kDB, 2, kReadAhead>();
       }
+    }
+    if constexpr (kSingleBuffer) {
+      __syncthreads();   // every wave is done with this chunk's K and V
+      if (it + 1 < walk.n_chunks) dma(it + 1, kb0, vb0);
     }
   };
   if constexpr (FULL) {
@@ -617,9 +634,6 @@ attn_bf16_kernel(const AttnParams p) {
 // ---------------------------------------------------------------------------
 // f32 kernel
 // ---------------------------------------------------------------------------
-
-constexpr int kF32Threads = 128;
-constexpr int kF32BN = 32;
 
 template <int D, bool RASTER>
 __global__ void __launch_bounds__(kF32Threads) attn_f32_kernel(const AttnParams p) {
@@ -717,39 +731,6 @@ __global__ void __launch_bounds__(kF32Threads) attn_f32_kernel(const AttnParams 
 // Launch
 // ---------------------------------------------------------------------------
 
-void fill_params(const AttnProblem& pr, int rows_per_item, AttnParams* p) {
-  p->q = pr.q; p->k = pr.k; p->v = pr.v; p->out = pr.out;
-  p->lse = pr.lse;
-  // rows per (batch, head) of the tensors: tile-major tensors of a padded
-  // tile grid hold n_tiles * tau rows
-  p->S = pr.dense || pr.raster ? pr.g.S : pr.g.S_pad;
-  p->heads = pr.heads;
-  p->dense = pr.dense ? 1 : 0;
-  p->scale_log2 = pr.scale * kLog2e;
-  if (pr.dense) {
-    p->n_units = 1;
-    p->unit_rows = pr.g.S;
-    p->nt = p->nh = p->nw = 1;
-    p->tau = pr.g.S;
-    p->T = p->H = p->W = p->ct = p->ch = p->cw = 1;
-    p->pad = 0;
-    p->plane_cpt = p->plane_cpp = 0;
-  } else {
-    p->n_units = pr.g.n_tiles;
-    p->unit_rows = pr.g.tau;
-    p->nt = pr.g.nt; p->nh = pr.g.nh; p->nw = pr.g.nw;
-    p->tau = pr.g.tau;
-    p->T = pr.g.T; p->H = pr.g.H; p->W = pr.g.W;
-    p->ct = pr.g.ct; p->ch = pr.g.ch; p->cw = pr.g.cw;
-    p->pad = pr.g.padded;
-    set_plane_chunks(p);
-    for (int h = 0; h < pr.heads; ++h)
-      for (int a = 0; a < 3; ++a) p->omega[h][a] = pr.omega[h][a];
-  }
-  p->row_blocks = (p->unit_rows + rows_per_item - 1) / rows_per_item;
-  const long long tasks = (long long)pr.B * pr.heads * p->n_units * p->row_blocks;
-  plan_tasks(p, tasks, pr.heads, pr.dense);
-}
 
 // LDS for the raster offsets of the longest window run, omega_w * tau keys.
 unsigned raster_table_bytes(const AttnProblem& pr) {
@@ -872,20 +853,10 @@ int launch_f32(const AttnProblem& pr, hipStream_t stream) {
 // Rows per bf16 work item: a whole 384-token tile when it fits, else 64 or 128.
 template <int D, bool QK8 = false>
 int dispatch_bf16(const AttnProblem& pr, hipStream_t stream) {
-  const int unit_rows = pr.dense ? pr.g.S : pr.g.tau;
-#ifndef STA_CFG_WAVES
-#define STA_CFG_WAVES 8
-#endif
-#ifndef STA_CFG_RB
-#define STA_CFG_RB 3
-#endif
-#ifndef STA_CFG_BN
-#define STA_CFG_BN 64
-#endif
-  constexpr int kBigRows = STA_CFG_WAVES * 16 * STA_CFG_RB;
-  if (unit_rows % kBigRows == 0)
-    return launch_bf16<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN, QK8>(pr, stream);
-  if (unit_rows <= 64) return launch_bf16<D, 4, 1, 64, QK8>(pr, stream);
+  const int rows = fwd_bf16_rows(pr.dense ? pr.g.S : pr.g.tau);
+  static_assert(Bf16Cfg<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN>::kRows == kFwdBigRows, "shape");
+  if (rows == kFwdBigRows) return launch_bf16<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN, QK8>(pr, stream);
+  if (rows == 64) return launch_bf16<D, 4, 1, 64, QK8>(pr, stream);
   return launch_bf16<D, 4, 2, 64, QK8>(pr, stream);
 }
 

@@ -1,7 +1,8 @@
 // Device-side building blocks shared by the attention kernels of libsta
-// (forward in sta_attention.hip, backward in sta_backward.hip): kernel
-// parameters, work-item decoding and the window walk, raster-order
-// addressing, the LDS layout of K/V-like chunks and their direct-to-LDS loads.
+// (forward in sta_attention.hip, backward in sta_backward.hip): cross-lane
+// reductions, the LDS layout of K/V-like chunks and their direct-to-LDS
+// loads, row maps and key masks. The work plan (kernel parameters, work-item
+// decoding, the window walk, raster-order addressing) is in sta_plan.h.
 //
 // Included only by HIP translation units; everything sits in an anonymous
 // namespace, so each includer gets its own copy.
@@ -12,6 +13,7 @@
 #include <type_traits>
 
 #include "sta_kernels.h"
+#include "sta_plan.h"
 
 namespace sta {
 namespace {
@@ -24,230 +26,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.69314718055994531f;
-constexpr int kXcds = 8;  // MI355X dispatches workgroups round-robin over 8 XCDs
-
-// Parameters shared by both kernels.
-struct AttnParams {
-  const void* q;
-  const void* k;
-  const void* v;
-  void* out;
-  float* lse;       // optional: log-sum-exp of every query row (natural log)
-  int S;            // tokens per (batch, head)
-  int heads;
-  int n_tasks;      // work items
-  int per_xcd;      // workgroups each XCD runs (the grid is kXcds * per_xcd)
-  int group;        // logical tasks an XCD takes in a row before the next XCD's turn
-  int row_blocks;   // work items per query unit
-  int n_units;      // query units per (batch, head): tiles, or 1 if dense
-  int unit_rows;    // rows per query unit: tau, or S if dense
-  float scale_log2; // scale * log2(e)
-  int dense;
-  int nt, nh, nw, tau;
-  int H, W, ct, ch, cw;  // volume and tile, for raster-order addressing
-  int T;
-  int pad;               // the tile grid reaches past the volume (padded tiles)
-  // Raster order, key chunks of 64 rows that each lie inside one t-plane of
-  // one tile (64 divides c_h * c_w, c_w divides 64, tau a multiple of 64):
-  // chunks per tile and per plane. 0 when that does not hold.
-  int plane_cpt, plane_cpp;
-  uint16_t omega[STA_MAX_HEADS][3];
-  uint8_t head_order[STA_MAX_HEADS];  // logical head slot -> head (heaviest windows first)
-};
-
-
-// Maps the hardware workgroup id to a logical task so that consecutive
-// logical tasks (the row blocks of one query tile, then neighbouring tiles
-// that share most of their keys) run on the same XCD and share its L2.
-__device__ __forceinline__ int logical_task(const AttnParams& p) {
-  const int bid = blockIdx.x;
-  const int x = bid % kXcds, r = bid / kXcds;
-  return (r / p.group) * (kXcds * p.group) + x * p.group + r % p.group;
-}
-
-// Host side: order the work and size the grid. With equal windows on every
-// head, each XCD takes one contiguous share of the tasks (group = share), so
-// neighbouring tiles, which read mostly the same keys, meet in one L2. With
-// unequal windows the heads are ordered by window size, heaviest first, and
-// the XCDs take turns in blocks of kMixedGroup tasks: every XCD then gets the
-// same mix of heavy and light work, and the light work comes last.
-constexpr int kMixedGroup = 32;
-
-// Host side: plane_cpt / plane_cpp of a sparse problem (needs tau, ch, cw).
-inline void set_plane_chunks(AttnParams* p) {
-  const int plane = p->ch * p->cw;
-  if (!p->pad && p->tau % 64 == 0 && plane % 64 == 0 && 64 % p->cw == 0) {
-    p->plane_cpt = p->tau / 64;
-    p->plane_cpp = plane / 64;
-  } else {
-    p->plane_cpt = p->plane_cpp = 0;
-  }
-}
-
-inline void plan_tasks(AttnParams* p, long long tasks, int heads, bool dense) {
-  p->n_tasks = (int)tasks;
-  int cost[STA_MAX_HEADS];
-  bool equal = true;
-  for (int h = 0; h < heads; ++h) {
-    cost[h] = dense ? 1 : p->omega[h][0] * p->omega[h][1] * p->omega[h][2];
-    p->head_order[h] = (uint8_t)h;
-    equal = equal && cost[h] == cost[0];
-  }
-  const long long share = (tasks + kXcds - 1) / kXcds;
-  if (equal) {
-    p->group = (int)(share > 0 ? share : 1);
-    p->per_xcd = p->group;
-    return;
-  }
-  for (int i = 1; i < heads; ++i) {  // stable insertion sort, descending cost
-    const uint8_t h = p->head_order[i];
-    int j = i;
-    while (j > 0 && cost[p->head_order[j - 1]] < cost[h]) {
-      p->head_order[j] = p->head_order[j - 1];
-      --j;
-    }
-    p->head_order[j] = h;
-  }
-  p->group = kMixedGroup;
-  const long long blocks = (tasks + (long long)kXcds * kMixedGroup - 1) / ((long long)kXcds * kMixedGroup);
-  p->per_xcd = (int)(blocks * kMixedGroup);
-}
-
-// Key runs of one work item: `runs` runs of `run_len` tokens; run r starts at
-// token run_start(r).
-struct KvRuns {
-  int runs, run_len;
-  int oh;             // omega_h (runs per t-step)
-  int st, sh, sw;     // window start in tiles
-  int nh, nw, tau;
-  int dense;
-  // Token index (tile-major order) of run r's first key.
-  __device__ __forceinline__ int run_start(int r) const {
-    if (dense) return 0;
-    const int it = r / oh, ih = r - (r / oh) * oh;
-    return (((st + it) * nh + (sh + ih)) * nw + sw) * tau;
-  }
-  // Raster token index of run r's first key (the run's tile-major key e sits
-  // at this plus the run offset table entry e).
-  __device__ __forceinline__ int run_start_raster(int r, int H, int W, int ct, int ch, int cw) const {
-    const int it = r / oh, ih = r - (r / oh) * oh;
-    return (((st + it) * ct) * H + (sh + ih) * ch) * W + sw * cw;
-  }
-};
-
-struct Task {
-  long long head_base;  // element offset of this (batch, head)
-  int row0;             // first query row (token index) of the work item
-  int valid_rows;       // rows of the work item inside its unit
-  int local0;           // first row of the work item within its unit
-  int qt, qh, qw;       // query tile coordinates (STA)
-  KvRuns kv;
-};
-
-// Whether row `local` (tile-major order inside the tile) of tile (qt, qh, qw)
-// is a token of the volume (false for padding positions of a partly padded
-// tile).
-__device__ __forceinline__ bool tile_row_real(const AttnParams& p, int qt, int qh, int qw, int local) {
-  const int plane = p.ch * p.cw;
-  const int lt = local / plane;
-  const int rem = local - lt * plane;
-  const int lh = rem / p.cw;
-  const int lw = rem - lh * p.cw;
-  return qt * p.ct + lt < p.T && qh * p.ch + lh < p.H && qw * p.cw + lw < p.W;
-}
-
-// Whether run r of a walk reaches past the volume (only then can its keys
-// include padding positions).
-__device__ __forceinline__ bool run_padded(const AttnParams& p, const KvRuns& kv, int r) {
-  const int it = r / kv.oh, ih = r - (r / kv.oh) * kv.oh;
-  const int tiles_w = kv.run_len / kv.tau;
-  return (kv.st + it + 1) * p.ct > p.T || (kv.sh + ih + 1) * p.ch > p.H ||
-         (kv.sw + tiles_w) * p.cw > p.W;
-}
-
-// Whether key e (tile-major order within the run) of run r is a token.
-__device__ __forceinline__ bool run_key_real(const AttnParams& p, const KvRuns& kv, int r, int e) {
-  const int it = r / kv.oh, ih = r - (r / kv.oh) * kv.oh;
-  const int tw = e / p.tau;
-  return tile_row_real(p, kv.st + it, kv.sh + ih, kv.sw + tw, e - tw * p.tau);
-}
-
-// Raster token index of row `local` (tile-major order inside the tile) of
-// query tile (qt, qh, qw).
-__device__ __forceinline__ int tile_row_raster(const AttnParams& p, int qt, int qh, int qw, int local) {
-  const int plane = p.ch * p.cw;
-  const int lt = local / plane;
-  const int rem = local - lt * plane;
-  const int lh = rem / p.cw;
-  const int lw = rem - lh * p.cw;
-  return ((qt * p.ct + lt) * p.H + qh * p.ch + lh) * p.W + qw * p.cw + lw;
-}
-
-// Raster offset, relative to the run's first key, of key e of a window run
-// (tile-major order within the run: tile along w, then the tile's tokens).
-__device__ __forceinline__ int run_offset_raster(const AttnParams& p, int e) {
-  const int tw = e / p.tau;
-  const int local = e - tw * p.tau;
-  const int plane = p.ch * p.cw;
-  const int lt = local / plane;
-  const int rem = local - lt * plane;
-  const int lh = rem / p.cw;
-  const int lw = rem - lh * p.cw;
-  return (lt * p.H + lh) * p.W + tw * p.cw + lw;
-}
-
-// Work item `task`: its (batch, head), its block of rows inside one unit, and
-// the runs of the other side it walks. Forward (KEYS = false): the unit is a
-// query tile and the runs cover the key tiles of its window. Backward over
-// keys (KEYS = true): the unit is a key tile and the runs cover the query
-// tiles whose window holds it (per axis an interval, window_inverse).
-template <int ROWS, bool KEYS = false>
-__device__ __forceinline__ Task decode_task(const AttnParams& p, int task, int D) {
-  Task t;
-  const int rb = task % p.row_blocks;
-  const int unit_bh = task / p.row_blocks;
-  const int unit = unit_bh % p.n_units;
-  const int bh = unit_bh / p.n_units;
-  const int h = p.head_order[bh % p.heads];
-  t.head_base = ((long long)(bh / p.heads) * p.heads + h) * p.S * D;
-  const int unit_row0 = unit * p.unit_rows;
-  t.row0 = unit_row0 + rb * ROWS;
-  t.local0 = rb * ROWS;
-  t.valid_rows = min(ROWS, p.unit_rows - rb * ROWS);
-  t.qt = t.qh = t.qw = 0;
-  KvRuns& kv = t.kv;
-  kv.dense = p.dense;
-  kv.nh = p.nh; kv.nw = p.nw; kv.tau = p.tau;
-  if (p.dense) {
-    kv.runs = 1; kv.run_len = p.S; kv.oh = 1; kv.st = kv.sh = kv.sw = 0;
-  } else {
-    const int ot = p.omega[h][0], oh = p.omega[h][1], ow = p.omega[h][2];
-    const int qw = unit % p.nw;
-    const int qh = (unit / p.nw) % p.nh;
-    const int qt = unit / (p.nw * p.nh);
-    t.qt = qt; t.qh = qh; t.qw = qw;
-    if (KEYS) {
-      int lo_t, hi_t, lo_h, hi_h, lo_w, hi_w;
-      window_inverse(qt, p.nt, ot, &lo_t, &hi_t);
-      window_inverse(qh, p.nh, oh, &lo_h, &hi_h);
-      window_inverse(qw, p.nw, ow, &lo_w, &hi_w);
-      kv.st = lo_t; kv.sh = lo_h; kv.sw = lo_w;
-      kv.oh = hi_h - lo_h + 1;
-      kv.runs = (hi_t - lo_t + 1) * kv.oh;
-      kv.run_len = (hi_w - lo_w + 1) * p.tau;
-    } else {
-      kv.st = window_start(qt, p.nt, ot);
-      kv.sh = window_start(qh, p.nh, oh);
-      kv.sw = window_start(qw, p.nw, ow);
-      kv.oh = oh;
-      kv.runs = ot * oh;
-      kv.run_len = ow * p.tau;
-    }
-  }
-  return t;
-}
+// The logical task of this workgroup (task_of_block).
+__device__ __forceinline__ int logical_task(const AttnParams& p) { return task_of_block(p, blockIdx.x); }
 
 // Max / sum of x over the four lanes l, l^16, l^32, l^48 (the lanes that
 // hold one query row in the MFMA output layouts). A permlane swap of x with
@@ -447,51 +227,6 @@ __device__ __forceinline__ RowMap<C, RB> map_rows(const AttnParams& p, const Tas
   return rm;
 }
 
-// Walks the key chunks of a work item: chunk `it` covers keys
-// row0(it) .. + BN of the head, of which nvalid(it) are inside the run.
-struct ChunkWalk {
-  int chunks_per_run, n_chunks, run_len, bn;
-  KvRuns kv;
-  bool dense;
-  __device__ __forceinline__ void at(int it, int* row0, int* nvalid) const {
-    const int run = it / chunks_per_run;
-    const int c0 = (it - run * chunks_per_run) * bn;
-    *row0 = (dense ? 0 : kv.run_start(run)) + c0;
-    *nvalid = min(bn, run_len - c0);
-  }
-  // Raster order, plane chunks: the raster token of the chunk's first key
-  // (the chunk is one 64-row piece of one t-plane of one tile).
-  __device__ __forceinline__ int at_plane(const AttnParams& p, int it) const {
-    const int run = it / chunks_per_run;
-    const int j = it - run * chunks_per_run;
-    const int tw = j / p.plane_cpt;
-    const int pp = j - tw * p.plane_cpt;
-    const int lt = pp / p.plane_cpp;
-    const int sub = pp - lt * p.plane_cpp;
-    return kv.run_start_raster(run, p.H, p.W, p.ct, p.ch, p.cw) +
-           (lt * p.H + sub * (64 / p.cw)) * p.W + tw * p.cw;
-  }
-  // Tile-major order on a padded grid: the first row of the tile the chunk
-  // starts in (a token: every tile starts inside the volume), the chunk's
-  // first key relative to it, and the number of valid keys.
-  __device__ __forceinline__ void at_tile(int it, int tau, int* tile_row0, int* key_base,
-                                          int* nvalid) const {
-    const int run = it / chunks_per_run;
-    const int c0 = (it - run * chunks_per_run) * bn;
-    *key_base = c0 % tau;
-    *tile_row0 = (dense ? 0 : kv.run_start(run)) + c0 - *key_base;
-    *nvalid = min(bn, run_len - c0);
-  }
-  // Raster order: the run's first raster token, the chunk's first key within
-  // the run, and the number of valid keys.
-  __device__ __forceinline__ void at_raster(const AttnParams& p, int it, int* base, int* c0,
-                                            int* nvalid) const {
-    const int run = it / chunks_per_run;
-    *c0 = (it - run * chunks_per_run) * bn;
-    *base = kv.run_start_raster(run, p.H, p.W, p.ct, p.ch, p.cw);
-    *nvalid = min(bn, run_len - *c0);
-  }
-};
 
 // Bit k set iff key k (0..63) of chunk `it` is a token of the volume: all
 // ones unless the problem is padded (PAD, a kernel variant of its own so that
@@ -508,17 +243,6 @@ __device__ __forceinline__ unsigned long long chunk_real_keys(const AttnParams& 
   return __ballot(real);
 }
 
-template <int BN, bool DENSE>
-__device__ __forceinline__ ChunkWalk make_walk(const Task& t, int S) {
-  ChunkWalk cw;
-  cw.kv = t.kv;
-  cw.dense = DENSE;
-  cw.run_len = DENSE ? S : t.kv.run_len;
-  cw.bn = BN;
-  cw.chunks_per_run = (cw.run_len + BN - 1) / BN;
-  cw.n_chunks = (DENSE ? 1 : t.kv.runs) * cw.chunks_per_run;
-  return cw;
-}
 
 }  // namespace
 }  // namespace sta

@@ -32,15 +32,6 @@
 namespace sta {
 namespace {
 
-struct BwdParams {
-  const void* dout;    // dO, same shape and order as q
-  const float* lse;    // [B][heads][S] forward log-sum-exp (natural log)
-  float* delta;        // [B][heads][S] D = dO . O (written by delta_kernel)
-  void* dq;
-  void* dk;
-  void* dv;
-  float scale;
-};
 
 // ---------------------------------------------------------------------------
 // D = rowsum(dO * O)
@@ -482,10 +473,195 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
 }
 
 // ---------------------------------------------------------------------------
+// dkdv kernel with paired waves (own rows: keys, 16 * RB per pair)
+// ---------------------------------------------------------------------------
+// The one-wave-per-16-keys kernel above reads every streamed Q and dO
+// fragment from LDS for a single MFMA, twice per chunk (row-wise and
+// transposed), which makes the LDS, not the matrix cores, its bound. Here a
+// pair of waves shares 16 * RB key rows and splits the four products:
+//   wave P (waves 0 .. PAIRS-1):  S = Q K^T, P = exp(S - lse),   dV^T += dO^T P
+//   wave S (waves PAIRS ..):      dP = dO V^T, dS = P * (dP - D), dK^T += Q^T dS
+// Each wave issues the same number of MFMAs as before, but every fragment it
+// reads feeds RB of them. Wave S takes P from wave P through LDS (bf16, the
+// values wave P multiplies dO by), after a second barrier per chunk; wave S
+// reads it before it reaches the next chunk's first barrier, so one P buffer
+// per pair suffices.
+template <int D, int PAIRS, int RB, int BN, bool RASTER, bool PAD, bool FULL>
+__global__ void __launch_bounds__(2 * PAIRS * 64, 1)
+bwd_dkdv_pair_kernel(const AttnParams p, const BwdParams b) {
+  constexpr int WAVES = 2 * PAIRS;
+  using C = Bf16Cfg<D, WAVES, RB, BN>;
+  static_assert(BN == 64, "one wave loads the chunk's lse and D rows");
+  constexpr int kRows = PAIRS * 16 * RB;   // key rows per work item
+  __shared__ __attribute__((aligned(1024))) char qb0[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char ob0[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char qb1[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char ob1[C::kChunkBytes];
+  __shared__ __attribute__((aligned(256))) float lb0[BN];
+  __shared__ __attribute__((aligned(256))) float db0[BN];
+  __shared__ __attribute__((aligned(256))) float lb1[BN];
+  __shared__ __attribute__((aligned(256))) float db1[BN];
+  // P of the current chunk per pair: slot j (rb * kKP + kp) of lane l at
+  // pbuf[pair][j][l], 16 bytes each (contiguous per instruction).
+  __shared__ __attribute__((aligned(1024))) bf16x8 pbuf[PAIRS][RB * C::kKP][64];
+  extern __shared__ int rtab[];
+
+  const int task = logical_task(p);
+  if (task >= p.n_tasks) return;
+  const Task t = decode_task<kRows, true>(p, task, D);
+  const long long rowbase = t.head_base / D;
+  const bf16_t* qg = static_cast<const bf16_t*>(p.q) + t.head_base;
+  const bf16_t* kg = static_cast<const bf16_t*>(p.k) + t.head_base;
+  const bf16_t* vg = static_cast<const bf16_t*>(p.v) + t.head_base;
+  const bf16_t* dog = static_cast<const bf16_t*>(b.dout) + t.head_base;
+  const float* lseg = b.lse + rowbase;
+  const float* delg = b.delta + rowbase;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pair = wave % PAIRS;
+  const bool wave_p = wave < PAIRS;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const ChunkWalk walk = make_walk<BN, false>(t, p.S);
+  if (RASTER) {
+    for (int e = threadIdx.x; e < walk.run_len; e += C::kThreads) rtab[e] = run_offset_raster(p, e);
+    __syncthreads();
+  }
+  auto dma = [&](int it, char* qdst, char* odst, float* ldst, float* ddst)
+                 __attribute__((always_inline)) {
+    int base, c0 = 0, nv;
+    const int* tab = nullptr;
+    if (RASTER) {
+      walk.at_raster(p, it, &base, &c0, &nv);
+      tab = rtab + c0;
+    } else if (PAD) {
+      walk.at_tile(it, p.tau, &base, &c0, &nv);   // padding rows load the tile's first row
+    } else {
+      walk.at(it, &base, &nv);
+    }
+    const int kb = RASTER ? 0 : c0;
+    const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
+    load_rows<C, WAVES>(qg, base, nv, qdst, wave, lane, tab, real, kb);
+    load_rows<C, WAVES>(dog, base, nv, odst, wave, lane, tab, real, kb);
+    if (wave == 0) {
+      load_row_values(lseg, base, nv, ldst, lane, tab, real, kb);
+      load_row_values(delg, base, nv, ddst, lane, tab, real, kb);
+    }
+  };
+  dma(0, qb0, ob0, lb0, db0);
+
+  // Own key rows: rows 16 * RB * pair + 16 * rb + l16 of the work item.
+  const RowMap<C, RB> rm = map_rows<C, RB, RASTER>(p, t, pair, l16);
+  int koff[C::kDK], voff[C::kDB];
+  lane_koff<C>(koff, l16, g);
+  lane_voff<C>(voff, l16, g);
+  // Whether query row 16*kt + 4g + r of chunk `it` is a token (else its P and
+  // dS are zero by selection: its lse / D may be garbage).
+  auto row_off = [&](int nvalid, unsigned long long real, int kt, int r) __attribute__((always_inline)) {
+    const int qrow = 16 * kt + 4 * g + r;
+    return !FULL && ((nvalid < C::kBN && qrow >= nvalid) || !((real >> qrow) & 1ull));
+  };
+
+  if (wave_p) {
+    bf16x8 kf[RB][C::kDK];
+    load_frags<C, RB>(kf, static_cast<const bf16_t*>(kg), rm, g);
+    f32x4 dv[RB][C::kDB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) dv[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto step = [&](const char* qcur, const char* ocur, const float* lcur, char* qnxt, char* onxt,
+                    float* lnxt, float* dnxt, int it) __attribute__((always_inline)) {
+      int row0, nvalid;
+      walk.at(it, &row0, &nvalid);
+      wait_vm_all();
+      __syncthreads();
+      const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
+      f32x4 s[RB][C::kKT];
+      mma_rows<C, RB>(s, qcur, koff, kf);    // S[q][key] = Q K^T
+      sched_phase<RB, C::kKT * C::kDK, 1, 3, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      if (it + 1 < walk.n_chunks) dma(it + 1, qnxt, onxt, lnxt, dnxt);
+      f32x4 lq[C::kKT];
+#pragma unroll
+      for (int kt = 0; kt < C::kKT; ++kt) lq[kt] = *reinterpret_cast<const f32x4*>(lcur + 16 * kt + 4 * g);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kt = 0; kt < C::kKT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -lq[kt][r] * kLog2e));
+            s[rb][kt][r] = row_off(nvalid, real, kt, r) ? 0.f : pr;   // P[q][key]
+          }
+      bf16x8 wf[RB][C::kKP];
+      pack_bf16<C, RB>(wf, s);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kp = 0; kp < C::kKP; ++kp) pbuf[pair][rb * C::kKP + kp][lane] = wf[rb][kp];
+      __syncthreads();                        // P of this chunk is visible to wave S
+      mma_tr<C, RB>(dv, ocur, voff, wf);     // dV^T[d][key] += dO^T P
+      sched_phase<RB, C::kKP * C::kDB, 2, 2, 0>();
+    };
+    for (int it = 0; it < walk.n_chunks; it += 2) {
+      step(qb0, ob0, lb0, qb1, ob1, lb1, db1, it);
+      if (it + 1 < walk.n_chunks) step(qb1, ob1, lb1, qb0, ob0, lb0, db0, it + 1);
+    }
+    store_rows<C, RB>(dv, static_cast<bf16_t*>(b.dv) + t.head_base, rm, g, 1.0f);
+  } else {
+    bf16x8 vf[RB][C::kDK];
+    load_frags<C, RB>(vf, vg, rm, g);
+    f32x4 dk[RB][C::kDB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) dk[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto step = [&](const char* qcur, const char* ocur, const float* dcur, char* qnxt, char* onxt,
+                    float* lnxt, float* dnxt, int it) __attribute__((always_inline)) {
+      int row0, nvalid;
+      walk.at(it, &row0, &nvalid);
+      wait_vm_all();
+      __syncthreads();
+      const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
+      f32x4 dp[RB][C::kKT];
+      mma_rows<C, RB>(dp, ocur, koff, vf);   // dP[q][key] = dO V^T
+      sched_phase<RB, C::kKT * C::kDK, 1, 3, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      if (it + 1 < walk.n_chunks) dma(it + 1, qnxt, onxt, lnxt, dnxt);
+      f32x4 dq_[C::kKT];
+#pragma unroll
+      for (int kt = 0; kt < C::kKT; ++kt) dq_[kt] = *reinterpret_cast<const f32x4*>(dcur + 16 * kt + 4 * g);
+      __syncthreads();                        // wave P has written this chunk's P
+      bf16x8 wd[RB][C::kKP];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kp = 0; kp < C::kKP; ++kp) {
+          const bf16x8 pw = pbuf[pair][rb * C::kKP + kp][lane];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            // slot j holds query row 32*kp + 4g + j (j < 4), or + 16 + (j - 4)
+            const int kt = 2 * kp + j / 4, r = j % 4;
+            const float ds = static_cast<float>(pw[j]) * (dp[rb][kt][r] - dq_[kt][r]);
+            wd[rb][kp][j] = static_cast<bf16_t>(row_off(nvalid, real, kt, r) ? 0.f : ds);
+          }
+        }
+      mma_tr<C, RB>(dk, qcur, voff, wd);     // dK^T[d][key] += Q^T dS
+      sched_phase<RB, C::kKP * C::kDB, 2, 2, 0>();
+    };
+    for (int it = 0; it < walk.n_chunks; it += 2) {
+      step(qb0, ob0, db0, qb1, ob1, lb1, db1, it);
+      if (it + 1 < walk.n_chunks) step(qb1, ob1, db1, qb0, ob0, lb0, db0, it + 1);
+    }
+    store_rows<C, RB>(dk, static_cast<bf16_t*>(b.dk) + t.head_base, rm, g, b.scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // f32 kernels: one wavefront per own row
 // ---------------------------------------------------------------------------
-
-constexpr int kF32Waves = 4;
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -602,33 +778,6 @@ __global__ void __launch_bounds__(kF32Waves * 64) bwd_f32_dkdv_kernel(const Attn
 // Launch
 // ---------------------------------------------------------------------------
 
-void fill_bwd_params(const BwdProblem& pr, int rows_per_item, AttnParams* p, BwdParams* b) {
-  const AttnProblem& a = pr.attn;
-  p->q = a.q; p->k = a.k; p->v = a.v; p->out = a.out;
-  p->lse = nullptr;
-  p->S = a.raster ? a.g.S : a.g.S_pad;
-  p->heads = a.heads;
-  p->dense = 0;
-  p->scale_log2 = a.scale * kLog2e;
-  p->n_units = a.g.n_tiles;
-  p->unit_rows = a.g.tau;
-  p->nt = a.g.nt; p->nh = a.g.nh; p->nw = a.g.nw;
-  p->tau = a.g.tau;
-  p->T = a.g.T; p->H = a.g.H; p->W = a.g.W;
-  p->pad = a.g.padded;
-  p->ct = a.g.ct; p->ch = a.g.ch; p->cw = a.g.cw;
-  set_plane_chunks(p);
-  for (int h = 0; h < a.heads; ++h)
-    for (int x = 0; x < 3; ++x) p->omega[h][x] = a.omega[h][x];
-  p->row_blocks = (p->unit_rows + rows_per_item - 1) / rows_per_item;
-  const long long tasks = (long long)a.B * a.heads * p->n_units * p->row_blocks;
-  plan_tasks(p, tasks, a.heads, false);
-  b->dout = pr.dout;
-  b->lse = pr.lse;
-  b->delta = pr.delta;
-  b->dq = pr.dq; b->dk = pr.dk; b->dv = pr.dv;
-  b->scale = a.scale;
-}
 
 // LDS for the raster offsets of the longest run: omega_w * tau keys for the
 // query side, the longest transposed interval along w times tau for the key
@@ -687,14 +836,50 @@ int launch_bf16_pass(const BwdProblem& pr, hipStream_t stream) {
   return (int)hipGetLastError();
 }
 
+// Key side with paired waves: PAIRS pairs of 16 * RB key rows.
+template <int D, int PAIRS, int RB>
+int launch_bf16_pair_pass(const BwdProblem& pr, hipStream_t stream) {
+  constexpr int kThreads = 2 * PAIRS * 64;
+  AttnParams p;
+  BwdParams b;
+  fill_bwd_params(pr, PAIRS * 16 * RB, &p, &b);
+  const unsigned grid = (unsigned)p.per_xcd * kXcds;
+  const bool raster = pr.attn.raster;
+  const unsigned lds = raster ? raster_bytes(pr.attn, true) : 0;
+  if (pr.attn.g.padded) {
+    if (raster)
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, PAIRS, RB, 64, true, true, false>), dim3(grid), dim3(kThreads), lds, stream, p, b);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, PAIRS, RB, 64, false, true, false>), dim3(grid), dim3(kThreads), 0, stream, p, b);
+  } else if (pr.attn.g.tau % 64 == 0) {
+    if (raster)
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, PAIRS, RB, 64, true, false, true>), dim3(grid), dim3(kThreads), lds, stream, p, b);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, PAIRS, RB, 64, false, false, true>), dim3(grid), dim3(kThreads), 0, stream, p, b);
+  } else {
+    if (raster)
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, PAIRS, RB, 64, true, false, false>), dim3(grid), dim3(kThreads), lds, stream, p, b);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, PAIRS, RB, 64, false, false, false>), dim3(grid), dim3(kThreads), 0, stream, p, b);
+  }
+  return (int)hipGetLastError();
+}
+
+#ifndef STA_CFG_BWD_PAIRS
+#define STA_CFG_BWD_PAIRS 1
+#endif
+
 template <int D>
 int launch_bf16_bwd(const BwdProblem& pr, hipStream_t stream) {
-  // Key side: 16 key rows per wave; query side: 32 query rows per wave.
-  int rc = pr.attn.g.tau >= 128 ? launch_bf16_pass<D, 8, 1, true>(pr, stream)
-                                : launch_bf16_pass<D, 4, 1, true>(pr, stream);
+  // Key side: pairs of waves sharing 32 key rows (or 16 key rows per wave on
+  // small tiles); query side: 32 query rows per wave.
+  const int tau = pr.attn.g.tau;
+  int rc = bwd_key_rows(tau) == 128 ? (STA_CFG_BWD_PAIRS ? launch_bf16_pair_pass<D, 4, 2>(pr, stream)
+                                                         : launch_bf16_pass<D, 8, 1, true>(pr, stream))
+                                    : launch_bf16_pass<D, 4, 1, true>(pr, stream);
   if (rc) return rc;
-  return pr.attn.g.tau >= 128 ? launch_bf16_pass<D, 4, 2, false>(pr, stream)
-                              : launch_bf16_pass<D, 4, 1, false>(pr, stream);
+  return bwd_query_rows(tau) == 128 ? launch_bf16_pass<D, 4, 2, false>(pr, stream)
+                                    : launch_bf16_pass<D, 4, 1, false>(pr, stream);
 }
 
 template <int D>

@@ -73,6 +73,8 @@ def short_name(n: str) -> str:
 
 def role(name: str) -> str:
     """What a kernel is, from its name and template arguments."""
+    if "bwd_dkdv_pair_kernel" in name:
+        return "STA backward, key side (dK, dV), paired waves"
     if "bwd_dkdv_kernel" in name or "bwd_f32_dkdv" in name:
         return "STA backward, key side (dK, dV)"
     if "bwd_dq_kernel" in name or "bwd_f32_dq" in name:
