@@ -5,14 +5,16 @@
 RUN_DIR holds what one profiling session of bench.py wrote:
   bench.json                 bench.py's JSON line, run without a profiler
   trace/bench_kernel_stats.csv
-      rocprofv3 --kernel-trace --stats -d RUN_DIR/trace -o bench -f csv -- python3 bench.py
+      rocprofv3 --kernel-trace --stats -d RUN_DIR/trace -o bench -f csv -- python3 bench.py --cpu none
   FETCH_SIZE/run_counter_collection.csv, WRITE_SIZE/run_counter_collection.csv
       rocprofv3 --pmc <counter> --kernel-trace -d RUN_DIR/<counter> -o run -f csv --
-          python3 bench.py --steps 2 --warmup 1 --cpu-budget 0 --dense-reps 1
+          python3 bench.py --steps 2 --warmup 1 --cpu none --dense-reps 1
           --compare-reps 1 --copy-reference
   MFMA/run_counter_collection.csv (optional)
       rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace
           -d RUN_DIR/MFMA -o run -f csv -- python3 bench.py <same arguments>
+  PIPE/run_counter_collection.csv, LDS/run_counter_collection.csv (optional)
+      the same with the PIPE_COUNTERS and LDS_COUNTERS sets below (one pass each)
 
 Writes, for the workload named in bench.json, a kernel-time table, an HBM
 traffic table, and per path (fused, three_call) a JSON record of the bytes
@@ -38,12 +40,18 @@ KERNEL_SOURCES = (
     "sparse_attention_video_tile_amd/csrc/sta_attn_common.h",
     "sparse_attention_video_tile_amd/csrc/sta_geometry.h",
     "sparse_attention_video_tile_amd/csrc/sta_kernels.h",
+    "sparse_attention_video_tile_amd/csrc/sta_plan.h",
 )
-TRACE_CMD = "rocprofv3 --kernel-trace --stats -d <outdir> -o bench -f csv -- python3 bench.py"
-PMC_ARGS = "--steps 2 --warmup 1 --cpu-budget 0 --dense-reps 1 --compare-reps 1 --copy-reference"
+TRACE_CMD = "rocprofv3 --kernel-trace --stats -d <outdir> -o bench -f csv -- python3 bench.py --cpu none"
+PMC_ARGS = "--steps 2 --warmup 1 --cpu none --dense-reps 1 --compare-reps 1 --copy-reference"
 
 
 MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE"
+# Issue and wait profile; LDS profile (each within one pass's counter limits).
+PIPE_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_VALU "
+                 "SQ_INSTS_MFMA SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_WAVE_CYCLES GRBM_GUI_ACTIVE")
+LDS_COUNTERS = ("SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS "
+                "SQ_INSTS_LDS_LOAD_BANDWIDTH SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
 N_CU = 256          # MI355X compute units
 SIMD_PER_CU = 4
 
@@ -68,6 +76,8 @@ def short_name(n: str) -> str:
         return "torch float32->bf16 cast (input generation)"
     if "copyBuffer" in n:
         return "HIP runtime copyBuffer (plain device copy)"
+    if "delta_kernel" in n and n.startswith("_Z"):   # reported mangled
+        return "delta_kernel"
     return n[:90]
 
 
@@ -127,6 +137,74 @@ def per_dispatch(path: str, counter: str = None):
         k = (int(r["Dispatch_Id"]), r["Kernel_Name"])
         agg[k] = agg.get(k, 0.0) + float(r["Counter_Value"])
     return agg
+
+
+def all_counters(path: str):
+    """{(dispatch, kernel): {counter: value summed over instances}}."""
+    agg = collections.OrderedDict()
+    for r in csv.DictReader(open(path)):
+        k = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+        c = agg.setdefault(k, collections.defaultdict(float))
+        c[r["Counter_Name"]] += float(r["Counter_Value"])
+    return agg
+
+
+def pipeline_summary(run: str, out: str, bench: dict, title: str) -> None:
+    """Per kernel: where the SIMDs' cycles go (MFMA, VALU, both, waiting) and
+    how hard the LDS is driven, from the PIPE and LDS counter passes."""
+    ppath = os.path.join(run, "PIPE", "run_counter_collection.csv")
+    lpath = os.path.join(run, "LDS", "run_counter_collection.csv")
+    if not (os.path.exists(ppath) and os.path.exists(lpath)):
+        return
+    pipe, lds = all_counters(ppath), all_counters(lpath)
+
+    def mean_by_kernel(agg, fn):
+        vals = collections.defaultdict(list)
+        for (_, n), c in agg.items():
+            if role(n) and c.get("GRBM_GUI_ACTIVE"):
+                vals[n].append(fn(c))
+        return {n: sum(v) / len(v) for n, v in vals.items()}
+
+    simd_cycles = lambda c: c["GRBM_GUI_ACTIVE"] / N_XCD * N_CU * SIMD_PER_CU
+    cu_cycles = lambda c: c["GRBM_GUI_ACTIVE"] / N_XCD * N_CU
+    cols = {
+        "mfma": mean_by_kernel(pipe, lambda c: c["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles(c)),
+        "valu": mean_by_kernel(pipe, lambda c: 4 * c["SQ_ACTIVE_INST_VALU"] / simd_cycles(c)),
+        "coexec": mean_by_kernel(pipe, lambda c: c["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd_cycles(c)),
+        "wait": mean_by_kernel(pipe, lambda c: c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"]),
+        "waitinst": mean_by_kernel(pipe, lambda c: c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]),
+        "vpm": mean_by_kernel(pipe, lambda c: c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"]
+                              if c["SQ_INSTS_MFMA"] else float("nan")),
+        "ldsbw": mean_by_kernel(lds, lambda c: 64 * c["SQ_INSTS_LDS_LOAD_BANDWIDTH"] / cu_cycles(c)),
+        "conf": mean_by_kernel(lds, lambda c: c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_LDS_IDX_ACTIVE"], 1)),
+        "ldswait": mean_by_kernel(lds, lambda c: c["SQ_WAIT_INST_LDS"] / max(c["SQ_ACTIVE_INST_LDS"], 1)),
+    }
+    L = [f"# Issue, wait and LDS profile per kernel, bench.py on {title}\n",
+         "Commands (repo root), one pass each:\n",
+         f"```\nrocprofv3 --pmc {PIPE_COUNTERS} --kernel-trace -d <outdir> -o run -f csv -- "
+         f"python3 bench.py {PMC_ARGS}\n"
+         f"rocprofv3 --pmc {LDS_COUNTERS} --kernel-trace -d <outdir> -o run -f csv -- "
+         f"python3 bench.py {PMC_ARGS}\n```\n",
+         "Per dispatch, averaged over each kernel's dispatches. SIMD cycles = GRBM_GUI_ACTIVE / "
+         f"{N_XCD} x {N_CU} CUs x {SIMD_PER_CU}. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / SIMD cycles; "
+         "VALU issuing = 4 x SQ_ACTIVE_INST_VALU (quad-cycles) / SIMD cycles; both = "
+         "SQ_VALU_MFMA_COEXEC_CYCLES / SIMD cycles (a VALU instruction running beside an MFMA); "
+         "waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES (share of a wave's life at a wait count or a "
+         "barrier), not issuing = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; VALU / MFMA = SQ_INSTS_VALU / "
+         "SQ_INSTS_MFMA (the VALU count includes the MFMAs); LDS read B/clk per CU = 64 x "
+         "SQ_INSTS_LDS_LOAD_BANDWIDTH / CU cycles; bank-conflict share = SQ_LDS_BANK_CONFLICT / "
+         "SQ_LDS_IDX_ACTIVE; LDS wait per LDS instruction = SQ_WAIT_INST_LDS / "
+         "SQ_ACTIVE_INST_LDS.\n",
+         "| kernel | role | MFMA busy | VALU issuing | both | waiting | not issuing | VALU / MFMA | "
+         "LDS read B/clk/CU | bank-conflict share | LDS wait per LDS inst |",
+         "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for n in cols["mfma"]:
+        g = lambda k: cols[k].get(n, float("nan"))
+        L.append(f"| `{short_name(n)}` | {role(n)} | {100 * g('mfma'):.1f}% | {100 * g('valu'):.1f}% | "
+                 f"{100 * g('coexec'):.1f}% | {100 * g('wait'):.1f}% | {100 * g('waitinst'):.1f}% | "
+                 f"{'-' if g('vpm') != g('vpm') else format(g('vpm'), '.2f')} | {g('ldsbw'):.1f} | {100 * g('conf'):.1f}% | {g('ldswait'):.2f} |")
+    open(os.path.join(out, f"attn_{bench['dtype']}_{bench['config']['workload']}_pipeline.md"), "w").write(
+        "\n".join(L) + "\n")
 
 
 def main(argv=None) -> int:
@@ -302,6 +380,7 @@ def main(argv=None) -> int:
             L.append(f"| `{short_name(n)}` | {role(n)} | {len(fr)} | {100 * sum(fr) / len(fr):.1f}% | "
                      f"{(sum(clk) / len(clk)) if clk else float('nan'):.2f} |")
         open(os.path.join(out, f"attn_{bench['dtype']}_{wl}_mfma_busy.md"), "w").write("\n".join(L) + "\n")
+    pipeline_summary(run, out, bench, title)
     print(json.dumps({p: r["bytes_per_launch"] for p, r in records.items()}))
     return 0
 
