@@ -240,6 +240,26 @@ int sta_forward_fp8(const void* q8, const void* k8, const void* v, void* out, in
                     float scale, float q_descale, float k_descale, int order, void* stream);
 
 /*
+ * sta_forward_fp8 that also writes each query row's log-sum-exp of its scores
+ * on the decoded values,
+ *     lse_i = log sum_j exp(scale * (q_descale Q8_i) . (k_descale K8_j))
+ * over the row's window keys (natural log, float32, summing the probabilities
+ * as rounded to bfloat16 for the P V product, as sta_forward_lse does). The
+ * decoded values times a power-of-two descale are bfloat16 values, so
+ * training with fp8 scores (the fixed-window fine-tuning of the pages:
+ * podcast transcript, the answer on fine-tuning; atlas.scime.ai summary,
+ * "Approach") runs sta_backward on the decoded q and k with this lse.
+ *   lse: device float [B][heads][S], 4-byte aligned, token order `order`;
+ *        written. Must not overlap q8, k8, v or out.
+ * Output values are identical to sta_forward_fp8's. Other arguments, rules
+ * and errors as sta_forward_fp8.
+ */
+int sta_forward_fp8_lse(const void* q8, const void* k8, const void* v, void* out, float* lse, int B,
+                        int heads, int head_dim, int T, int H, int W, const int* tile,
+                        const int* window, float scale, float q_descale, float k_descale,
+                        int order, void* stream);
+
+/*
  * STA backward: gradients of sum(dout * O) with respect to q, k and v, for
  * training a model with a fixed STA window (the fine-tuning of the pages:
  * podcast transcript, the answer on fine-tuning; atlas.scime.ai summary,

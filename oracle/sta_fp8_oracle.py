@@ -22,6 +22,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from .sta_backward_oracle import sta_lse
 from .sta_oracle import sta_attention, sta_attention_rows
 
 
@@ -57,3 +58,16 @@ def sta_attention_fp8_rows(q8, k8, v, tile, window, scale, q_descale, k_descale,
     k = e4m3_decode(k8[b:b + 1, h:h + 1]) * float(k_descale)
     vv = np.asarray(v[b:b + 1, h:h + 1], dtype=np.float64)
     return sta_attention_rows(q, k, vv, tile, window, scale, 0, 0, query_tokens)
+
+
+def sta_lse_fp8(q8, k8, tile, windows, scale, q_descale, k_descale) -> np.ndarray:
+    """Row log-sum-exp (float64, raster order, shape (B, heads, T, H, W)) of the
+    STA scores on the decoded fp8 values, scale * (q_descale Q8_i) .
+    (k_descale K8_j), over each row's window keys: the probabilities a
+    fixed-window backward pass recomputes from (atlas.scime.ai summary,
+    "Approach": fine-tuning with the window fixed)."""
+    q = e4m3_decode(q8) * float(q_descale)
+    k = e4m3_decode(k8) * float(k_descale)
+    if not (np.all(np.isfinite(q)) and np.all(np.isfinite(k))):
+        raise ValueError("NaN code in q8 or k8")
+    return sta_lse(q, k, tile, windows, scale)

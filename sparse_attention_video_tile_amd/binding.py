@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libsta.so")
 STA_OK, STA_ERR_INVALID_ARG, STA_ERR_UNSUPPORTED, STA_ERR_HIP = 0, -1, -2, -3
 STA_BF16, STA_F32 = 0, 1
 STA_MAX_HEADS = 256
-ABI_VERSION = 4
+ABI_VERSION = 5
 STA_TILE_MAJOR, STA_RASTER = 0, 1
 
 EXPORTS = (
@@ -36,6 +36,7 @@ EXPORTS = (
     "sta_forward_raster",
     "sta_forward_lse",
     "sta_forward_fp8",
+    "sta_forward_fp8_lse",
     "sta_backward",
     "sta_backward_noalloc",
     "sta_window_recall",
@@ -95,6 +96,10 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.sta_forward_fp8.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                                     c_int, c_int, c_int, int3, int3, c_float, c_float, c_float,
                                     c_int, c_void_p]
+    lib.sta_forward_fp8_lse.restype = c_int
+    lib.sta_forward_fp8_lse.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int,
+                                        c_int, c_int, c_int, c_int, int3, int3, c_float, c_float,
+                                        c_float, c_int, c_void_p]
     lib.sta_backward.restype = c_int
     lib.sta_backward.argtypes = [c_void_p] * 10 + [c_int, c_int, c_int, c_int, c_int, c_int, int3,
                                                    int3, c_float, c_int, c_int, c_void_p]
@@ -419,6 +424,19 @@ def sta_forward_fp8(q8: torch.Tensor, k8: torch.Tensor, v: torch.Tensor, tile: S
     torch.float8_e4m3fn), per-tensor descales and bf16 v; returns bf16 out.
     Raster (B, heads, T, H, W, 128) tensors, or tile-major (B, heads, S, 128)
     ones with `volume`."""
+    return _forward_fp8(q8, k8, v, tile, window, q_descale, k_descale, scale, volume, out, None, False)
+
+
+def sta_forward_fp8_lse(q8: torch.Tensor, k8: torch.Tensor, v: torch.Tensor, tile: Sequence[int],
+                        window, q_descale: float, k_descale: float, scale: Optional[float] = None,
+                        volume: Optional[Sequence[int]] = None, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """sta_forward_fp8 returning (out, lse); lse is float32 of v's shape
+    without d, the row log-sum-exp of the scores on the decoded values."""
+    return _forward_fp8(q8, k8, v, tile, window, q_descale, k_descale, scale, volume, out, lse, True)
+
+
+def _forward_fp8(q8, k8, v, tile, window, q_descale, k_descale, scale, volume, out, lse, with_lse):
     lib = load_library()
     if q8.shape != k8.shape or q8.shape != v.shape:
         raise ValueError("q8, k8, v must share a shape")
@@ -433,14 +451,27 @@ def sta_forward_fp8(q8: torch.Tensor, k8: torch.Tensor, v: torch.Tensor, tile: S
         out = torch.empty_like(v)
     elif out.shape != v.shape or out.dtype != v.dtype:
         raise ValueError("out must match v")
-    dev = _require_gpu(q8, k8, v, out)
+    if not with_lse:
+        dev = _require_gpu(q8, k8, v, out)
+        with torch.cuda.device(dev):
+            rc = lib.sta_forward_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(), B,
+                                     heads, d, T, H, W, _int_array(tile),
+                                     _int_array(_windows_per_head(window, heads)), float(scale),
+                                     float(q_descale), float(k_descale), order, _stream(dev))
+        _check(rc, "sta_forward_fp8")
+        return out
+    if lse is None:
+        lse = torch.empty(v.shape[:-1], dtype=torch.float32, device=v.device)
+    elif lse.shape != v.shape[:-1] or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of v's shape without d")
+    dev = _require_gpu(q8, k8, v, out, lse)
     with torch.cuda.device(dev):
-        rc = lib.sta_forward_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(), B, heads,
-                                 d, T, H, W, _int_array(tile),
-                                 _int_array(_windows_per_head(window, heads)), float(scale),
-                                 float(q_descale), float(k_descale), order, _stream(dev))
-    _check(rc, "sta_forward_fp8")
-    return out
+        rc = lib.sta_forward_fp8_lse(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), B, heads, d, T, H, W, _int_array(tile),
+                                     _int_array(_windows_per_head(window, heads)), float(scale),
+                                     float(q_descale), float(k_descale), order, _stream(dev))
+    _check(rc, "sta_forward_fp8_lse")
+    return out, lse
 
 
 def sta_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,

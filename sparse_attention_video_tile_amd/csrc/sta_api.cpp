@@ -256,7 +256,7 @@ int forward_common(const void* q, const void* k, const void* v, void* out, float
 
 extern "C" {
 
-int sta_abi_version(void) { return 4; }
+int sta_abi_version(void) { return 5; }
 
 const char* sta_last_error(void) { return g_last_error.c_str(); }
 
@@ -339,8 +339,9 @@ int forward_common(const void* q, const void* k, const void* v, void* out, float
     const int es = elem_size(dtype);
     const int rows = raster ? p.g.S : p.g.S_pad;
     const size_t bytes = (size_t)B * heads * rows * (es ? es : 1) * head_dim;
+    const size_t qk_bytes = qk_fp8 ? (size_t)B * heads * rows * head_dim : bytes;
     const size_t lbytes = (size_t)B * heads * rows * sizeof(float);
-    if (overlaps(lse, lbytes, q, bytes) || overlaps(lse, lbytes, k, bytes) ||
+    if (overlaps(lse, lbytes, q, qk_bytes) || overlaps(lse, lbytes, k, qk_bytes) ||
         overlaps(lse, lbytes, v, bytes) || overlaps(lse, lbytes, out, bytes))
       return fail(STA_ERR_INVALID_ARG, "lse overlaps a tensor");
   }
@@ -449,9 +450,12 @@ int sta_forward_lse(const void* q, const void* k, const void* v, void* out, floa
                         dtype, stream, order == STA_RASTER);
 }
 
-int sta_forward_fp8(const void* q8, const void* k8, const void* v, void* out, int B, int heads,
-                    int head_dim, int T, int H, int W, const int* tile, const int* window,
-                    float scale, float q_descale, float k_descale, int order, void* stream) {
+namespace {
+
+int forward_fp8_common(const void* q8, const void* k8, const void* v, void* out, float* lse, int B,
+                       int heads, int head_dim, int T, int H, int W, const int* tile,
+                       const int* window, float scale, float q_descale, float k_descale, int order,
+                       void* stream) {
   if (order != STA_TILE_MAJOR && order != STA_RASTER)
     return fail(STA_ERR_INVALID_ARG, "unknown token order %d", order);
   if (!(q_descale > 0.0f) || !isfinite(q_descale) || !(k_descale > 0.0f) || !isfinite(k_descale))
@@ -463,8 +467,26 @@ int sta_forward_fp8(const void* q8, const void* k8, const void* v, void* out, in
   if (!(scale > 0.0f) || !isfinite(scale) || !(folded > 0.0f) || !isfinite(folded))
     return fail(STA_ERR_INVALID_ARG, "scale %g times the descales must be finite and positive",
                 (double)scale);
-  return forward_common(q8, k8, v, out, nullptr, B, heads, head_dim, T, H, W, tile, window, folded,
+  return forward_common(q8, k8, v, out, lse, B, heads, head_dim, T, H, W, tile, window, folded,
                         STA_BF16, stream, order == STA_RASTER, true);
+}
+
+}  // namespace
+
+int sta_forward_fp8(const void* q8, const void* k8, const void* v, void* out, int B, int heads,
+                    int head_dim, int T, int H, int W, const int* tile, const int* window,
+                    float scale, float q_descale, float k_descale, int order, void* stream) {
+  return forward_fp8_common(q8, k8, v, out, nullptr, B, heads, head_dim, T, H, W, tile, window,
+                            scale, q_descale, k_descale, order, stream);
+}
+
+int sta_forward_fp8_lse(const void* q8, const void* k8, const void* v, void* out, float* lse, int B,
+                        int heads, int head_dim, int T, int H, int W, const int* tile,
+                        const int* window, float scale, float q_descale, float k_descale,
+                        int order, void* stream) {
+  if (!lse) return fail(STA_ERR_INVALID_ARG, "lse is NULL");
+  return forward_fp8_common(q8, k8, v, out, lse, B, heads, head_dim, T, H, W, tile, window, scale,
+                            q_descale, k_descale, order, stream);
 }
 
 int sta_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,

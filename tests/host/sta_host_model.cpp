@@ -380,6 +380,8 @@ void run_valid(const Problem& pr) {
     if (pr.dtype == STA_BF16 && pr.d == 128) {
       rc = sta_forward_fp8(slot(0), slot(1), slot(2), wslot(3), pr.B, pr.heads, pr.d, pr.T, pr.H, pr.W, t, w, scale, 0.5f, 0.25f, order, nullptr);
       if (rc != STA_ERR_UNSUPPORTED || !strstr(sta_last_error(), "raster")) expect(rc, 0, "sta_forward_fp8");
+      rc = sta_forward_fp8_lse(slot(0), slot(1), slot(2), wslot(3), reinterpret_cast<float*>(wslot(4)), pr.B, pr.heads, pr.d, pr.T, pr.H, pr.W, t, w, scale, 0.5f, 0.25f, order, nullptr);
+      if (rc != STA_ERR_UNSUPPORTED || !strstr(sta_last_error(), "raster")) expect(rc, 0, "sta_forward_fp8_lse");
     }
     const int cands[6] = {w[0], w[1], w[2], t[0], t[1], t[2]};
     const bool padded = pr.T % t[0] || pr.H % t[1] || pr.W % t[2];

@@ -153,6 +153,28 @@ def test_forward_lse_rejects_bad_arguments(lib):
     assert "overlap" in binding.last_error()
 
 
+def test_forward_fp8_lse_rejects_bad_arguments(lib):
+    """lse NULL, bad descales and head_dim are refused; lse is checked for
+    overlap against q8 and k8 at one byte an element (an lse right after q8
+    is accepted, and the call then fails on the overlapping output instead)."""
+    t, w = i3(6, 8, 8), i3(18, 24, 24)
+    f = lib.sta_forward_fp8_lse
+    n = 30 * 48 * 80 * 128               # elements of one (b, h) tensor
+    q8, k8, v = FAKE, FAKE + 4 * n, FAKE + 8 * n
+
+    def call(lse, out=FAKE + 12 * n, d=128, qd=1.0, kd=1.0):
+        return f(q8, k8, v, out, lse, 1, 1, d, 30, 48, 80, t, w, 0.1, qd, kd, 1, None)
+
+    assert call(None) == -1
+    assert call(FAKE + 16 * n, qd=0.0) == -1
+    assert call(FAKE + 16 * n, kd=float("inf")) == -1
+    assert call(FAKE + 16 * n, d=64) == binding.STA_ERR_UNSUPPORTED
+    assert call(q8 + n - 64) == -1
+    assert "lse overlaps" in binding.last_error()
+    assert call(q8 + n, out=v + 64) == -1
+    assert "output overlaps" in binding.last_error()
+
+
 def backward_args(**kw):
     a = dict(q=FAKE, k=FAKE * 2000, v=FAKE * 4000, o=FAKE * 6000, do=FAKE * 8000, lse=FAKE * 10000,
              dq=FAKE * 12000, dk=FAKE * 14000, dv=FAKE * 16000, delta=FAKE * 18000, B=1, heads=1,

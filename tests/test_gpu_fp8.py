@@ -3,7 +3,9 @@ oracle on the same codes, in both token orders, on small seeded workloads
 (several tiles, ragged runs, a padded tile grid, per-head windows) and on
 sampled rows of the 30x48x80 workload in the launch configuration of the
 raster-order kernel; plus agreement with the bf16 kernel on the decoded values
-(every E4M3 value times a power-of-two descale is a bf16 value)."""
+(every E4M3 value times a power-of-two descale is a bf16 value). The row
+log-sum-exp of the fp8 scores, and the training path it enables (the bf16
+backward on the decoded q and k with that log-sum-exp), against the oracle."""
 
 import math
 
@@ -13,8 +15,8 @@ import torch
 
 import oracle
 from sparse_attention_video_tile_amd import binding, workloads
-from tests.parity_util import (assert_close, default_scale, e4m3_codes, e4m3_descale, errors,
-                               to_gpu)
+from tests.parity_util import (LSE_BF16_MAX_ABS, assert_close, assert_grad_close, default_scale,
+                               e4m3_codes, e4m3_descale, errors, to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,6 +54,32 @@ def run_fp8(w, inp, q8, k8, qd, kd, order):
     if order == "tile_major":
         got = oracle.from_tile_major(got, w.volume, w.tile)
     return got
+
+
+def run_fp8_lse(w, windows, v, q8, k8, qd, kd, order, scale):
+    """fp8 forward with log-sum-exp through the C ABI -> (out, lse) as raster
+    torch tensors (out bf16, lse float32); also checks that the output equals
+    the forward without lse bit for bit (on the token rows: the padding rows
+    of a tile-major output are left unwritten)."""
+    if order == "tile_major":
+        q8, k8 = (oracle.to_tile_major(x, w.tile) for x in (q8, k8))
+        v = oracle.to_tile_major(v, w.tile)
+    q8g, k8g = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (q8, k8))
+    vg = to_gpu(v, "bf16")
+    vol = w.volume if order == "tile_major" else None
+    out, lse = binding.sta_forward_fp8_lse(q8g, k8g, vg, w.tile, windows, qd, kd, scale=scale,
+                                           volume=vol)
+    plain = binding.sta_forward_fp8(q8g, k8g, vg, w.tile, windows, qd, kd, scale=scale,
+                                    volume=vol)
+    torch.cuda.synchronize()
+    if order == "tile_major":
+        raster = lambda x: torch.from_numpy(oracle.from_tile_major(x.float().cpu().numpy(), w.volume,
+                                                                   w.tile)).to(torch.bfloat16).cuda()
+        out, plain = raster(out), raster(plain)
+        lse = torch.from_numpy(oracle.from_tile_major(lse.cpu().numpy()[..., None], w.volume,
+                                                      w.tile)[..., 0]).cuda()
+    assert torch.equal(out, plain), "output differs from the fp8 forward without lse"
+    return out, lse
 
 
 @pytest.mark.parametrize("order", ["raster", "tile_major"])
@@ -200,4 +228,76 @@ def test_fp8_invalid_inputs_raise():
                                 to_gpu(i64.v, "bf16"), w64.tile, i64.windows, 1.0, 1.0)
     with pytest.raises(TypeError):
         binding.sta_forward_fp8(q8g.float(), k8g, v, w.tile, inp.windows, qd, kd)
+    torch.cuda.synchronize()
+
+
+LSE_CASES = [CASES[0], CASES[2], CASES[6], CASES[7]]
+
+
+@pytest.mark.parametrize("order", ["raster", "tile_major"])
+@pytest.mark.parametrize("case", LSE_CASES, ids=lambda c: c[0])
+def test_fp8_lse_matches_oracle(case, order):
+    name, volume, tile, windows = case
+    w = workloads.small_case(volume, tile, windows, head_dim=128, dtype="bf16", B=2, seed=31,
+                             name=name)
+    print(f"[case] fp8 forward with lse {order} {w}", flush=True)
+    inp = workloads.make_inputs(w)
+    q8, k8, qd, kd = fp8_inputs(inp)
+    scale = default_scale(128)
+    out, lse = run_fp8_lse(w, inp.windows, inp.v, q8, k8, qd, kd, order, scale)
+    ref = oracle.sta_lse_fp8(q8, k8, tile, inp.windows, scale, qd, kd)
+    err = np.abs(lse.cpu().numpy().astype(np.float64) - ref).max()
+    print(f"[parity] fp8 {name} {order} lse max_abs {err:.3e}", flush=True)
+    assert err <= LSE_BF16_MAX_ABS
+    assert_close(out.float().cpu().numpy(),
+                 oracle.sta_attention_fp8(q8, k8, inp.v, tile, inp.windows, scale, qd, kd), "bf16",
+                 f"fp8 lse forward {name} {order}")
+
+
+@pytest.mark.parametrize("order", ["raster", "tile_major"])
+@pytest.mark.parametrize("case", LSE_CASES[:2] + LSE_CASES[3:], ids=lambda c: c[0])
+def test_fp8_training_path_gradients(case, order):
+    """fp8 scores in the forward, gradients from the bf16 backward on the
+    decoded q and k (exact bf16 values) with the fp8 forward's out and lse:
+    equal to the oracle's gradients of the attention on the decoded values
+    (the fp8 rounding of q and k is taken as given, not differentiated)."""
+    name, volume, tile, windows = case
+    w = workloads.small_case(volume, tile, windows, head_dim=128, dtype="bf16", B=2, seed=37,
+                             name=name)
+    print(f"[case] fp8 training path {order} {w}", flush=True)
+    inp = workloads.make_inputs(w)
+    dout = workloads.make_grad_output(w)
+    q8, k8, qd, kd = fp8_inputs(inp)
+    scale = default_scale(128)
+    out, lse = run_fp8_lse(w, inp.windows, inp.v, q8, k8, qd, kd, order, scale)
+    qdec, kdec = oracle.e4m3_decode(q8) * qd, oracle.e4m3_decode(k8) * kd
+    q, k, v, do = (to_gpu(x, "bf16") for x in (qdec, kdec, inp.v, dout))
+    assert torch.equal(q.double().cpu(), torch.from_numpy(qdec)), "decoded q is not a bf16 value"
+    if order == "raster":
+        grads = binding.sta_backward(q, k, v, out, do, lse, tile, inp.windows, scale)
+    else:
+        tmj = lambda x: binding.sta_reorder_tiles(x.contiguous(), tile)
+        lse_t = binding.sta_reorder_tiles(lse.unsqueeze(-1).expand(*lse.shape, 4).contiguous(),
+                                          tile)[..., 0].contiguous()
+        g = binding.sta_backward(tmj(q), tmj(k), tmj(v), tmj(out), tmj(do), lse_t, tile,
+                                 inp.windows, scale, volume=volume)
+        grads = tuple(binding.sta_restore_order(x, volume, tile) for x in g)
+    torch.cuda.synchronize()
+    ref = oracle.sta_backward(qdec, kdec, inp.v, dout, tile, inp.windows, scale)
+    for nm, g, r in zip(("dq", "dk", "dv"), grads, ref):
+        assert_grad_close(g.float().cpu().numpy(), r, "bf16", f"fp8 path {name} {order} {nm}")
+
+
+def test_fp8_lse_argument_errors():
+    w = workloads.small_case((4, 8, 8), (2, 4, 4), [(4, 8, 8)], head_dim=128, dtype="bf16", seed=1,
+                             name="fp8_lse_args")
+    inp = workloads.make_inputs(w)
+    q8, k8, qd, kd = fp8_inputs(inp)
+    q8g, k8g = (torch.from_numpy(x).cuda() for x in (q8, k8))
+    v = to_gpu(inp.v, "bf16")
+    with pytest.raises(ValueError):   # lse of the wrong shape
+        binding.sta_forward_fp8_lse(q8g, k8g, v, w.tile, inp.windows, qd, kd,
+                                    lse=torch.empty(3, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):   # descale not positive
+        binding.sta_forward_fp8_lse(q8g, k8g, v, w.tile, inp.windows, 0.0, kd)
     torch.cuda.synchronize()

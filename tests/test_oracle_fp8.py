@@ -1,10 +1,12 @@
 """Pins for the fp8 oracle (CPU): the E4M3 decoder against the format's fixed
-values and torch's own float8_e4m3fn type, and the fp8 attention against
-closed forms, invariants of the descales and a library attention."""
+values and torch's own float8_e4m3fn type, and the fp8 attention and its row
+log-sum-exp against closed forms, invariants of the descales and library
+routines."""
 
 import math
 
 import numpy as np
+import scipy.special
 import torch
 
 import oracle
@@ -121,3 +123,48 @@ def test_row_subsets_match_whole_fp8_output():
                                                  qd, kd, b, h, rows)
             np.testing.assert_allclose(part, full[b, h].reshape(-1, 128)[rows], rtol=1e-12,
                                        atol=1e-14)
+
+
+def test_lse_fp8_zero_queries_give_log_of_window_size():
+    """All scores zero: every row's log-sum-exp is the log of its window's key
+    count (a closed form independent of the keys and the descales)."""
+    w, inp = _case()
+    q8 = np.zeros(inp.q.shape, dtype=np.uint8)
+    kd = e4m3_descale(inp.k)
+    k8 = e4m3_codes(inp.k, kd)
+    lse = oracle.sta_lse_fp8(q8, k8, w.tile, inp.windows, 0.3, 2.0, kd)
+    toks = np.arange(int(np.prod(w.volume)))
+    for h in range(w.heads):
+        counts = oracle.token_mask_rows(w.volume, w.tile, tuple(inp.windows[h]), toks).sum(axis=1)
+        assert np.allclose(lse[0, h].reshape(-1), np.log(counts), rtol=0, atol=1e-12)
+
+
+def test_lse_fp8_whole_volume_equals_scipy_logsumexp():
+    """Whole-volume window: the row log-sum-exp over every key, computed with
+    scipy on values decoded by torch's float8_e4m3fn type."""
+    volume, tile = (2, 4, 4), (1, 2, 2)
+    w = workloads.small_case(volume, tile, [volume, volume], head_dim=128, dtype="bf16", seed=5,
+                             name="fp8_lse_dense_pin")
+    inp = workloads.make_inputs(w)
+    qd, kd = e4m3_descale(inp.q), e4m3_descale(inp.k)
+    q8, k8 = e4m3_codes(inp.q, qd), e4m3_codes(inp.k, kd)
+    s = 0.125
+    lse = oracle.sta_lse_fp8(q8, k8, tile, inp.windows, s, qd, kd)
+    qt = torch.from_numpy(q8).view(torch.float8_e4m3fn).to(torch.float64).numpy() * qd
+    kt = torch.from_numpy(k8).view(torch.float8_e4m3fn).to(torch.float64).numpy() * kd
+    for h in range(w.heads):
+        qf, kf = qt[0, h].reshape(-1, 128), kt[0, h].reshape(-1, 128)
+        want = scipy.special.logsumexp(s * qf @ kf.T, axis=1)
+        assert np.allclose(lse[0, h].reshape(-1), want, rtol=0, atol=1e-12)
+
+
+def test_lse_fp8_descales_fold_into_the_scale_and_commute():
+    w, inp = _case(seed=11)
+    qd, kd = e4m3_descale(inp.q), e4m3_descale(inp.k)
+    q8, k8 = e4m3_codes(inp.q, qd), e4m3_codes(inp.k, kd)
+    s = 1.0 / math.sqrt(128)
+    a = oracle.sta_lse_fp8(q8, k8, w.tile, inp.windows, s, qd, kd)
+    b = oracle.sta_lse_fp8(q8, k8, w.tile, inp.windows, s * qd * kd, 1.0, 1.0)
+    c = oracle.sta_lse_fp8(q8, k8, w.tile, inp.windows, s, kd, qd)
+    assert np.allclose(a, b, rtol=0, atol=1e-12)
+    assert np.allclose(a, c, rtol=0, atol=1e-12)
