@@ -449,6 +449,9 @@ def main(argv=None):
             "frac": attn_tflops / peak,
             "traffic": recorded_traffic(w.name, args.path) if w.dtype == "bf16" else None,
             "launch_ms": attn_ms,
+            "launch_note": "one step's attention launches, HIP events around them: whole-tile work "
+                           "items, then (when they leave the last round mostly idle) that round "
+                           "as 64-row items in a second launch",
         },
         "cpu_baseline": cpu,
         "dense": dense,

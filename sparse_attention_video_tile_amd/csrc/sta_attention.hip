@@ -22,6 +22,8 @@
 // FMA arithmetic; it serves float32 problems.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "sta_attn_common.h"
 
 namespace sta {
@@ -796,12 +798,11 @@ bool chunks_full(const AttnProblem& pr, int bn) {
   return true;
 }
 
+// One launch of the bf16 kernels with work items of C::kRows rows, planned
+// in `p`, on `grid` workgroups.
 template <int D, int WAVES, int RB, int BN, bool QK8>
-int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
+int launch_bf16_planned(const AttnProblem& pr, const AttnParams& p, unsigned grid, hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
-  AttnParams p;
-  fill_params(pr, C::kRows, &p);
-  const unsigned grid = (unsigned)p.per_xcd * kXcds;
   // plane chunks address K/V by arithmetic and need no offset table
   const bool full = chunks_full(pr, BN);
   const unsigned table = (full && BN == 64 && p.plane_cpt > 0) ? 0 : raster_table_bytes(pr);
@@ -838,6 +839,32 @@ int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
   return (int)hipGetLastError();
 }
 
+template <int D, int WAVES, int RB, int BN, bool QK8>
+int launch_bf16(const AttnProblem& pr, hipStream_t stream) {
+  AttnParams p;
+  fill_params(pr, Bf16Cfg<D, WAVES, RB, BN>::kRows, &p);
+  return launch_bf16_planned<D, WAVES, RB, BN, QK8>(pr, p, (unsigned)p.per_xcd * kXcds, stream);
+}
+
+// Compute units per XCD of the current device (0 if unknown), cached.
+int cu_per_xcd() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  static std::atomic<int> cache[64];
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    v = cus >= kXcds ? cus / kXcds : -1;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v > 0 ? v : 0;
+}
+
+#ifndef STA_CFG_TAIL_SPLIT
+#define STA_CFG_TAIL_SPLIT 1
+#endif
+
 template <int D>
 int launch_f32(const AttnProblem& pr, hipStream_t stream) {
   AttnParams p;
@@ -855,7 +882,20 @@ template <int D, bool QK8 = false>
 int dispatch_bf16(const AttnProblem& pr, hipStream_t stream) {
   const int rows = fwd_bf16_rows(pr.dense ? pr.g.S : pr.g.tau);
   static_assert(Bf16Cfg<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN>::kRows == kFwdBigRows, "shape");
-  if (rows == kFwdBigRows) return launch_bf16<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN, QK8>(pr, stream);
+  if (rows == kFwdBigRows) {
+    // The last, partly filled round of whole-tile items runs as 64-row items
+    // in a second launch when that spreads it over the XCD (plan_tail_split).
+    AttnParams p, tp;
+    fill_params(pr, kFwdBigRows, &p);
+    int main_per_xcd = p.per_xcd;
+    const bool tail = STA_CFG_TAIL_SPLIT &&
+                      plan_tail_split(pr, p, kFwdBigRows, kFwdTailRows, cu_per_xcd(), &tp, &main_per_xcd);
+    const int rc = launch_bf16_planned<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN, QK8>(
+        pr, p, (unsigned)main_per_xcd * kXcds, stream);
+    if (rc || !tail) return rc;
+    static_assert(Bf16Cfg<D, 4, 1, 64>::kRows == kFwdTailRows, "tail shape");
+    return launch_bf16_planned<D, 4, 1, 64, QK8>(pr, tp, (unsigned)tp.per_xcd * kXcds, stream);
+  }
   if (rows == 64) return launch_bf16<D, 4, 1, 64, QK8>(pr, stream);
   return launch_bf16<D, 4, 2, 64, QK8>(pr, stream);
 }

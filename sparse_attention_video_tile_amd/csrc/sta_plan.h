@@ -34,6 +34,11 @@ struct AttnParams {
   int n_tasks;      // work items
   int per_xcd;      // workgroups each XCD runs (the grid is kXcds * per_xcd)
   int group;        // logical tasks an XCD takes in a row before the next XCD's turn
+  // Tail launch (0 otherwise): each workgroup runs one of tail_split row
+  // blocks of a work item of an XCD's last round, which starts at round
+  // tail_r0 of the XCD (see plan_tail_split).
+  int tail_split;
+  int tail_r0;
   int row_blocks;   // work items per query unit
   int n_units;      // query units per (batch, head): tiles, or 1 if dense
   int unit_rows;    // rows per query unit: tau, or S if dense
@@ -72,6 +77,7 @@ inline void set_plane_chunks(AttnParams* p) {
 
 inline void plan_tasks(AttnParams* p, long long tasks, int heads, bool dense) {
   p->n_tasks = (int)tasks;
+  p->tail_split = p->tail_r0 = 0;
   int cost[STA_MAX_HEADS];
   bool equal = true;
   for (int h = 0; h < heads; ++h) {
@@ -380,6 +386,8 @@ inline void fill_bwd_params(const BwdProblem& pr, int rows_per_item, AttnParams*
 #define STA_CFG_BN 64
 #endif
 constexpr int kFwdBigRows = STA_CFG_WAVES * 16 * STA_CFG_RB;
+// Rows of the items a split last round runs as (4 waves of 16 rows).
+constexpr int kFwdTailRows = 64;
 // bf16 forward: the big shape when a unit is whole blocks of it, else 4 waves
 // of 16 rows (units of at most 64 rows) or of 32 rows.
 inline int fwd_bf16_rows(int unit_rows) {
@@ -399,7 +407,41 @@ inline int bwd_query_rows(int tau) { return tau >= 128 ? 128 : 64; }
 // run on the same XCD and share its L2.
 STA_HD int task_of_block(const AttnParams& p, int bid) {
   const int x = bid % kXcds, r = bid / kXcds;
+  if (p.tail_split) {
+    // Tail launch: row block r % tail_split of the work item the XCD's round
+    // tail_r0 + r / tail_split would have run, on the same XCD.
+    const int mr = p.tail_r0 + r / p.tail_split;
+    const int item = (mr / p.group) * (kXcds * p.group) + x * p.group + mr % p.group;
+    return item * p.tail_split + r % p.tail_split;
+  }
   return (r / p.group) * (kXcds * p.group) + x * p.group + r % p.group;
+}
+
+// Host side: the last round of work items. Under an equal-cost plan each XCD
+// runs `group` items on cu_per_xcd CUs, one workgroup per CU; when group is
+// not a multiple of cu_per_xcd the last round leaves most of the XCD idle for
+// a whole item. If its items, cut into split = main_rows / tail_rows row
+// blocks, fit two to a CU, the main launch stops before that round and `t`
+// describes a second launch of tail_rows-row items that runs them side by
+// side. Row block b of item i is item i * split + b of the tail launch (the
+// same rows as under a plain tail_rows-row plan). Returns whether to split;
+// *main_per_xcd is the main launch's workgroups per XCD either way.
+inline bool plan_tail_split(const AttnProblem& pr, const AttnParams& m, int main_rows, int tail_rows,
+                            int cu_per_xcd, AttnParams* t, int* main_per_xcd) {
+  *main_per_xcd = m.per_xcd;
+  if (cu_per_xcd <= 0 || m.group != m.per_xcd || m.group < cu_per_xcd) return false;
+  if (tail_rows <= 0 || main_rows % tail_rows || m.unit_rows % main_rows) return false;
+  const int rem = m.group % cu_per_xcd;
+  const int split = main_rows / tail_rows;
+  if (rem == 0 || (long long)rem * split > 2LL * cu_per_xcd) return false;
+  fill_params(pr, tail_rows, t);
+  if ((long long)t->n_tasks != (long long)m.n_tasks * split) return false;
+  t->group = m.group;
+  t->per_xcd = rem * split;
+  t->tail_split = split;
+  t->tail_r0 = m.group - rem;
+  *main_per_xcd = m.group - rem;
+  return true;
 }
 
 }  // namespace

@@ -98,6 +98,7 @@ def role(name: str) -> str:
         lse_only = len(a) > 6 and a[6] == "true"
         pad = len(a) > 7 and a[7] == "true"
         qk8 = len(a) > 10 and a[10] == "true"
+        small = a[1] == "4" and a[2] == "1"   # 4 waves of 16 rows: 64-row items
         what = "dense comparator" if dense else (
             "STA forward, raster order (fused path)" if raster else "STA forward, tile-major (three-call path)")
         if lse_only:
@@ -106,6 +107,8 @@ def role(name: str) -> str:
             what += ", padded grid"
         if qk8:
             what += ", fp8 q and k"
+        if small:
+            what += ", 64-row items"
         return what
     if "attn_f32_kernel" in name:
         return "STA forward, float32"
@@ -121,9 +124,28 @@ def _targs(name: str):
 
 
 def is_headline(name: str) -> bool:
-    """The fused (raster-order) forward kernel that bench.py times: not the
-    log-sum-exp-only or padded variants."""
+    """The fused (raster-order) forward kernel that bench.py times, whole-tile
+    items: not the log-sum-exp-only, padded or 64-row variants."""
     return role(name) == "STA forward, raster order (fused path)"
+
+
+def is_headline_tail(name: str) -> bool:
+    """The second launch of a headline step: the last round's items as 64-row
+    items (absent when the work items fill every round)."""
+    return role(name) == "STA forward, raster order (fused path), 64-row items"
+
+
+def step_dispatches(ids_names):
+    """[(main dispatch id, tail dispatch id or None)] of the headline steps,
+    in order, from (dispatch id, kernel name) pairs: a tail launch belongs to
+    the main launch it directly follows."""
+    steps = []
+    for d, n in sorted(ids_names):
+        if is_headline(n):
+            steps.append([d, None])
+        elif is_headline_tail(n) and steps and steps[-1][1] is None and d == steps[-1][0] + 1:
+            steps[-1][1] = d
+    return [tuple(x) for x in steps]
 
 
 N_XCD = 8   # rocprofv3 reports GRBM_GUI_ACTIVE summed over the XCDs
@@ -245,18 +267,29 @@ def main(argv=None) -> int:
     tpath = os.path.join(run, "trace", "bench_kernel_trace.csv")
     if os.path.exists(tpath):
         fused = cfg.get("path", "fused") == "fused"
-        disp = sorted((int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-                      for r in csv.DictReader(open(tpath))
-                      if "attn_bf16_kernel" in r["Kernel_Name"] and (
-                          is_headline(r["Kernel_Name"]) if fused else
-                          role(r["Kernel_Name"]) == "STA forward, tile-major (three-call path)"))
+        rows_t = list(csv.DictReader(open(tpath)))
+        dur = {int(r["Dispatch_Id"]): int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows_t}
+        if fused:
+            steps = step_dispatches((int(r["Dispatch_Id"]), r["Kernel_Name"]) for r in rows_t)
+        else:
+            steps = sorted((int(r["Dispatch_Id"]), None) for r in rows_t
+                           if role(r["Kernel_Name"]) == "STA forward, tile-major (three-call path)")
         w0, ns = bench["warmup"], bench["steps"]
-        if len(disp) >= w0 + ns:
-            sel = [d for _, d in disp[w0:w0 + ns]]
-            timed = sum(sel) / len(sel) / 1e6
-    L += ["", f"Timed launches: dispatches {bench['warmup'] + 1}..{bench['warmup'] + bench['steps']} of "
-          f"the {rf['kernel']} (the first warm-up + timed launches of that kernel in the run) average "
-          + (f"{timed:.3f} ms in the trace." if timed is not None else "n/a (no kernel trace)."),
+        if len(steps) >= w0 + ns:
+            sel = steps[w0:w0 + ns]
+            main_ms = sum(dur[m] for m, _ in sel) / len(sel) / 1e6
+            tail_ms = sum(dur[t] for _, t in sel if t is not None) / len(sel) / 1e6
+            timed = (main_ms, tail_ms, sum(1 for _, t in sel if t is not None))
+    if timed is None:
+        tline = "n/a (no kernel trace)."
+    elif timed[2]:
+        tline = (f"{timed[0]:.3f} ms (whole-tile items) + {timed[1]:.3f} ms (the last round as 64-row "
+                 f"items, a second launch) = {timed[0] + timed[1]:.3f} ms a step in the trace.")
+    else:
+        tline = f"{timed[0]:.3f} ms in the trace."
+    L += ["", f"Timed steps: steps {bench['warmup'] + 1}..{bench['warmup'] + bench['steps']} of "
+          f"the {rf['kernel']} (the first warm-up + timed steps of that path in the run) average "
+          + tline,
           f"bench.py's HIP-event average for the same launches in the same command without the "
           f"profiler: {rf['launch_ms']:.3f} ms, {rf['achieved']:.1f} TFLOP/s of algorithmic work "
           f"({cfg['algorithmic_tflop_per_step']:.4f} TFLOP per launch), {100 * rf['frac']:.1f}% of "
@@ -293,10 +326,15 @@ def main(argv=None) -> int:
     # headline: the fused kernel's first 1 + 2 dispatches (warm-up + timed
     # steps of the counter runs); later dispatches of the same kernel belong
     # to other workloads
-    head = [k for k in fetch if is_headline(k[1])][:3]
+    # a step's traffic: its whole-tile launch plus its tail launch, if any
+    names = {d: n for (d, n) in fetch}
+    hsteps = step_dispatches(names.items())[:3]
+    head = [(m, names[m]) for m, _ in hsteps]
     if head:
-        hf = sum(fetch[k] for k in head) / len(head)
-        hw = sum(write[k] for k in head if k in write) / len(head)
+        def per_step(c):
+            return sum(c.get((m, names[m]), 0.0) + (c.get((t, names[t]), 0.0) if t is not None else 0.0)
+                       for m, t in hsteps) / len(hsteps)
+        hf, hw = per_step(fetch), per_step(write)
         records["fused"] = {
             "kernel": short_name(head[0][1]), "workload": wl, "path": "fused",
             "dispatches": len(head),
@@ -308,7 +346,8 @@ def main(argv=None) -> int:
             "fetch_kib_to_bytes": fscale * 1024, "write_kib_to_bytes": wscale * 1024,
             "commands": [pmc_cmd("FETCH_SIZE"), pmc_cmd("WRITE_SIZE")],
         }
-        L.append(f"| `{short_name(head[0][1])}` | the timed launches of the fused path only | {len(head)} | "
+        L.append(f"| `{short_name(head[0][1])}` | the timed steps of the fused path only (with their "
+                 f"64-row tail launches) | {len(head)} | "
                  f"{hf:.0f} | {hw:.0f} | {hf * fscale * 1024 / 1e9:.3f} | {hw * wscale * 1024 / 1e9:.3f} | "
                  f"{3 * tensor / 1e9:.3f} + {tensor / 1e9:.3f} |")
     for n in kernels:
@@ -339,10 +378,24 @@ def main(argv=None) -> int:
                 "write_kib_to_bytes": wscale * 1024,
                 "commands": [pmc_cmd("FETCH_SIZE"), pmc_cmd("WRITE_SIZE")],
             }
+    # the tile-major path's step: add its 64-row tail launch, if it has one
+    tails = [n for n in kernels if role(n) == "STA forward, tile-major (three-call path), 64-row items"]
+    if "three_call" in records and tails:
+        f, w, _ = summarize(lambda x: x == tails[0])
+        rec = records["three_call"]
+        rec["read_bytes_per_launch"] += f * fscale * 1024
+        rec["write_bytes_per_launch"] += w * wscale * 1024
+        rec["bytes_per_launch"] = rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"]
+        rec["tail_kernel"] = short_name(tails[0])
+    if "fused" in records and any(t is not None for _, t in hsteps):
+        rec = records["fused"]
+        rec["tail_kernel"] = short_name(names[next(t for _, t in hsteps if t is not None)])
     L += ["", "\"Algorithmic\" counts every input element once and every output element once "
           "(q, k, v read; o written). The attention kernels re-read K and V for every query tile "
           "whose window holds them; what the counters show is the traffic below L2 (HBM and the "
-          "memory-side cache)."]
+          "memory-side cache). A step of either path is one launch of whole-tile items and, when "
+          "the items do not fill the last round, a second launch of that round as 64-row items; "
+          "the JSON records count both."]
     open(os.path.join(out, f"attn_{bench['dtype']}_{wl}_traffic.md"), "w").write("\n".join(L) + "\n")
     for path, rec in records.items():
         fn = os.path.join(out, f"attn_{bench['dtype']}_{path}_{wl}_traffic.json")

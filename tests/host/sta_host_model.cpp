@@ -38,6 +38,7 @@ struct Ctx {
   std::string what;     // the problem under test
   long long checks = 0;
   long long launches = 0;
+  long long tail_launches = 0;   // forward launches whose last round ran as 64-row items
 } g_ctx;
 
 #define CHECK_ROW(row_, rows_, msg_)                                                         \
@@ -133,12 +134,11 @@ void check_head(const AttnParams& p, const Task& t, int D, long long total_rows)
   CHECK_ROW(t.head_base / D + p.S - 1, total_rows, "head end");
 }
 
-// The bf16 forward (attn_bf16_kernel) and its dense form, every workgroup of
-// the grid of one launch.
+// The bf16 forward (attn_bf16_kernel) and its dense form: every workgroup of
+// the grid of one launch planned in p; each task it runs is marked in seen.
 template <int ROWS>
-void model_bf16_forward(const sta::AttnProblem& pr) {
-  AttnParams p;
-  sta::fill_params(pr, ROWS, &p);
+void model_bf16_launch(const sta::AttnProblem& pr, const AttnParams& p, long long grid,
+                       std::vector<char>& seen) {
   const int D = pr.head_dim;
   const long long total_rows = (long long)pr.B * pr.heads * p.S;
   const bool full = [&] {
@@ -154,9 +154,7 @@ void model_bf16_forward(const sta::AttnProblem& pr) {
     table_len = pr.omega[h][2] * pr.g.tau > table_len ? pr.omega[h][2] * pr.g.tau : table_len;
   CHECK(!pr.raster || pr.dense || plane || table_len <= sta::kMaxRasterRun, "raster table fits LDS");
   const int k_row_bytes = pr.qk_fp8 ? D : 2 * D;
-  const long long grid = (long long)p.per_xcd * sta::kXcds;
-  CHECK(p.n_tasks <= grid, "grid covers every task");
-  std::vector<char> seen(p.n_tasks, 0);
+  CHECK(grid <= (1LL << 31) - 1, "grid fits the launch");
   for (long long bid = 0; bid < grid; ++bid) {
     const int task = sta::task_of_block(p, (int)bid);
     if (task >= p.n_tasks) continue;
@@ -169,8 +167,38 @@ void model_bf16_forward(const sta::AttnProblem& pr) {
     for (int it = 0; it < w.n_chunks; ++it)
       model_chunk(p, w, it, pr.raster && !pr.dense, plane, p.pad, p.S, k_row_bytes, table_len, "key");
   }
-  for (int i = 0; i < p.n_tasks; ++i) CHECK(seen[i], "every task has a workgroup");
   ++g_ctx.launches;
+}
+
+// Compute units per XCD the model plans for (MI355X: 256 over 8 XCDs).
+constexpr int kModelCuPerXcd = 32;
+
+// The bf16 forward as the launcher issues it: the main launch, and for whole-
+// tile items a second launch of the last round cut into 64-row items when
+// plan_tail_split asks for it. Every row block must run exactly once.
+template <int ROWS>
+void model_bf16_forward(const sta::AttnProblem& pr) {
+  AttnParams p, tp;
+  sta::fill_params(pr, ROWS, &p);
+  int main_per_xcd = p.per_xcd;
+  const bool tail = ROWS == sta::kFwdBigRows &&
+                    sta::plan_tail_split(pr, p, ROWS, sta::kFwdTailRows, kModelCuPerXcd, &tp, &main_per_xcd);
+  std::vector<char> seen(p.n_tasks, 0);
+  model_bf16_launch<ROWS>(pr, p, (long long)main_per_xcd * sta::kXcds, seen);
+  if (!tail) {
+    CHECK(p.n_tasks <= (long long)p.per_xcd * sta::kXcds, "grid covers every task");
+    for (int i = 0; i < p.n_tasks; ++i) CHECK(seen[i], "every task has a workgroup");
+    return;
+  }
+  ++g_ctx.tail_launches;
+  std::vector<char> tseen(tp.n_tasks, 0);
+  model_bf16_launch<sta::kFwdTailRows>(pr, tp, (long long)tp.per_xcd * sta::kXcds, tseen);
+  for (int i = 0; i < p.n_tasks; ++i) {
+    int parts = 0;
+    for (int b = 0; b < tp.tail_split; ++b) parts += tseen[(size_t)i * tp.tail_split + b];
+    CHECK(seen[i] ? parts == 0 : parts == tp.tail_split,
+          "each item once: whole in the main launch or all its row blocks in the tail launch");
+  }
 }
 
 // The float32 forward (attn_f32_kernel): one thread per query row, 32-key
@@ -491,6 +519,7 @@ int main() {
              raster ? "raster" : "tile-major", outside, p.S, worst, pr.g.S_pad);
     }
   }
-  printf("host model: %lld launches modelled, %lld checks, all in bounds\n", g_ctx.launches, g_ctx.checks);
+  printf("host model: %lld launches modelled (%lld forwards with a split last round), %lld checks, all in bounds\n",
+         g_ctx.launches, g_ctx.tail_launches, g_ctx.checks);
   return 0;
 }
