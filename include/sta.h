@@ -336,6 +336,27 @@ int sta_window_recall(const void* q, const void* k, float* recall, float* worksp
                       void* stream);
 
 /*
+ * sta_window_recall on fp8 queries and keys: the recall of each candidate
+ * window for the scores of sta_forward_fp8,
+ *     scale * (q_descale Q8_i) . (k_descale K8_j),
+ * so that windows are ranked on the same scores the fp8 forward computes
+ * (recall and the per-head window choice: podcast transcript, the answers on
+ * attention recall and on choosing the window per head; FP8 inside the sparse
+ * attention kernel: dianyo ICML2025 blog, Sparse VideoGen, "Observation &
+ * Proposed Method"). Both log-sum-exp passes sum the probabilities in
+ * float32 without rounding them.
+ *   q8, k8: device uint8 [B][heads][S][128], E4M3 codes as in
+ *           sta_forward_fp8, token order `order`, read.
+ *   q_descale, k_descale: finite, > 0.
+ * head_dim must be 128 (else STA_ERR_UNSUPPORTED). Other arguments, buffers,
+ * rules and errors as sta_window_recall.
+ */
+int sta_window_recall_fp8(const void* q8, const void* k8, float* recall, float* workspace, int B,
+                          int heads, int head_dim, int T, int H, int W, const int* tile,
+                          const int* candidates, int n_candidates, float scale, float q_descale,
+                          float k_descale, int order, void* stream);
+
+/*
  * Full softmax attention over all S keys (the computation STA replaces, used
  * as the speed-up denominator: atlas.scime.ai summary, "Key results").
  *   q, k, v, out: device [B][heads][S][head_dim], any common token order.

@@ -12,4 +12,4 @@ from .sta_backward_oracle import (  # noqa: F401
     sta_lse,
     window_recall,
 )
-from .sta_fp8_oracle import e4m3_decode, sta_attention_fp8, sta_attention_fp8_rows, sta_lse_fp8  # noqa: F401
+from .sta_fp8_oracle import e4m3_decode, sta_attention_fp8, sta_attention_fp8_rows, sta_lse_fp8, window_recall_fp8  # noqa: F401

@@ -22,7 +22,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .sta_backward_oracle import sta_lse
+from .sta_backward_oracle import sta_lse, window_recall
 from .sta_oracle import sta_attention, sta_attention_rows
 
 
@@ -71,3 +71,14 @@ def sta_lse_fp8(q8, k8, tile, windows, scale, q_descale, k_descale) -> np.ndarra
     if not (np.all(np.isfinite(q)) and np.all(np.isfinite(k))):
         raise ValueError("NaN code in q8 or k8")
     return sta_lse(q, k, tile, windows, scale)
+
+
+def window_recall_fp8(q8, k8, tile, candidates, scale, q_descale, k_descale) -> np.ndarray:
+    """Attention recall (float64, (B, heads, n_candidates)) of each candidate
+    window for the scores on the decoded fp8 values (podcast transcript, the
+    answer on attention recall): the oracle's recall on those values."""
+    q = e4m3_decode(q8) * float(q_descale)
+    k = e4m3_decode(k8) * float(k_descale)
+    if not (np.all(np.isfinite(q)) and np.all(np.isfinite(k))):
+        raise ValueError("NaN code in q8 or k8")
+    return window_recall(q, k, tile, candidates, scale)

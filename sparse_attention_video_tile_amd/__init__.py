@@ -26,5 +26,6 @@ from .binding import (  # noqa: F401
     sta_restore_order,
     sta_tile_list_len,
     sta_window_recall,
+    sta_window_recall_fp8,
     tile_major_rows,
 )

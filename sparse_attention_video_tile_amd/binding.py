@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libsta.so")
 STA_OK, STA_ERR_INVALID_ARG, STA_ERR_UNSUPPORTED, STA_ERR_HIP = 0, -1, -2, -3
 STA_BF16, STA_F32 = 0, 1
 STA_MAX_HEADS = 256
-ABI_VERSION = 5
+ABI_VERSION = 6
 STA_TILE_MAJOR, STA_RASTER = 0, 1
 
 EXPORTS = (
@@ -40,6 +40,7 @@ EXPORTS = (
     "sta_backward",
     "sta_backward_noalloc",
     "sta_window_recall",
+    "sta_window_recall_fp8",
     "sta_full_attention",
     "sta_last_error",
 )
@@ -115,6 +116,10 @@ def open_library(path: str) -> ctypes.CDLL:
         f.restype = c_int
         f.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                       c_int, c_int, c_int, int3, int3, c_float, c_int, c_void_p]
+    lib.sta_window_recall_fp8.restype = c_int
+    lib.sta_window_recall_fp8.argtypes = [c_void_p] * 4 + [c_int, c_int, c_int, c_int, c_int, c_int, int3,
+                                                           c_void_p, c_int, c_float, c_float, c_float,
+                                                           c_int, c_void_p]
     lib.sta_window_recall.restype = c_int
     lib.sta_window_recall.argtypes = [c_void_p] * 4 + [c_int, c_int, c_int, c_int, c_int, c_int, int3,
                                                        int3, c_int, c_float, c_int, c_int, c_void_p]
@@ -568,6 +573,41 @@ def sta_window_recall(q: torch.Tensor, k: torch.Tensor, tile: Sequence[int], can
                                    B, heads, d, T, H, W, _int_array(tile), _int_array(cand), n,
                                    float(scale), _dtype_code(q), order, _stream(dev))
     _check(rc, "sta_window_recall")
+    return recall
+
+
+def sta_window_recall_fp8(q8: torch.Tensor, k8: torch.Tensor, tile: Sequence[int], candidates,
+                          q_descale: float, k_descale: float, scale: Optional[float] = None,
+                          volume: Optional[Sequence[int]] = None,
+                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """sta_window_recall on fp8 (OCP E4M3) q8, k8 (torch.uint8 codes or
+    torch.float8_e4m3fn) with per-tensor descales: float32 (B, heads,
+    n_candidates)."""
+    lib = load_library()
+    if k8.shape != q8.shape:
+        raise ValueError("k8 must match q8 in shape")
+    if q8.dtype not in _FP8_DTYPES or k8.dtype not in _FP8_DTYPES:
+        raise TypeError("q8 and k8 must be torch.uint8 codes or torch.float8_e4m3fn")
+    B, heads, d, (T, H, W), order = _order_shapes(q8, volume, tile)
+    cand = [int(x) for x in torch.as_tensor(candidates, dtype=torch.int64).reshape(-1).tolist()]
+    if len(cand) == 0 or len(cand) % 3:
+        raise ValueError("candidates must be a non-empty list of (t, h, w) windows")
+    n = len(cand) // 3
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    S = T * H * W if order == STA_RASTER else tile_major_rows((T, H, W), tile)
+    if workspace is None:
+        workspace = torch.empty((2, B, heads, S), dtype=torch.float32, device=q8.device)
+    elif workspace.numel() < 2 * B * heads * S or workspace.dtype != torch.float32 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous float32 tensor of at least 2*B*heads*S elements")
+    recall = torch.empty((B, heads, n), dtype=torch.float32, device=q8.device)
+    dev = _require_gpu(q8, k8, recall, workspace)
+    with torch.cuda.device(dev):
+        rc = lib.sta_window_recall_fp8(q8.data_ptr(), k8.data_ptr(), recall.data_ptr(),
+                                       workspace.data_ptr(), B, heads, d, T, H, W, _int_array(tile),
+                                       _int_array(cand), n, float(scale), float(q_descale),
+                                       float(k_descale), order, _stream(dev))
+    _check(rc, "sta_window_recall_fp8")
     return recall
 
 

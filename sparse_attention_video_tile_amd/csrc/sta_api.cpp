@@ -256,7 +256,7 @@ int forward_common(const void* q, const void* k, const void* v, void* out, float
 
 extern "C" {
 
-int sta_abi_version(void) { return 5; }
+int sta_abi_version(void) { return 6; }
 
 const char* sta_last_error(void) { return g_last_error.c_str(); }
 
@@ -505,10 +505,13 @@ int sta_backward_noalloc(const void* q, const void* k, const void* v, const void
                          tile, window, scale, dtype, order, stream, true);
 }
 
-int sta_window_recall(const void* q, const void* k, float* recall, float* workspace, int B,
-                      int heads, int head_dim, int T, int H, int W, const int* tile,
-                      const int* candidates, int n_candidates, float scale, int dtype, int order,
-                      void* stream) {
+namespace {
+
+// Window recall for bf16 / float32 q, k, or fp8 codes (qk_fp8: dtype is
+// STA_BF16, scale already carries the descales).
+int recall_common(const void* q, const void* k, float* recall, float* workspace, int B, int heads,
+                  int head_dim, int T, int H, int W, const int* tile, const int* candidates,
+                  int n_candidates, float scale, int dtype, int order, void* stream, bool qk_fp8) {
   if (!q || !k || !recall || !workspace || !candidates)
     return fail(STA_ERR_INVALID_ARG, "a pointer is NULL");
   if (n_candidates <= 0) return fail(STA_ERR_INVALID_ARG, "n_candidates=%d must be positive", n_candidates);
@@ -541,7 +544,7 @@ int sta_window_recall(const void* q, const void* k, float* recall, float* worksp
     return fail(STA_ERR_INVALID_ARG, "recall and workspace must be 4-byte aligned");
   const long long BH = (long long)B * heads;
   if (BH > (1LL << 24)) return fail(STA_ERR_INVALID_ARG, "B*heads=%lld is too large", BH);
-  const size_t tb = (size_t)BH * win.g.S * head_dim * es;
+  const size_t tb = (size_t)BH * win.g.S * head_dim * (qk_fp8 ? 1 : es);
   const size_t wb = 2 * (size_t)BH * win.g.S * sizeof(float);
   const size_t rb = (size_t)BH * n_candidates * sizeof(float);
   if (overlaps(workspace, wb, q, tb) || overlaps(workspace, wb, k, tb) ||
@@ -552,14 +555,14 @@ int sta_window_recall(const void* q, const void* k, float* recall, float* worksp
   // full-attention lse (token order does not matter for all-keys attention)
   dense.q = q; dense.k = k; dense.v = k; dense.out = nullptr; dense.lse = lse_full;
   dense.B = B; dense.heads = heads; dense.head_dim = head_dim; dense.dtype = dtype; dense.scale = scale;
-  dense.dense = true; dense.raster = false; dense.lse_only = true; dense.qk_fp8 = false;
+  dense.dense = true; dense.raster = false; dense.lse_only = true; dense.qk_fp8 = qk_fp8;
   memset(&dense.g, 0, sizeof(dense.g));
   dense.g.S = win.g.S;
   rc = sta::launch_attention(dense, stream);
   if (rc) return rc < 0 ? fail(rc, "no kernel for dtype %d with head_dim %d", dtype, head_dim) : launched(rc);
   win.q = q; win.k = k; win.v = k; win.out = nullptr; win.lse = lse_win;
   win.B = B; win.heads = heads; win.head_dim = head_dim; win.dtype = dtype; win.scale = scale;
-  win.dense = false; win.raster = order == STA_RASTER; win.lse_only = true; win.qk_fp8 = false;
+  win.dense = false; win.raster = order == STA_RASTER; win.lse_only = true; win.qk_fp8 = qk_fp8;
   for (int c = 0; c < n_candidates; ++c) {
     for (int h = 0; h < heads; ++h) {
       win.omega[h][0] = (uint16_t)(candidates[3 * c] / win.g.ct);
@@ -573,6 +576,33 @@ int sta_window_recall(const void* q, const void* k, float* recall, float* worksp
     if (rc) return launched(rc);
   }
   return ok();
+}
+
+}  // namespace
+
+int sta_window_recall(const void* q, const void* k, float* recall, float* workspace, int B,
+                      int heads, int head_dim, int T, int H, int W, const int* tile,
+                      const int* candidates, int n_candidates, float scale, int dtype, int order,
+                      void* stream) {
+  return recall_common(q, k, recall, workspace, B, heads, head_dim, T, H, W, tile, candidates,
+                       n_candidates, scale, dtype, order, stream, false);
+}
+
+int sta_window_recall_fp8(const void* q8, const void* k8, float* recall, float* workspace, int B,
+                          int heads, int head_dim, int T, int H, int W, const int* tile,
+                          const int* candidates, int n_candidates, float scale, float q_descale,
+                          float k_descale, int order, void* stream) {
+  if (!(q_descale > 0.0f) || !isfinite(q_descale) || !(k_descale > 0.0f) || !isfinite(k_descale))
+    return fail(STA_ERR_INVALID_ARG, "descales %g, %g must be finite and positive",
+                (double)q_descale, (double)k_descale);
+  if (head_dim != 128)
+    return fail(STA_ERR_UNSUPPORTED, "head_dim %d: the fp8 kernels need 128", head_dim);
+  const float folded = scale * q_descale * k_descale;
+  if (!(scale > 0.0f) || !isfinite(scale) || !(folded > 0.0f) || !isfinite(folded))
+    return fail(STA_ERR_INVALID_ARG, "scale %g times the descales must be finite and positive",
+                (double)scale);
+  return recall_common(q8, k8, recall, workspace, B, heads, head_dim, T, H, W, tile, candidates,
+                       n_candidates, folded, STA_BF16, order, stream, true);
 }
 
 int sta_full_attention(const void* q, const void* k, const void* v, void* out, int B, int heads,

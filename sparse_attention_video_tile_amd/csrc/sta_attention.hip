@@ -742,14 +742,23 @@ unsigned raster_table_bytes(const AttnProblem& pr) {
 }
 
 // FULL implies !PAD; plane chunks imply FULL (whole 64-key chunks per tile).
-// QK8 (fp8 q and k) has no log-sum-exp-only form; the host never asks for one.
 template <int D, int WAVES, int RB, int BN, bool PAD, bool FULL, bool QK8>
 void launch_sparse(const AttnProblem& pr, const AttnParams& p, unsigned grid, unsigned table,
                    hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
   const bool plane = FULL && BN == 64 && p.plane_cpt > 0;
   if constexpr (QK8) {
-    if (pr.raster && plane)
+    if (pr.lse_only) {   // window recall on fp8 q and k
+      if (pr.raster && plane)
+        hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, true, false, true, true, true>),
+                           dim3(grid), dim3(C::kThreads), 0, stream, p);
+      else if (pr.raster)
+        hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, true, PAD, false, FULL, true>),
+                           dim3(grid), dim3(C::kThreads), table, stream, p);
+      else
+        hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false, true, PAD, false, FULL, true>),
+                           dim3(grid), dim3(C::kThreads), 0, stream, p);
+    } else if (pr.raster && plane)
       hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, false, false, true, true, true>),
                          dim3(grid), dim3(C::kThreads), 0, stream, p);
     else if (pr.raster)
@@ -807,7 +816,16 @@ int launch_bf16_planned(const AttnProblem& pr, const AttnParams& p, unsigned gri
   const bool full = chunks_full(pr, BN);
   const unsigned table = (full && BN == 64 && p.plane_cpt > 0) ? 0 : raster_table_bytes(pr);
   if constexpr (QK8) {
-    if (pr.dense || pr.lse_only) return STA_ERR_UNSUPPORTED;
+    if (pr.dense && !pr.lse_only) return STA_ERR_UNSUPPORTED;
+    if (pr.dense) {   // the full-attention pass of window recall on fp8 q and k
+      if (full)
+        hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false, true, false, false, true, true>),
+                           dim3(grid), dim3(C::kThreads), 0, stream, p);
+      else
+        hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, true, false, true, false, false, false, true>),
+                           dim3(grid), dim3(C::kThreads), 0, stream, p);
+      return (int)hipGetLastError();
+    }
     if (pr.g.padded)
       launch_sparse<D, WAVES, RB, BN, true, false, true>(pr, p, grid, table, stream);
     else if (full)

@@ -416,6 +416,10 @@ void run_valid(const Problem& pr) {
     const int want_recall = f32_padded || (padded && order == 0) ? STA_ERR_UNSUPPORTED : STA_OK;
     rc = sta_window_recall(slot(0), slot(1), reinterpret_cast<float*>(wslot(2)), reinterpret_cast<float*>(wslot(3)), pr.B, pr.heads, pr.d, pr.T, pr.H, pr.W, t, cands, 2, scale, pr.dtype, order, nullptr);
     if (rc != STA_ERR_UNSUPPORTED || !strstr(sta_last_error(), "raster")) expect(rc, want_recall, "sta_window_recall");
+    if (pr.dtype == STA_BF16 && pr.d == 128) {
+      rc = sta_window_recall_fp8(slot(0), slot(1), reinterpret_cast<float*>(wslot(2)), reinterpret_cast<float*>(wslot(3)), pr.B, pr.heads, pr.d, pr.T, pr.H, pr.W, t, cands, 2, scale, 0.5f, 0.25f, order, nullptr);
+      if (rc != STA_ERR_UNSUPPORTED || !strstr(sta_last_error(), "raster")) expect(rc, want_recall, "sta_window_recall_fp8");
+    }
   }
   // the dense comparator once at the large shape, on every small one
   if ((long long)pr.T * pr.H * pr.W > 20000 && strcmp(pr.name, "sta_30x48x80_whole_volume") != 0) return;

@@ -175,6 +175,26 @@ def test_forward_fp8_lse_rejects_bad_arguments(lib):
     assert "output overlaps" in binding.last_error()
 
 
+def test_window_recall_fp8_rejects_bad_arguments(lib):
+    t = i3(6, 8, 8)
+    cands = binding._int_array([18, 24, 24, 30, 48, 80])
+    f = lib.sta_window_recall_fp8
+    n = 30 * 48 * 80 * 128
+    q8, k8, rec, ws = FAKE, FAKE + 4 * n, FAKE + 8 * n, FAKE + 12 * n
+
+    def call(d=128, qd=1.0, kd=1.0, nc=2, order=1, ws=ws):
+        return f(q8, k8, rec, ws, 1, 1, d, 30, 48, 80, t, cands, nc, 0.1, qd, kd, order, None)
+
+    assert call(qd=-1.0) == -1
+    assert call(kd=float("nan")) == -1
+    assert call(d=64) == binding.STA_ERR_UNSUPPORTED
+    assert call(nc=0) == -1
+    assert call(order=3) == -1
+    # the workspace is checked against q8 at one byte an element
+    assert call(ws=q8 + n - 64) == -1
+    assert "overlap" in binding.last_error()
+
+
 def backward_args(**kw):
     a = dict(q=FAKE, k=FAKE * 2000, v=FAKE * 4000, o=FAKE * 6000, do=FAKE * 8000, lse=FAKE * 10000,
              dq=FAKE * 12000, dk=FAKE * 14000, dv=FAKE * 16000, delta=FAKE * 18000, B=1, heads=1,

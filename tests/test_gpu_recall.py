@@ -1,6 +1,7 @@
 """GPU: window recall (share of full-attention probability kept by a candidate
 window, averaged over query rows) against the float64 oracle on small seeded
-workloads in both token orders, and its invariants at the 30x48x80 shape."""
+workloads in both token orders, and its invariants at the 30x48x80 shape; the
+same on fp8 (E4M3) queries and keys."""
 
 import numpy as np
 import pytest
@@ -8,7 +9,8 @@ import torch
 
 import oracle
 from sparse_attention_video_tile_amd import binding, workloads
-from tests.parity_util import LSE_FP32_SUM_MAX_ABS, RECALL_MAX_ABS, default_scale, to_gpu
+from tests.parity_util import (LSE_FP32_SUM_MAX_ABS, RECALL_MAX_ABS, default_scale, e4m3_codes,
+                               e4m3_descale, to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,3 +92,48 @@ def test_recall_full_size_invariants():
     assert np.abs(r[..., 2] - 1.0).max() <= RECALL_FULL_SIZE_ABS
     assert np.all(r[..., 0] <= r[..., 1] + 1e-6) and np.all(r[..., 1] <= r[..., 2] + 1e-6)
     assert np.abs(r - rt).max() <= 1e-4
+
+
+FP8_CASES = [CASES[0], CASES[2], ("padded_tile96", (7, 12, 20), (3, 4, 8), [(3, 4, 8), (6, 8, 16)], 2, 128, "bf16")]
+
+
+# recall on a padded grid is defined for raster order only (the API refuses
+# tile-major there), so the padded case runs in raster order
+FP8_RUNS = [(c, o) for c in FP8_CASES for o in ("raster", "tile_major")
+            if o == "raster" or not any(n % t for n, t in zip(c[1], c[2]))]
+
+
+@pytest.mark.parametrize("case,order", FP8_RUNS, ids=lambda x: x[0] if isinstance(x, tuple) else x)
+def test_recall_fp8_matches_oracle(case, order):
+    """Window recall on fp8 (E4M3) q and k: the oracle's recall on the decoded
+    values, to the bound of the float32 log-sum-exp passes; and the bf16
+    recall on the decoded values (the same exact products) agrees to the
+    same bound."""
+    name, volume, tile, cands, heads, d, dtype = case
+    w = workloads.small_case(volume, tile, [cands[0]] * heads, head_dim=d, dtype=dtype, B=2, seed=41,
+                             name=name, sinusoid_amp=0.5)
+    print(f"[case] recall fp8 {order} {w}", flush=True)
+    inp = workloads.make_inputs(w)
+    qd, kd = e4m3_descale(inp.q), e4m3_descale(inp.k)
+    q8, k8 = e4m3_codes(inp.q, qd), e4m3_codes(inp.k, kd)
+    scale = default_scale(d)
+    q8g, k8g = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (q8, k8))
+    qb = to_gpu(oracle.e4m3_decode(q8) * qd, "bf16")
+    kb = to_gpu(oracle.e4m3_decode(k8) * kd, "bf16")
+    if order == "raster":
+        got = binding.sta_window_recall_fp8(q8g, k8g, tile, cands, qd, kd, scale)
+        via_bf16 = binding.sta_window_recall(qb, kb, tile, cands, scale)
+    else:
+        q8t, k8t = (torch.from_numpy(np.ascontiguousarray(oracle.to_tile_major(x, tile))).cuda()
+                    for x in (q8, k8))
+        got = binding.sta_window_recall_fp8(q8t, k8t, tile, cands, qd, kd, scale, volume=volume)
+        qt, kt = binding.sta_reorder_tiles(qb, tile), binding.sta_reorder_tiles(kb, tile)
+        via_bf16 = binding.sta_window_recall(qt, kt, tile, cands, scale, volume=volume)
+    torch.cuda.synchronize()
+    ref = oracle.window_recall_fp8(q8, k8, tile, cands, scale, qd, kd)
+    err = np.abs(got.cpu().numpy().astype(np.float64) - ref).max()
+    err_b = np.abs(got.cpu().numpy().astype(np.float64) - via_bf16.cpu().numpy()).max()
+    print(f"[parity] fp8 {name} {order} recall max_abs {err:.3e}, vs bf16 on decoded {err_b:.3e}",
+          flush=True)
+    assert err <= RECALL_MAX_ABS
+    assert err_b <= 2 * RECALL_MAX_ABS

@@ -168,3 +168,45 @@ def test_lse_fp8_descales_fold_into_the_scale_and_commute():
     c = oracle.sta_lse_fp8(q8, k8, w.tile, inp.windows, s, kd, qd)
     assert np.allclose(a, b, rtol=0, atol=1e-12)
     assert np.allclose(a, c, rtol=0, atol=1e-12)
+
+
+def test_recall_fp8_closed_forms():
+    """Zero query codes: every key gets the same full-attention probability,
+    so a window keeps its share of the keys; the whole volume keeps all of it;
+    nested windows keep more."""
+    w, inp = _case()
+    kd = e4m3_descale(inp.k)
+    k8 = e4m3_codes(inp.k, kd)
+    q8 = np.zeros(inp.q.shape, dtype=np.uint8)
+    cands = [(2, 4, 4), (4, 4, 4), (4, 8, 8)]
+    r = oracle.window_recall_fp8(q8, k8, w.tile, cands, 0.2, 1.0, kd)
+    S = int(np.prod(w.volume))
+    toks = np.arange(S)
+    for c, win in enumerate(cands):
+        share = oracle.token_mask_rows(w.volume, w.tile, win, toks).sum() / (S * S)
+        assert np.allclose(r[0, :, c], share, rtol=0, atol=1e-12)
+    qd = e4m3_descale(inp.q)
+    q8 = e4m3_codes(inp.q, qd)
+    r = oracle.window_recall_fp8(q8, k8, w.tile, cands, 1.0 / math.sqrt(128), qd, kd)
+    assert np.allclose(r[..., 2], 1.0, rtol=0, atol=1e-12)
+    assert np.all(r[..., 0] < r[..., 1]) and np.all(r[..., 1] < r[..., 2])
+
+
+def test_recall_fp8_is_the_recall_of_torch_decoded_values():
+    """The fp8 recall equals the recall definition evaluated directly, with
+    scipy, on values decoded by torch's float8_e4m3fn type: the mean over
+    rows of the full softmax mass on the window's keys."""
+    w, inp = _case(seed=7)
+    qd, kd = e4m3_descale(inp.q), e4m3_descale(inp.k)
+    q8, k8 = e4m3_codes(inp.q, qd), e4m3_codes(inp.k, kd)
+    s = 1.0 / math.sqrt(128)
+    win = (2, 4, 4)
+    r = oracle.window_recall_fp8(q8, k8, w.tile, [win], s, qd, kd)
+    qt = torch.from_numpy(q8).view(torch.float8_e4m3fn).to(torch.float64).numpy() * qd
+    kt = torch.from_numpy(k8).view(torch.float8_e4m3fn).to(torch.float64).numpy() * kd
+    toks = np.arange(int(np.prod(w.volume)))
+    mask = oracle.token_mask_rows(w.volume, w.tile, win, toks)
+    for h in range(w.heads):
+        sc = s * qt[0, h].reshape(-1, 128) @ kt[0, h].reshape(-1, 128).T
+        p = np.exp(sc - scipy.special.logsumexp(sc, axis=1, keepdims=True))
+        assert np.allclose(r[0, h, 0], (p * mask).sum(axis=1).mean(), rtol=0, atol=1e-12)
