@@ -21,6 +21,7 @@ CASES = [
     ("tile64_d64", (12, 16, 16), (4, 4, 4), [(4, 8, 12)], 64, "bf16"),
     ("tile48_ragged", (9, 8, 12), (3, 4, 4), [(6, 4, 8), (9, 8, 12)], 128, "bf16"),
     ("tile128", (8, 8, 16), (4, 4, 8), [(4, 8, 8)], 128, "bf16"),
+    ("tile192", (9, 16, 24), (3, 8, 8), [(6, 16, 16), (9, 8, 24)], 128, "bf16"),
     ("tile8_tiny", (4, 4, 6), (2, 2, 2), [(2, 2, 2), (4, 2, 4)], 64, "bf16"),
     ("image_2d_tile8x8", (1, 32, 48), (1, 8, 8), [(1, 24, 24), (1, 8, 16)], 128, "bf16"),
     ("f32_d64", (12, 16, 16), (4, 4, 4), [(12, 12, 12), (4, 8, 12)], 64, "f32"),
@@ -117,7 +118,8 @@ def test_backward_matches_oracle(case, order):
         assert_grad_close(g.float().cpu().numpy(), r, dtype, f"{name} {order} {nm}")
 
 
-@pytest.mark.parametrize("case", CASES[:4] + CASES[6:], ids=lambda c: c[0])
+@pytest.mark.parametrize("case", [c for c in CASES if c[0] not in ("tile128", "tile8_tiny")],
+                         ids=lambda c: c[0])
 def test_backward_orders_agree_bit_for_bit(case):
     name, volume, tile, windows, d, dtype = case
     w = workloads.small_case(volume, tile, windows, head_dim=d, dtype=dtype, seed=23, name=name)
