@@ -857,9 +857,7 @@ int launch_bf16_pair_pass(const BwdProblem& pr, hipStream_t stream) {
       hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, PAIRS, RB, 64, true, false, true>), dim3(grid), dim3(kThreads), lds, stream, p, b);
     else
       hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, PAIRS, RB, 64, false, false, true>), dim3(grid), dim3(kThreads), 0, stream, p, b);
-    return (int)hipGetLastError();
-  }
-  if (pr.attn.g.padded) {
+  } else if (pr.attn.g.padded) {
     if (raster)
       hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, PAIRS, RB, 64, true, true, false>), dim3(grid), dim3(kThreads), lds, stream, p, b);
     else
