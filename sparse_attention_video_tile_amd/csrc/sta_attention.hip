@@ -92,23 +92,49 @@ __device__ __forceinline__ void qk_step(WaveState<C, RB>& w, f32x4 (&sc)[RB][C::
   }
 }
 
+// This lane's keys of a chunk that are tokens: bit 4*kt + r for key
+// 16*kt + 4g + r (the lane's keys in the S^T layout), from the chunk's token
+// mask `real` and its key count nvalid.
+__device__ __forceinline__ unsigned lane_key_mask(unsigned long long real, int nvalid, int g) {
+  const unsigned long long v = nvalid >= 64 ? real : real & ((1ull << nvalid) - 1ull);
+  const unsigned long long x = v >> (4 * g);
+  unsigned km = 0;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) km |= (unsigned)((x >> (16 * kt)) & 0xFull) << (4 * kt);
+  return km;
+}
+
+// Initial accumulator of score tile kt: 0 for this lane's keys that are
+// tokens, -inf for the others. The MFMAs add finite products (such keys load a
+// token's row), so their scores come out -inf and their probabilities 0,
+// with no test after the products.
+__device__ __forceinline__ f32x4 key_bias(unsigned km, int kt) {
+  f32x4 b;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) b[r] = ((km >> (4 * kt + r)) & 1u) ? 0.f : -INFINITY;
+  return b;
+}
+
 // Scores S^T[key][row] = K Q^T for one chunk; lane (l16, g) ends up with keys
-// 16*kt + 4g + r of query row l16 of each 16-row block.
-template <class C, int RB>
+// 16*kt + 4g + r of query row l16 of each 16-row block. MASK: keys outside
+// km score -inf.
+template <class C, int RB, bool MASK = false>
 __device__ __forceinline__ void qk_into(WaveState<C, RB>& w, f32x4 (&sc)[RB][C::kKT],
-                                        const char* kbuf, int l16, int g) {
+                                        const char* kbuf, int l16, int g, unsigned km = 0) {
 #pragma unroll
   for (int kt = 0; kt < C::kKT; ++kt) {
+    const f32x4 init = MASK ? key_bias(km, kt) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) sc[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) sc[rb][kt] = init;
 #pragma unroll
     for (int dk = 0; dk < C::kDK; ++dk) qk_step<C, RB>(w, sc, kt, dk, kbuf);
   }
 }
 
-template <class C, int RB>
-__device__ __forceinline__ void qk_chunk(WaveState<C, RB>& w, const char* kbuf, int l16, int g) {
-  qk_into<C, RB>(w, w.s, kbuf, l16, g);
+template <class C, int RB, bool MASK = false>
+__device__ __forceinline__ void qk_chunk(WaveState<C, RB>& w, const char* kbuf, int l16, int g,
+                                         unsigned km = 0) {
+  qk_into<C, RB, MASK>(w, w.s, kbuf, l16, g, km);
 }
 
 // Moves each row's reference max to the larger of it and the row's maximum
@@ -275,10 +301,11 @@ __device__ __forceinline__ void sched_reads_ahead() {
 // runs the max-first order of the masked path instead.
 
 // S^T of score tile kt (keys 16*kt ..) for every row block.
-template <class C, int RB>
-__device__ __forceinline__ void qk_tile(WaveState<C, RB>& w, int kt, const char* kbuf) {
+template <class C, int RB, bool MASK = false>
+__device__ __forceinline__ void qk_tile(WaveState<C, RB>& w, int kt, const char* kbuf, unsigned km = 0) {
+  const f32x4 init = MASK ? key_bias(km, kt) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) w.s[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < RB; ++rb) w.s[rb][kt] = init;
 #pragma unroll
   for (int dk = 0; dk < C::kDK; ++dk) qk_step<C, RB>(w, w.s, kt, dk, kbuf);
 }
@@ -524,21 +551,28 @@ attn_bf16_kernel(const AttnParams p) {
     const unsigned long long real = chunk_real_keys<PAD && !DENSE>(p, walk, it, lane);
     wait_vm_all();     // this wave's loads of chunk `it` have landed in LDS
     __syncthreads();   // ... and every wave's; chunk it-1's buffers are free
-    if constexpr (FULL && !decltype(first)::value) {
+    if constexpr (!decltype(first)::value) {
+      // Every chunk after the first: the probabilities of score tile kt go
+      // out between the QK^T MFMAs of tile kt + 1, and one sum test per chunk
+      // stands in for the chunk maximum. Keys that are not tokens (padding,
+      // a ragged run end) start at -inf (key_bias) instead of being masked
+      // after the products.
+      constexpr bool kMask = !FULL;
+      const unsigned km = kMask ? lane_key_mask(real, nvalid, g) : 0u;
       float lc[RB];
       if constexpr (LSE_ONLY) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) lc[rb] = 0.f;
 #pragma unroll
         for (int kt = 0; kt < C::kKT; ++kt) {
-          qk_tile<C, RB>(w, kt, kcur);
+          qk_tile<C, RB, kMask>(w, kt, kcur, km);
           if (kt > 0) exp_sum_tile<C, RB>(w, kt - 1, p.scale_log2, lc);
         }
         exp_sum_tile<C, RB>(w, C::kKT - 1, p.scale_log2, lc);
       } else {
 #pragma unroll
         for (int kt = 0; kt < C::kKT; ++kt) {
-          qk_tile<C, RB>(w, kt, kcur);
+          qk_tile<C, RB, kMask>(w, kt, kcur, km);
           if (kt > 0) exp_tile<C, RB>(w, kt - 1, p.scale_log2);
         }
         exp_tile<C, RB>(w, C::kKT - 1, p.scale_log2);
@@ -563,7 +597,7 @@ attn_bf16_kernel(const AttnParams p) {
       for (int rb = 0; rb < RB; ++rb) grow |= !(lc[rb] <= 256.0f);   // also an infinite sum
       if (__any(grow)) {
         keep_branch();
-        qk_chunk<C, RB>(w, kcur, l16, g);
+        qk_chunk<C, RB, kMask>(w, kcur, l16, g, km);
         float mx[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -592,7 +626,7 @@ attn_bf16_kernel(const AttnParams p) {
         sched_reads_ahead<RB, C::kKP * C::kDB, 2, kReadAhead>();
       }
     } else {
-      // Chunks that may hold masked keys (a ragged run end, padding positions).
+      // The first chunk: products, then masking and the lane maxima.
       qk_chunk<C, RB>(w, kcur, l16, g);
       sched_reads_ahead<RB, C::kKT * C::kDK, QK8 ? 2 : 1, kReadAhead>();
       __builtin_amdgcn_sched_barrier(0);
@@ -614,19 +648,14 @@ attn_bf16_kernel(const AttnParams p) {
       if (it + 1 < walk.n_chunks) dma(it + 1, kb0, vb0);
     }
   };
-  if constexpr (FULL) {
-    // The first chunk sets the reference max: the max-first order, which the
-    // sum test would otherwise send down its rare branch every time.
-    chunk_step(FirstChunk<true>{}, kb0, vb0, kb1, vb1, 0);
-    for (int it = 1; it < walk.n_chunks; it += 2) {
-      chunk_step(FirstChunk<false>{}, kb1, vb1, kb0, vb0, it);
-      if (it + 1 < walk.n_chunks) chunk_step(FirstChunk<false>{}, kb0, vb0, kb1, vb1, it + 1);
-    }
-  } else {
-    for (int it = 0; it < walk.n_chunks; it += 2) {
-      chunk_step(FirstChunk<false>{}, kb0, vb0, kb1, vb1, it);
-      if (it + 1 < walk.n_chunks) chunk_step(FirstChunk<false>{}, kb1, vb1, kb0, vb0, it + 1);
-    }
+  // The first chunk sets the reference max: the max-first order (with the
+  // masks of its keys that are not tokens), which the sum test would
+  // otherwise send down its rare branch every time. A work item's first
+  // chunk always holds a token (its window's first tile starts at one).
+  chunk_step(FirstChunk<true>{}, kb0, vb0, kb1, vb1, 0);
+  for (int it = 1; it < walk.n_chunks; it += 2) {
+    chunk_step(FirstChunk<false>{}, kb1, vb1, kb0, vb0, it);
+    if (it + 1 < walk.n_chunks) chunk_step(FirstChunk<false>{}, kb0, vb0, kb1, vb1, it + 1);
   }
   // The row map is built again rather than kept in registers across the loop.
   store_out<C, RB>(w, LSE_ONLY ? nullptr : og, p.lse ? p.lse + t.head_base / D : nullptr,
