@@ -92,29 +92,6 @@ __device__ __forceinline__ void qk_step(WaveState<C, RB>& w, f32x4 (&sc)[RB][C::
   }
 }
 
-// This lane's keys of a chunk that are tokens: bit 4*kt + r for key
-// 16*kt + 4g + r (the lane's keys in the S^T layout), from the chunk's token
-// mask `real` and its key count nvalid.
-__device__ __forceinline__ unsigned lane_key_mask(unsigned long long real, int nvalid, int g) {
-  const unsigned long long v = nvalid >= 64 ? real : real & ((1ull << nvalid) - 1ull);
-  const unsigned long long x = v >> (4 * g);
-  unsigned km = 0;
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) km |= (unsigned)((x >> (16 * kt)) & 0xFull) << (4 * kt);
-  return km;
-}
-
-// Initial accumulator of score tile kt: 0 for this lane's keys that are
-// tokens, -inf for the others. The MFMAs add finite products (such keys load a
-// token's row), so their scores come out -inf and their probabilities 0,
-// with no test after the products.
-__device__ __forceinline__ f32x4 key_bias(unsigned km, int kt) {
-  f32x4 b;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) b[r] = ((km >> (4 * kt + r)) & 1u) ? 0.f : -INFINITY;
-  return b;
-}
-
 // Scores S^T[key][row] = K Q^T for one chunk; lane (l16, g) ends up with keys
 // 16*kt + 4g + r of query row l16 of each 16-row block. MASK: keys outside
 // km score -inf.

@@ -192,6 +192,30 @@ __device__ __forceinline__ void load_rows_plane(const void* src, int chunk_row0,
   }
 }
 
+// This lane's streamed rows of a chunk that are tokens: bit 4*kt + r for row
+// 16*kt + 4g + r of the chunk (the rows a lane holds in a 16x16 MFMA result
+// tile kt, lane = l16 + 16g), from the chunk's token mask `real` and its row
+// count nvalid.
+__device__ __forceinline__ unsigned lane_key_mask(unsigned long long real, int nvalid, int g) {
+  const unsigned long long v = nvalid >= 64 ? real : real & ((1ull << nvalid) - 1ull);
+  const unsigned long long x = v >> (4 * g);
+  unsigned km = 0;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) km |= (unsigned)((x >> (16 * kt)) & 0xFull) << (4 * kt);
+  return km;
+}
+
+// Initial accumulator of score tile kt: 0 for this lane's rows that are
+// tokens, -inf for the others. The MFMAs add finite products (such rows load a
+// token's row), so their scores come out -inf and their probabilities 0,
+// with no test after the products.
+__device__ __forceinline__ f32x4 key_bias(unsigned km, int kt) {
+  f32x4 b;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) b[r] = ((km >> (4 * kt + r)) & 1u) ? 0.f : -INFINITY;
+  return b;
+}
+
 __device__ __forceinline__ void wait_vm_all() {
   // vmcnt(0); expcnt and lgkmcnt left at their maxima (not waited on).
   __builtin_amdgcn_s_waitcnt(0x0F70);

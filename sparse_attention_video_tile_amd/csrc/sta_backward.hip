@@ -84,15 +84,17 @@ __device__ __forceinline__ void lane_voff(int (&voff)[C::kDB], int l16, int g) {
 
 // acc[rb][kt] = X Y^T for one chunk: X = the buffer's rows (16*kt ..), Y = the
 // wave's own rows held as fragments fr. Lane (l16, g) receives buffer rows
-// 16*kt + 4g + r against own row l16 of block rb.
-template <class C, int RB>
+// 16*kt + 4g + r against own row l16 of block rb. MASK: buffer rows outside
+// the lane's token mask km start at -inf, so their scores are -inf.
+template <class C, int RB, bool MASK = false>
 __device__ __forceinline__ void mma_rows(f32x4 (&acc)[RB][C::kKT], const char* buf,
                                          const int (&koff)[C::kDK],
-                                         const bf16x8 (&fr)[RB][C::kDK]) {
+                                         const bf16x8 (&fr)[RB][C::kDK], unsigned km = 0) {
 #pragma unroll
   for (int kt = 0; kt < C::kKT; ++kt) {
+    const f32x4 init = MASK ? key_bias(km, kt) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) acc[rb][kt] = init;
 #pragma unroll
     for (int dk = 0; dk < C::kDK; ++dk) {
       const bf16x8 x = *reinterpret_cast<const bf16x8*>(buf + koff[dk] + 16 * kt * C::kRowBytes);
@@ -289,8 +291,11 @@ bwd_dq_kernel(const AttnParams p, const BwdParams b) {
     wait_vm_all();
     __syncthreads();
     const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
+    // keys that are not tokens (padding, a ragged run end) score -inf: their
+    // P^T and dS^T come out 0 (their K and V rows are a token's, finite)
+    const unsigned km = FULL ? 0u : lane_key_mask(real, nvalid, g);
     f32x4 s[RB][C::kKT], dp[RB][C::kKT];
-    mma_rows<C, RB>(s, kcur, koff, qf);    // S^T[key][row] = K Q^T
+    mma_rows<C, RB, !FULL>(s, kcur, koff, qf, km);    // S^T[key][row] = K Q^T
     sched_phase<RB, C::kKT * C::kDK, 1, 3, 0>();
     // P^T while dP^T = V dO^T runs
 #pragma unroll
@@ -310,11 +315,8 @@ bwd_dq_kernel(const AttnParams p, const BwdParams b) {
 #pragma unroll
       for (int kt = 0; kt < C::kKT; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = 16 * kt + 4 * g + r;
-          const bool off = !FULL && ((nvalid < C::kBN && key >= nvalid) || !((real >> key) & 1ull));
-          s[rb][kt][r] = off ? 0.f : s[rb][kt][r] * (dp[rb][kt][r] - dl[rb]);   // dS^T
-        }
+        for (int r = 0; r < 4; ++r)
+          s[rb][kt][r] = s[rb][kt][r] * (dp[rb][kt][r] - dl[rb]);   // dS^T
     bf16x8 wf[RB][C::kKP];
     pack_bf16<C, RB>(wf, s);
     mma_tr<C, RB>(acc, kcur, voff, wf);    // dQ^T[d][row] += K^T dS^T
@@ -416,8 +418,11 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
     wait_vm_all();
     __syncthreads();
     const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
+    // query rows that are not tokens score -inf: their P and dS come out 0
+    // (their Q, dO, lse and D are a token's, finite)
+    const unsigned km = FULL ? 0u : lane_key_mask(real, nvalid, g);
     f32x4 s[RB][C::kKT];
-    mma_rows<C, RB>(s, qcur, koff, kf);    // S[q][key] = Q K^T
+    mma_rows<C, RB, !FULL>(s, qcur, koff, kf, km);    // S[q][key] = Q K^T
     sched_phase<RB, C::kKT * C::kDK, 1, 3, 0>();
     __builtin_amdgcn_sched_barrier(0);
     if (it + 1 < walk.n_chunks) dma(it + 1, qnxt, onxt, lnxt, dnxt);
@@ -433,12 +438,8 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
 #pragma unroll
       for (int kt = 0; kt < C::kKT; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qrow = 16 * kt + 4 * g + r;
-          const bool off = !FULL && ((nvalid < C::kBN && qrow >= nvalid) || !((real >> qrow) & 1ull));
-          const float pr = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -lq[kt][r] * kLog2e));
-          s[rb][kt][r] = off ? 0.f : pr;                  // P[q][key]
-        }
+        for (int r = 0; r < 4; ++r)   // P[q][key]
+          s[rb][kt][r] = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -lq[kt][r] * kLog2e));
     bf16x8 wf[RB][C::kKP];
     pack_bf16<C, RB>(wf, s);
     f32x4 dp[RB][C::kKT];
@@ -450,13 +451,8 @@ bwd_dkdv_kernel(const AttnParams p, const BwdParams b) {
 #pragma unroll
       for (int kt = 0; kt < C::kKT; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          // a masked row may carry garbage lse / D (padding rows of a tile-major
-          // tensor are never written): select, do not multiply
-          const int qrow = 16 * kt + 4 * g + r;
-          const bool off = !FULL && ((nvalid < C::kBN && qrow >= nvalid) || !((real >> qrow) & 1ull));
-          s[rb][kt][r] = off ? 0.f : s[rb][kt][r] * (dp[rb][kt][r] - dq_[kt][r]);   // dS
-        }
+        for (int r = 0; r < 4; ++r)   // dS
+          s[rb][kt][r] = s[rb][kt][r] * (dp[rb][kt][r] - dq_[kt][r]);
     bf16x8 wd[RB][C::kKP];
     pack_bf16<C, RB>(wd, s);
     mma_tr<C, RB>(dv, ocur, voff, wf);     // dV^T[d][key] += dO^T P
@@ -556,12 +552,6 @@ bwd_dkdv_pair_kernel(const AttnParams p, const BwdParams b) {
   int koff[C::kDK], voff[C::kDB];
   lane_koff<C>(koff, l16, g);
   lane_voff<C>(voff, l16, g);
-  // Whether query row 16*kt + 4g + r of chunk `it` is a token (else its P and
-  // dS are zero by selection: its lse / D may be garbage).
-  auto row_off = [&](int nvalid, unsigned long long real, int kt, int r) __attribute__((always_inline)) {
-    const int qrow = 16 * kt + 4 * g + r;
-    return !FULL && ((nvalid < C::kBN && qrow >= nvalid) || !((real >> qrow) & 1ull));
-  };
 
   if (wave_p) {
     bf16x8 kf[RB][C::kDK];
@@ -578,8 +568,11 @@ bwd_dkdv_pair_kernel(const AttnParams p, const BwdParams b) {
       wait_vm_all();
       __syncthreads();
       const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
+      // query rows that are not tokens score -inf, so their P is 0 (and so
+      // is wave S's dS, which multiplies P)
+      const unsigned km = FULL ? 0u : lane_key_mask(real, nvalid, g);
       f32x4 s[RB][C::kKT];
-      mma_rows<C, RB>(s, qcur, koff, kf);    // S[q][key] = Q K^T
+      mma_rows<C, RB, !FULL>(s, qcur, koff, kf, km);    // S[q][key] = Q K^T
       sched_phase<RB, C::kKT * C::kDK, 1, 3, 0>();
       __builtin_amdgcn_sched_barrier(0);
       if (it + 1 < walk.n_chunks) dma(it + 1, qnxt, onxt, lnxt, dnxt);
@@ -591,10 +584,8 @@ bwd_dkdv_pair_kernel(const AttnParams p, const BwdParams b) {
 #pragma unroll
         for (int kt = 0; kt < C::kKT; ++kt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float pr = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -lq[kt][r] * kLog2e));
-            s[rb][kt][r] = row_off(nvalid, real, kt, r) ? 0.f : pr;   // P[q][key]
-          }
+          for (int r = 0; r < 4; ++r)   // P[q][key]
+            s[rb][kt][r] = __builtin_amdgcn_exp2f(fmaf(s[rb][kt][r], p.scale_log2, -lq[kt][r] * kLog2e));
       bf16x8 wf[RB][C::kKP];
       pack_bf16<C, RB>(wf, s);
 #pragma unroll
@@ -624,7 +615,6 @@ bwd_dkdv_pair_kernel(const AttnParams p, const BwdParams b) {
       walk.at(it, &row0, &nvalid);
       wait_vm_all();
       __syncthreads();
-      const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
       f32x4 dp[RB][C::kKT];
       mma_rows<C, RB>(dp, ocur, koff, vf);   // dP[q][key] = dO V^T
       sched_phase<RB, C::kKT * C::kDK, 1, 3, 0>();
@@ -644,8 +634,7 @@ bwd_dkdv_pair_kernel(const AttnParams p, const BwdParams b) {
           for (int j = 0; j < 8; ++j) {
             // slot j holds query row 32*kp + 4g + j (j < 4), or + 16 + (j - 4)
             const int kt = 2 * kp + j / 4, r = j % 4;
-            const float ds = static_cast<float>(pw[j]) * (dp[rb][kt][r] - dq_[kt][r]);
-            wd[rb][kp][j] = static_cast<bf16_t>(row_off(nvalid, real, kt, r) ? 0.f : ds);
+            wd[rb][kp][j] = static_cast<bf16_t>(static_cast<float>(pw[j]) * (dp[rb][kt][r] - dq_[kt][r]));
           }
         }
       mma_tr<C, RB>(dk, qcur, voff, wd);     // dK^T[d][key] += Q^T dS
@@ -839,7 +828,9 @@ int launch_bf16_pass(const BwdProblem& pr, hipStream_t stream) {
 // Key side with paired waves: PAIRS pairs of 16 * RB key rows. Sharing more
 // key rows a pair cuts the LDS bytes each MFMA needs (every streamed
 // fragment feeds RB products): 48 rows a pair measured 6-8 % faster than 32
-// on the 30x48x80 workloads, bit-identical gradients.
+// on the 30x48x80 workloads, bit-identical gradients. Rows that are not
+// tokens are handled by -inf starts, not selects, which keeps every variant
+// within the registers.
 template <int D, int PAIRS, int RB>
 int launch_bf16_pair_pass(const BwdProblem& pr, hipStream_t stream) {
   constexpr int kThreads = 2 * PAIRS * 64;
@@ -849,15 +840,7 @@ int launch_bf16_pair_pass(const BwdProblem& pr, hipStream_t stream) {
   const unsigned grid = (unsigned)p.per_xcd * kXcds;
   const bool raster = pr.attn.raster;
   const unsigned lds = raster ? raster_bytes(pr.attn, true) : 0;
-  if constexpr (RB == 3) {
-    // 48 rows a pair fit the registers only without the per-row masking of
-    // padded or ragged chunks (bwd_key_rows picks this shape only then)
-    if (pr.attn.g.padded || pr.attn.g.tau % 64) return STA_ERR_UNSUPPORTED;
-    if (raster)
-      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, PAIRS, RB, 64, true, false, true>), dim3(grid), dim3(kThreads), lds, stream, p, b);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, PAIRS, RB, 64, false, false, true>), dim3(grid), dim3(kThreads), 0, stream, p, b);
-  } else if (pr.attn.g.padded) {
+  if (pr.attn.g.padded) {
     if (raster)
       hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, PAIRS, RB, 64, true, true, false>), dim3(grid), dim3(kThreads), lds, stream, p, b);
     else
@@ -881,7 +864,7 @@ int launch_bf16_bwd(const BwdProblem& pr, hipStream_t stream) {
   // Key side: pairs of waves sharing 32 key rows (or 16 key rows per wave on
   // small tiles); query side: 32 query rows per wave.
   const int tau = pr.attn.g.tau;
-  const int kr = bwd_key_rows(tau, pr.attn.g.padded);
+  const int kr = bwd_key_rows(tau);
   int rc = kr == 192   ? launch_bf16_pair_pass<D, 4, 3>(pr, stream)
            : kr == 128 ? launch_bf16_pair_pass<D, 4, 2>(pr, stream)
                        : launch_bf16_pass<D, 4, 1, true>(pr, stream);

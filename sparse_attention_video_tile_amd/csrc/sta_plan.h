@@ -396,13 +396,12 @@ inline int fwd_bf16_rows(int unit_rows) {
 constexpr int kF32Threads = 128;   // float32 forward: one thread per query row
 constexpr int kF32BN = 32;         // float32 forward: keys per chunk
 constexpr int kF32Waves = 4;       // float32 backward: one wave per own row
-// bf16 backward, key side: 4 pairs of waves sharing 48 key rows when every
-// query chunk is 64 tokens (no padding, tau a multiple of 64) and the items
-// tile tau (the only case whose registers hold 48 rows without spilling),
-// else pairs sharing 32 key rows (tiles of at least 128 tokens), else 4
-// waves of 16; query side: 4 waves of 32 query rows, else of 16.
-inline int bwd_key_rows(int tau, bool padded) {
-  if (!padded && tau % 64 == 0 && tau % 192 == 0) return 192;
+// bf16 backward, key side: 4 pairs of waves sharing 48 key rows when such
+// items tile tau, else pairs sharing 32 key rows (tiles of at least 128
+// tokens), else 4 waves of 16; query side: 4 waves of 32 query rows, else of
+// 16.
+inline int bwd_key_rows(int tau) {
+  if (tau % 192 == 0) return 192;
   return tau >= 128 ? 128 : 64;
 }
 inline int bwd_query_rows(int tau) { return tau >= 128 ? 128 : 64; }

@@ -335,7 +335,7 @@ int launch_backward(const BwdProblem& pb, void*) {
     ++g_ctx.launches;
     return 0;
   }
-  const int kr = bwd_key_rows(a.g.tau, a.g.padded), qr = bwd_query_rows(a.g.tau);
+  const int kr = bwd_key_rows(a.g.tau), qr = bwd_query_rows(a.g.tau);
   if (kr == 192 && qr == 128) model_bf16_backward<192, 128>(pb);
   else if (kr == 128 && qr == 128) model_bf16_backward<128, 128>(pb);
   else if (kr == 64 && qr == 64) model_bf16_backward<64, 64>(pb);
