@@ -2,10 +2,10 @@
 the benchmark times (the raster-order kernel). The oracle computes sampled
 query rows one by one (corner, edge and interior tiles of several heads), and
 every row of one whole head of the (18,24,24) workload and of the mixed
-workload's heaviest head that is not the whole volume (a process pool of the
-oracle over the host's cores); whole-volume STA is also compared element by
-element with the dense kernel, and the raster-order kernel with the reorder +
-tile-major path."""
+workload's heaviest head that is not the whole volume, and the last four
+tiles of every head (a process pool of the oracle over the host's cores);
+whole-volume STA is also compared element by element with the dense kernel,
+and the raster-order kernel with the reorder + tile-major path."""
 
 import time
 
@@ -104,6 +104,32 @@ def test_full_size_sampled_rows(w):
         print(f"[parity] whole-volume STA vs dense: max {diff.max().item():.3e} "
               f"mean {diff.mean().item():.3e}", flush=True)
         assert diff.max().item() <= 2e-2 and diff.mean().item() <= 2e-3
+
+
+@pytest.mark.timeout(300)   # input draws, then 96 query tiles of the oracle on the host
+def test_full_size_last_tiles_of_every_head():
+    """Every row of the last four query tiles of every head of the (18,24,24)
+    workload: at 24 heads the 7200 whole-tile work items leave a partly filled
+    last round on each XCD, which runs as 64-row items in a second launch, and
+    those items are last tiles of heads. Checked against the oracle (process
+    pool) element by element."""
+    w = workloads.STA_18_24_24
+    print(f"[case] full size {w.name}: last four tiles of every head", flush=True)
+    inp = workloads.make_inputs(w)
+    q, k, v = (to_gpu(x, w.dtype) for x in (inp.q, inp.k, inp.v))
+    out = binding.sliding_tile_attention(q, k, v, w.tile, inp.windows)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().reshape(w.B, w.heads, -1, w.head_dim)
+    n = oracle.tile_grid(w.volume, w.tile)
+    n_tiles = n[0] * n[1] * n[2]
+    last = list(range(n_tiles - 4, n_tiles))
+    jobs = pool.tile_jobs(w.volume, w.tile, [(0, h) for h in range(w.heads)], tiles=last)
+    ref, wall, workers = pool.sta_attention_pool(inp.q, inp.k, inp.v, w.tile, inp.windows,
+                                                 default_scale(w.head_dim), jobs)
+    print(f"[oracle] {len(jobs)} tiles: {wall:.1f} s on {workers} workers", flush=True)
+    for h in range(w.heads):
+        rows = np.concatenate([oracle.tile_tokens(w.volume, w.tile, t) for t in last])
+        assert_close(got[0, h, rows], ref[(0, h)][rows], w.dtype, f"{w.name} head {h} last tiles")
 
 
 @pytest.mark.parametrize("w", [workloads.STA_18_24_24, workloads.MIXED_HEADS], ids=lambda w: w.name)
