@@ -169,16 +169,17 @@ def time_backward(w, args, torch, binding, q, k, v, windows, fwd_flops, stream, 
 
 def time_recall(w, args, torch, binding, workloads, q, k, stream, ev):
     """sta_window_recall over the five window options of the mixed workload
-    on the headline q, k. Work counted: the QK^T products of the dense
-    log-sum-exp (2 S^2 d per head) and of every candidate window (2 tau^2 d
-    per computed tile pair); the exponentials are not counted."""
+    on the headline q, k. Work counted: the QK^T products of the full-attention
+    log-sum-exp (2 S^2 d per head), which every candidate's sums come out of
+    (one pass; separate candidate passes would add 2 tau^2 d per computed tile
+    pair of each window); the exponentials are not counted."""
     cands = [tuple(c) for c in workloads.MIXED_WINDOW_OPTIONS]
     S = w.seq_len
     tau = w.tile[0] * w.tile[1] * w.tile[2]
     flops = float(w.B) * w.heads * 2.0 * S * S * w.head_dim
-    for c in cands:
-        flops += float(w.B) * binding.sta_kv_pair_count(w.heads, w.volume, w.tile, [c]) * 2.0 * tau * tau * w.head_dim
-    ws = torch.empty((2, w.B, w.heads, S), dtype=torch.float32, device="cuda")
+    per_candidate = sum(float(w.B) * binding.sta_kv_pair_count(w.heads, w.volume, w.tile, [c]) * 2.0 * tau * tau
+                        * w.head_dim for c in cands)
+    ws = torch.empty((len(cands) + 1, w.B, w.heads, S), dtype=torch.float32, device="cuda")
     r = binding.sta_window_recall(q, k, w.tile, cands, workspace=ws)  # warm-up
     torch.cuda.synchronize()
     e0, e1 = ev(), ev()
@@ -192,6 +193,7 @@ def time_recall(w, args, torch, binding, workloads, q, k, stream, ev):
     mean = r.mean(dim=(0, 1)).cpu().tolist()
     del ws, r
     return {"ms": ms, "tflops": tf, "frac_of_peak": tf / BF16_PEAK_TFLOPS, "algorithmic_tflop": flops / 1e12,
+            "candidate_passes_tflop": per_candidate / 1e12,
             "candidates": cands, "mean_recall_on_iid_inputs": mean}
 
 

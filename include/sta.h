@@ -316,14 +316,21 @@ int sta_backward_noalloc(const void* q, const void* k, const void* v, const void
  * window per head by profiling (podcast transcript, the answers on attention
  * recall and on choosing the window per head; dianyo ICML2025 blog, STA
  * section, recall of local windows across prompts).
- * Computed as the mean of exp(lse_c(i) - lse_full(i)) from the two row
+ * Computed as the mean of exp(lse_c(i) - lse_full(i)) from the row
  * log-sum-exps (the attention kernels in a log-sum-exp-only mode: no V, no
  * output; with bf16 inputs this mode sums the probabilities in float32
  * without rounding them to bfloat16, as nothing multiplies them), then a
- * deterministic double-precision reduction per (b, h).
+ * deterministic double-precision reduction per (b, h). With bf16 (or fp8)
+ * inputs, whole 64-key chunks per tile, no padding and at most 8 candidates,
+ * one pass over all keys (the whole volume as the window) also sums each
+ * candidate window's share, since every chunk lies in one key tile; else a
+ * full-attention pass and one pass per candidate.
  *   q, k:        device [B][heads][S][head_dim], token order `order`, read.
  *   recall:      device float [B][heads][n_candidates], written.
- *   workspace:   device float [2][B][heads][S], caller-owned scratch.
+ *   workspace:   device float [n_candidates + 1][B][heads][S], caller-owned;
+ *                written with the row log-sum-exps over all keys (slot 0)
+ *                and over each candidate's window (slot c + 1), in the
+ *                token order of q.
  *   candidates:  host int[n_candidates][3], token windows, each valid for
  *                the volume and tile (same rule as `window`); applied to
  *                every head.

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libsta.so")
 STA_OK, STA_ERR_INVALID_ARG, STA_ERR_UNSUPPORTED, STA_ERR_HIP = 0, -1, -2, -3
 STA_BF16, STA_F32 = 0, 1
 STA_MAX_HEADS = 256
-ABI_VERSION = 6
+ABI_VERSION = 7
 STA_TILE_MAJOR, STA_RASTER = 0, 1
 
 EXPORTS = (
@@ -550,7 +550,9 @@ def sta_window_recall(q: torch.Tensor, k: torch.Tensor, tile: Sequence[int], can
                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Share of full-attention probability each candidate window keeps, averaged
     over the query rows: float32 (B, heads, n_candidates). Raster 6-D tensors,
-    or tile-major 4-D ones with `volume`."""
+    or tile-major 4-D ones with `volume`. `workspace` (float32, (n_candidates +
+    1) * B * heads * S elements) receives the row log-sum-exps: all keys, then
+    each candidate's window."""
     lib = load_library()
     if k.shape != q.shape or k.dtype != q.dtype:
         raise ValueError("k must match q in shape and dtype")
@@ -563,9 +565,11 @@ def sta_window_recall(q: torch.Tensor, k: torch.Tensor, tile: Sequence[int], can
         scale = 1.0 / math.sqrt(d)
     S = T * H * W if order == STA_RASTER else tile_major_rows((T, H, W), tile)
     if workspace is None:
-        workspace = torch.empty((2, B, heads, S), dtype=torch.float32, device=q.device)
-    elif workspace.numel() < 2 * B * heads * S or workspace.dtype != torch.float32 or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous float32 tensor of at least 2*B*heads*S elements")
+        workspace = torch.empty((n + 1, B, heads, S), dtype=torch.float32, device=q.device)
+    elif (workspace.numel() < (n + 1) * B * heads * S or workspace.dtype != torch.float32
+          or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous float32 tensor of at least "
+                         "(n_candidates+1)*B*heads*S elements")
     recall = torch.empty((B, heads, n), dtype=torch.float32, device=q.device)
     dev = _require_gpu(q, k, recall, workspace)
     with torch.cuda.device(dev):
@@ -597,9 +601,11 @@ def sta_window_recall_fp8(q8: torch.Tensor, k8: torch.Tensor, tile: Sequence[int
         scale = 1.0 / math.sqrt(d)
     S = T * H * W if order == STA_RASTER else tile_major_rows((T, H, W), tile)
     if workspace is None:
-        workspace = torch.empty((2, B, heads, S), dtype=torch.float32, device=q8.device)
-    elif workspace.numel() < 2 * B * heads * S or workspace.dtype != torch.float32 or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous float32 tensor of at least 2*B*heads*S elements")
+        workspace = torch.empty((n + 1, B, heads, S), dtype=torch.float32, device=q8.device)
+    elif (workspace.numel() < (n + 1) * B * heads * S or workspace.dtype != torch.float32
+          or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous float32 tensor of at least "
+                         "(n_candidates+1)*B*heads*S elements")
     recall = torch.empty((B, heads, n), dtype=torch.float32, device=q8.device)
     dev = _require_gpu(q8, k8, recall, workspace)
     with torch.cuda.device(dev):

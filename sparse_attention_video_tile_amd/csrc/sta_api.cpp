@@ -256,7 +256,7 @@ int forward_common(const void* q, const void* k, const void* v, void* out, float
 
 extern "C" {
 
-int sta_abi_version(void) { return 6; }
+int sta_abi_version(void) { return 7; }
 
 const char* sta_last_error(void) { return g_last_error.c_str(); }
 
@@ -329,6 +329,7 @@ int forward_common(const void* q, const void* k, const void* v, void* out, float
   p.raster = raster;
   p.lse_only = false;
   p.qk_fp8 = qk_fp8;
+  p.n_cand = 0;
   int rc = check_volume(T, H, W, tile, &p.g);
   if (rc) return rc;
   if ((rc = check_windows(p.g, heads, window, p.omega))) return rc;
@@ -377,6 +378,7 @@ int backward_common(const void* q, const void* k, const void* v, const void* out
   p.raster = order == STA_RASTER;
   p.lse_only = false;
   p.qk_fp8 = false;
+  p.n_cand = 0;
   if ((rc = check_volume(T, H, W, tile, &p.g))) return rc;
   if ((rc = check_windows(p.g, heads, window, p.omega))) return rc;
   if ((rc = check_f32_padding(p.g, dtype))) return rc;
@@ -545,24 +547,60 @@ int recall_common(const void* q, const void* k, float* recall, float* workspace,
   const long long BH = (long long)B * heads;
   if (BH > (1LL << 24)) return fail(STA_ERR_INVALID_ARG, "B*heads=%lld is too large", BH);
   const size_t tb = (size_t)BH * win.g.S * head_dim * (qk_fp8 ? 1 : es);
-  const size_t wb = 2 * (size_t)BH * win.g.S * sizeof(float);
+  const size_t wb = (size_t)(n_candidates + 1) * BH * win.g.S * sizeof(float);
   const size_t rb = (size_t)BH * n_candidates * sizeof(float);
   if (overlaps(workspace, wb, q, tb) || overlaps(workspace, wb, k, tb) ||
       overlaps(recall, rb, q, tb) || overlaps(recall, rb, k, tb) || overlaps(recall, rb, workspace, wb))
     return fail(STA_ERR_INVALID_ARG, "recall or workspace overlaps an input or each other");
   float* lse_full = workspace;
-  float* lse_win = workspace + (size_t)BH * win.g.S;
+  const size_t slot = (size_t)BH * win.g.S;
+  // One pass when the kernels allow it: STA with the whole volume as every
+  // head's window (full attention) that also sums, per candidate, the
+  // probabilities of the keys the candidate's window holds.
+  if (n_candidates <= sta::kMaxRecallCand && !win.g.padded) {
+    static thread_local sta::AttnProblem one;
+    one.q = q; one.k = k; one.v = k; one.out = nullptr; one.lse = lse_full;
+    one.B = B; one.heads = heads; one.head_dim = head_dim; one.dtype = dtype; one.scale = scale;
+    one.dense = false; one.raster = order == STA_RASTER; one.lse_only = true; one.qk_fp8 = qk_fp8;
+    one.g = win.g;
+    for (int h = 0; h < heads; ++h) {
+      one.omega[h][0] = (uint16_t)win.g.nt;
+      one.omega[h][1] = (uint16_t)win.g.nh;
+      one.omega[h][2] = (uint16_t)win.g.nw;
+    }
+    one.n_cand = n_candidates;
+    one.lse_cand = workspace + slot;
+    one.cand_stride = (long long)slot;
+    for (int c = 0; c < n_candidates; ++c) {
+      one.cand_omega[c][0] = (uint16_t)(candidates[3 * c] / win.g.ct);
+      one.cand_omega[c][1] = (uint16_t)(candidates[3 * c + 1] / win.g.ch);
+      one.cand_omega[c][2] = (uint16_t)(candidates[3 * c + 2] / win.g.cw);
+    }
+    rc = sta::launch_attention(one, stream);
+    if (rc > 0) return launched(rc);
+    if (rc == 0) {
+      for (int c = 0; c < n_candidates; ++c) {
+        rc = sta::launch_recall_reduce(lse_full, workspace + (c + 1) * slot, recall, (int)BH, win.g.S,
+                                       n_candidates, c, stream);
+        if (rc) return launched(rc);
+      }
+      return ok();
+    }
+    // no one-pass kernel for this problem: one pass per candidate below
+  }
   // full-attention lse (token order does not matter for all-keys attention)
   dense.q = q; dense.k = k; dense.v = k; dense.out = nullptr; dense.lse = lse_full;
   dense.B = B; dense.heads = heads; dense.head_dim = head_dim; dense.dtype = dtype; dense.scale = scale;
   dense.dense = true; dense.raster = false; dense.lse_only = true; dense.qk_fp8 = qk_fp8;
+  dense.n_cand = 0;
   memset(&dense.g, 0, sizeof(dense.g));
   dense.g.S = win.g.S;
   rc = sta::launch_attention(dense, stream);
   if (rc) return rc < 0 ? fail(rc, "no kernel for dtype %d with head_dim %d", dtype, head_dim) : launched(rc);
-  win.q = q; win.k = k; win.v = k; win.out = nullptr; win.lse = lse_win;
+  win.q = q; win.k = k; win.v = k; win.out = nullptr;
   win.B = B; win.heads = heads; win.head_dim = head_dim; win.dtype = dtype; win.scale = scale;
   win.dense = false; win.raster = order == STA_RASTER; win.lse_only = true; win.qk_fp8 = qk_fp8;
+  win.n_cand = 0;
   for (int c = 0; c < n_candidates; ++c) {
     for (int h = 0; h < heads; ++h) {
       win.omega[h][0] = (uint16_t)(candidates[3 * c] / win.g.ct);
@@ -570,9 +608,10 @@ int recall_common(const void* q, const void* k, float* recall, float* workspace,
       win.omega[h][2] = (uint16_t)(candidates[3 * c + 2] / win.g.cw);
     }
     if (win.raster && (rc = check_raster_runs(win.g, heads, win.omega, false))) return rc;
+    win.lse = workspace + (c + 1) * slot;   // candidate c's row lse
     rc = sta::launch_attention(win, stream);
     if (rc) return rc < 0 ? fail(rc, "no kernel for dtype %d with head_dim %d", dtype, head_dim) : launched(rc);
-    rc = sta::launch_recall_reduce(lse_full, lse_win, recall, (int)BH, win.g.S, n_candidates, c, stream);
+    rc = sta::launch_recall_reduce(lse_full, win.lse, recall, (int)BH, win.g.S, n_candidates, c, stream);
     if (rc) return launched(rc);
   }
   return ok();
@@ -613,6 +652,7 @@ int sta_full_attention(const void* q, const void* k, const void* v, void* out, i
   p.raster = false;
   p.lse_only = false;
   p.qk_fp8 = false;
+  p.n_cand = 0;
   p.lse = nullptr;
   p.q = q; p.k = k; p.v = v; p.out = out;
   p.B = B; p.heads = heads; p.head_dim = head_dim; p.dtype = dtype; p.scale = scale;

@@ -436,19 +436,29 @@ __device__ __forceinline__ void store_out(WaveState<C, RB>& w, bf16_t* og, float
 // masked path (two paths in one kernel would not fit the register file).
 // QK8: q and k are fp8 e4m3 (their scales folded into p.scale_log2).
 template <int D, int WAVES, int RB, int BN, bool DENSE, bool RASTER, bool LSE_ONLY = false,
-          bool PAD = false, bool PLANE = false, bool FULL = false, bool QK8 = false>
-__global__ void __launch_bounds__(WAVES * 64, (WAVES <= 4 ? 2 : 1))
+          bool PAD = false, bool PLANE = false, bool FULL = false, bool QK8 = false,
+          bool RECALL = false>
+// (Second bound: waves per SIMD the registers must allow. The one-pass recall
+// kernels keep to 128 registers so that two 8-wave workgroups share a CU, as
+// the other log-sum-exp-only kernels do by themselves.)
+__global__ void __launch_bounds__(WAVES * 64, (RECALL ? 4 : WAVES <= 4 ? 2 : 1))
 attn_bf16_kernel(const AttnParams p) {
+  // RECALL: the log-sum-exp-only pass over the whole volume that also sums,
+  // for each candidate window, the probabilities of the keys it holds (whole
+  // 64-key chunks of one key tile each, so membership is per chunk).
+  static_assert(!RECALL || (LSE_ONLY && FULL && !DENSE && BN == 64 && (!RASTER || PLANE)),
+                "one-pass recall: whole chunks, no raster offset table");
   using C = Bf16Cfg<D, WAVES, RB, BN, QK8>;
   using KG = typename C::KGeom;
   // K and V buffers of two chunks. They are separate objects and the loop
   // selects them statically, so the compiler can tell the chunk being read
   // apart from the one the LDS DMA is filling and does not wait for the
   // prefetch before reading.
+  // (Log-sum-exp only: no V, so no V buffers; more workgroups fit a CU.)
   __shared__ __attribute__((aligned(1024))) char kb0[KG::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char vb0[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char vb0[LSE_ONLY ? 16 : C::kChunkBytes];
   __shared__ __attribute__((aligned(1024))) char kb1[KG::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char vb1[C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char vb1[LSE_ONLY ? 16 : C::kChunkBytes];
   // Raster offsets of one window run (RASTER only), sized at launch.
   extern __shared__ int rtab[];
 
@@ -477,6 +487,53 @@ attn_bf16_kernel(const AttnParams p) {
     for (int e = threadIdx.x; e < walk.run_len; e += C::kThreads) rtab[e] = run_offset_raster(p, e);
     __syncthreads();
   }
+  // RECALL: bit c of cand_tab[it] says whether candidate window c of this
+  // work item's query tile holds the key tile of chunk it (the table lives in
+  // dynamic LDS, which these kernels use for nothing else; the first chunk's
+  // barrier publishes it). lc_c: each candidate's probability sums, per lane
+  // like w.lsum and against the same reference max.
+  unsigned char* cand_tab = reinterpret_cast<unsigned char*>(rtab);
+  float lc_c[kMaxRecallCand][RB];
+  if constexpr (RECALL) {
+#pragma unroll
+    for (int c = 0; c < kMaxRecallCand; ++c)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) lc_c[c][rb] = 0.f;
+    // Per axis first: bit c of axis_tab[off_a + i] says whether candidate c's
+    // window (clamped around this item's query tile) holds tile i along axis
+    // a; one thread per (axis, tile). Then one entry per chunk, the AND of
+    // its key tile's three axis masks.
+    unsigned char* axis_tab = cand_tab + ((p.cand_chunks + 3) & ~3);
+    const int na = p.nt + p.nh + p.nw;
+    for (int e = threadIdx.x; e < na; e += C::kThreads) {
+      const int a = e < p.nt ? 0 : e < p.nt + p.nh ? 1 : 2;
+      const int i = e - (a == 0 ? 0 : a == 1 ? p.nt : p.nt + p.nh);
+      const int n = a == 0 ? p.nt : a == 1 ? p.nh : p.nw;
+      const int q = a == 0 ? t.qt : a == 1 ? t.qh : t.qw;
+      unsigned m = 0;
+      for (int c = 0; c < p.n_cand; ++c) {
+        const int om = p.cand_omega[c][a];
+        m |= ((unsigned)(i - window_start(q, n, om)) < (unsigned)om ? 1u : 0u) << c;
+      }
+      axis_tab[e] = static_cast<unsigned char>(m);
+    }
+    __syncthreads();
+    const int cpt = p.tau / BN;   // chunks per key tile
+    for (int e = threadIdx.x; e < walk.n_chunks && e < p.cand_chunks; e += C::kThreads) {
+      const int run = e / walk.chunks_per_run, j = e - run * walk.chunks_per_run;
+      const int kt = t.kv.st + run / t.kv.oh, kh = t.kv.sh + run % t.kv.oh;
+      const int kw = t.kv.sw + j / cpt;
+      cand_tab[e] = axis_tab[kt] & axis_tab[p.nt + kh] & axis_tab[p.nt + p.nh + kw];
+    }
+  }
+  auto recall_add = [&](unsigned cm, const float (&x)[RB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < kMaxRecallCand; ++c)
+      if ((cm >> c) & 1u) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) lc_c[c][rb] += x[rb];
+      }
+  };
   auto dma = [&](int it, char* kdst, char* vdst) __attribute__((always_inline)) {
     if constexpr (plane) {
       const int row0 = walk.at_plane(p, it);
@@ -528,6 +585,13 @@ attn_bf16_kernel(const AttnParams p) {
     const unsigned long long real = chunk_real_keys<PAD && !DENSE>(p, walk, it, lane);
     wait_vm_all();     // this wave's loads of chunk `it` have landed in LDS
     __syncthreads();   // ... and every wave's; chunk it-1's buffers are free
+    // RECALL: the chunk's candidate bits, read here so that the wait for them
+    // does not fall among the operand reads of the MFMA phases
+    unsigned cm = 0;
+    if constexpr (RECALL) {
+      cm = it < p.cand_chunks ? __builtin_amdgcn_readfirstlane(cand_tab[it]) : 0u;
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (!decltype(first)::value) {
       // Every chunk after the first: the probabilities of score tile kt go
       // out between the QK^T MFMAs of tile kt + 1, and one sum test per chunk
@@ -584,7 +648,18 @@ attn_bf16_kernel(const AttnParams p) {
             a = fmaxf(a, fmaxf(fmaxf(w.s[rb][kt][0], w.s[rb][kt][1]), fmaxf(w.s[rb][kt][2], w.s[rb][kt][3])));
           mx[rb] = a * p.scale_log2;
         }
+        float m_old[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) m_old[rb] = w.m[rb];
         rescale_to<C, RB>(w, mx);
+        if constexpr (RECALL) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const float a = __builtin_amdgcn_exp2f(m_old[rb] - w.m[rb]);
+#pragma unroll
+            for (int c = 0; c < kMaxRecallCand; ++c) lc_c[c][rb] *= a;
+          }
+        }
         if constexpr (LSE_ONLY) {
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) lc[rb] = 0.f;
@@ -598,6 +673,7 @@ attn_bf16_kernel(const AttnParams p) {
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) w.lsum[rb] += lc[rb];
+      if constexpr (RECALL) recall_add(cm, lc);
       if constexpr (!LSE_ONLY) {
         pv_chunk<C, RB>(w, vcur, l16, g);
         sched_reads_ahead<RB, C::kKP * C::kDB, 2, kReadAhead>();
@@ -612,6 +688,13 @@ attn_bf16_kernel(const AttnParams p) {
       // (measured: 2 % faster than issuing right after the barrier).
       if (!kSingleBuffer && it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
       softmax_chunk<C, RB, LSE_ONLY>(w, nvalid, real, p.scale_log2, g);
+      if constexpr (RECALL) {
+        // the work item's first chunk: the row sums were 0 before it
+        float x[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) x[rb] = w.lsum[rb];
+        recall_add(cm, x);
+      }
       // No fence before PV: the scheduler starts the PV MFMAs of the first
       // row block while the exponentials of the others are still being
       // issued (the same wave issuing both is what lets them run side by side).
@@ -635,8 +718,21 @@ attn_bf16_kernel(const AttnParams p) {
     if (it + 1 < walk.n_chunks) chunk_step(FirstChunk<false>{}, kb0, vb0, kb1, vb1, it + 1);
   }
   // The row map is built again rather than kept in registers across the loop.
-  store_out<C, RB>(w, LSE_ONLY ? nullptr : og, p.lse ? p.lse + t.head_base / D : nullptr,
-                   map_rows<C, RB, RASTER>(p, t, wave, l16), g);
+  const RowMap<C, RB> rm_out = map_rows<C, RB, RASTER>(p, t, wave, l16);
+  store_out<C, RB>(w, LSE_ONLY ? nullptr : og, p.lse ? p.lse + t.head_base / D : nullptr, rm_out, g);
+  if constexpr (RECALL) {
+    // each candidate's row log-sum-exp: ln 2 * (m + log2 of its row sum)
+#pragma unroll
+    for (int c = 0; c < kMaxRecallCand; ++c) {
+      if (c >= p.n_cand) break;   // uniform
+      float* dst = p.lse_cand + c * p.cand_stride + t.head_base / D;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float l = row_sum4(lc_c[c][rb]);
+        if (rm_out.ok[rb] && g == 0) dst[rm_out.tok[rb]] = (w.m[rb] + __log2f(l)) * kLn2;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -748,6 +844,31 @@ unsigned raster_table_bytes(const AttnProblem& pr) {
 }
 
 // FULL implies !PAD; plane chunks imply FULL (whole 64-key chunks per tile).
+// One-pass window recall (lse_only with candidate windows): whole-chunk
+// kernels that address K by arithmetic (tile-major, or raster plane chunks);
+// the per-chunk candidate table takes cand_chunks bytes of dynamic LDS.
+// Returns false when no such kernel fits the problem.
+template <int D, int WAVES, int RB, int BN, bool FULL, bool QK8>
+bool launch_recall_pass(const AttnProblem& pr, const AttnParams& p, unsigned grid, hipStream_t stream) {
+  using C = Bf16Cfg<D, WAVES, RB, BN>;
+  if constexpr (!FULL || BN != 64 || Bf16Cfg<D, WAVES, RB, BN>::kRows != kRecallRows) {
+    return false;   // only the recall shape (dispatch_bf16) has these kernels
+  } else {
+    const bool plane = p.plane_cpt > 0;
+    // the per-chunk table, then the per-axis masks it is built from
+    const unsigned tab = (unsigned)(((p.cand_chunks + 3) & ~3) + p.nt + p.nh + p.nw);
+    if (pr.raster && plane)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, true, true, false, true, true, QK8, true>),
+                         dim3(grid), dim3(C::kThreads), tab, stream, p);
+    else if (!pr.raster)
+      hipLaunchKernelGGL((attn_bf16_kernel<D, WAVES, RB, BN, false, false, true, false, false, true, QK8, true>),
+                         dim3(grid), dim3(C::kThreads), tab, stream, p);
+    else
+      return false;
+    return true;
+  }
+}
+
 template <int D, int WAVES, int RB, int BN, bool PAD, bool FULL, bool QK8>
 void launch_sparse(const AttnProblem& pr, const AttnParams& p, unsigned grid, unsigned table,
                    hipStream_t stream) {
@@ -821,6 +942,12 @@ int launch_bf16_planned(const AttnProblem& pr, const AttnParams& p, unsigned gri
   // plane chunks address K/V by arithmetic and need no offset table
   const bool full = chunks_full(pr, BN);
   const unsigned table = (full && BN == 64 && p.plane_cpt > 0) ? 0 : raster_table_bytes(pr);
+  if (p.n_cand > 0) {
+    if (!pr.lse_only || pr.dense) return STA_ERR_UNSUPPORTED;
+    const bool ok = full && !pr.g.padded && p.cand_chunks <= kMaxRecallTable &&
+                    (full ? launch_recall_pass<D, WAVES, RB, BN, true, QK8>(pr, p, grid, stream) : false);
+    return ok ? (int)hipGetLastError() : STA_ERR_UNSUPPORTED;
+  }
   if constexpr (QK8) {
     if (pr.dense && !pr.lse_only) return STA_ERR_UNSUPPORTED;
     if (pr.dense) {   // the full-attention pass of window recall on fp8 q and k
@@ -906,6 +1033,12 @@ template <int D, bool QK8 = false>
 int dispatch_bf16(const AttnProblem& pr, hipStream_t stream) {
   const int rows = fwd_bf16_rows(pr.dense ? pr.g.S : pr.g.tau);
   static_assert(Bf16Cfg<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN>::kRows == kFwdBigRows, "shape");
+  // One-pass window recall: 4-wave items of 128 rows, which keep the
+  // candidate sums within 128 registers (four workgroups a CU).
+  if (pr.n_cand > 0) {
+    static_assert(Bf16Cfg<D, 4, 2, 64>::kRows == kRecallRows, "recall shape");
+    return launch_bf16<D, 4, 2, 64, QK8>(pr, stream);
+  }
   if (rows == kFwdBigRows) {
     // The last, partly filled round of whole-tile items runs as 64-row items
     // in a second launch when that spreads it over the XCD (plan_tail_split).
@@ -928,6 +1061,8 @@ int dispatch_bf16(const AttnProblem& pr, hipStream_t stream) {
 
 int launch_attention(const AttnProblem& pr, void* stream_ptr) {
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  // one-pass window recall exists for the bf16 (and fp8 q/k) kernels only
+  if (pr.n_cand > 0 && (pr.dtype != STA_BF16 || pr.dense || !pr.lse_only)) return STA_ERR_UNSUPPORTED;
   const long long units = pr.dense ? 1 : pr.g.n_tiles;
   const long long tasks_upper = (long long)pr.B * pr.heads * units * (pr.dense ? pr.g.S : pr.g.tau);
   if (tasks_upper > (1LL << 31) - 1) return (int)hipErrorInvalidValue;

@@ -15,6 +15,12 @@ namespace sta {
 // (the run's table of raster offsets is kept in LDS).
 constexpr int kMaxRasterRun = 8192;
 
+// Candidate windows one window-recall pass scores at once, and the largest
+// per-chunk candidate table (bytes of dynamic LDS, one per 64-key chunk of
+// the whole volume) it keeps.
+constexpr int kMaxRecallCand = 8;
+constexpr int kMaxRecallTable = 65536;
+
 struct AttnProblem {
   const void* q;
   const void* k;
@@ -31,6 +37,14 @@ struct AttnProblem {
   Geometry g;      // for dense problems only g.S is used
   // Window per head in tiles (sparse problems only).
   uint16_t omega[STA_MAX_HEADS][3];
+  // Window recall in one pass (lse_only, the whole volume as every head's
+  // window): the log-sum-exp of each query row over the keys of candidate
+  // window c (in tiles) goes to lse_cand + c * cand_stride, in lse's layout.
+  // n_cand = 0 otherwise.
+  int n_cand;
+  float* lse_cand;
+  long long cand_stride;
+  uint16_t cand_omega[kMaxRecallCand][3];
 };
 
 int launch_reorder(const void* src, void* dst, int BH, int row_bytes, const Geometry& g,

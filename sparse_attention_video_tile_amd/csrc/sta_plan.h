@@ -54,6 +54,13 @@ struct AttnParams {
   int plane_cpt, plane_cpp;
   uint16_t omega[STA_MAX_HEADS][3];
   uint8_t head_order[STA_MAX_HEADS];  // logical head slot -> head (heaviest windows first)
+  // Window recall in one pass (see AttnProblem); cand_chunks: entries of the
+  // per-chunk candidate table in dynamic LDS (the walk's chunk count).
+  int n_cand;
+  int cand_chunks;
+  float* lse_cand;
+  long long cand_stride;
+  uint16_t cand_omega[kMaxRecallCand][3];
 };
 
 // Host side: order the work and size the grid. With equal windows on every
@@ -302,6 +309,11 @@ STA_HD ChunkWalk make_walk(const Task& t, int S) {
 inline void fill_params(const AttnProblem& pr, int rows_per_item, AttnParams* p) {
   p->q = pr.q; p->k = pr.k; p->v = pr.v; p->out = pr.out;
   p->lse = pr.lse;
+  p->n_cand = pr.dense ? 0 : pr.n_cand;
+  p->lse_cand = pr.lse_cand;
+  p->cand_stride = pr.cand_stride;
+  for (int c = 0; c < kMaxRecallCand; ++c)
+    for (int a = 0; a < 3; ++a) p->cand_omega[c][a] = c < p->n_cand ? pr.cand_omega[c][a] : 0;
   // rows per (batch, head) of the tensors: tile-major tensors of a padded
   // tile grid hold n_tiles * tau rows
   p->S = pr.dense || pr.raster ? pr.g.S : pr.g.S_pad;
@@ -329,6 +341,8 @@ inline void fill_params(const AttnProblem& pr, int rows_per_item, AttnParams* p)
       for (int a = 0; a < 3; ++a) p->omega[h][a] = pr.omega[h][a];
   }
   p->row_blocks = (p->unit_rows + rows_per_item - 1) / rows_per_item;
+  // one entry per 64-key chunk of the whole-volume walk
+  p->cand_chunks = p->n_cand ? (int)((long long)p->n_units * ((p->tau + 63) / 64)) : 0;
   const long long tasks = (long long)pr.B * pr.heads * p->n_units * p->row_blocks;
   plan_tasks(p, tasks, pr.heads, pr.dense);
 }
@@ -350,6 +364,10 @@ inline void fill_bwd_params(const BwdProblem& pr, int rows_per_item, AttnParams*
   const AttnProblem& a = pr.attn;
   p->q = a.q; p->k = a.k; p->v = a.v; p->out = a.out;
   p->lse = nullptr;
+  p->n_cand = 0;
+  p->cand_chunks = 0;
+  p->lse_cand = nullptr;
+  p->cand_stride = 0;
   p->S = a.raster ? a.g.S : a.g.S_pad;
   p->heads = a.heads;
   p->dense = 0;
@@ -388,6 +406,8 @@ inline void fill_bwd_params(const BwdProblem& pr, int rows_per_item, AttnParams*
 constexpr int kFwdBigRows = STA_CFG_WAVES * 16 * STA_CFG_RB;
 // Rows of the items a split last round runs as (4 waves of 16 rows).
 constexpr int kFwdTailRows = 64;
+// Rows of the items of a one-pass window recall (4 waves of 32 rows).
+constexpr int kRecallRows = 128;
 // bf16 forward: the big shape when a unit is whole blocks of it, else 4 waves
 // of 16 rows (units of at most 64 rows) or of 32 rows.
 inline int fwd_bf16_rows(int unit_rows) {

@@ -39,6 +39,7 @@ struct Ctx {
   long long checks = 0;
   long long launches = 0;
   long long tail_launches = 0;   // forward launches whose last round ran as 64-row items
+  long long recall_passes = 0;   // one-pass window recall launches
 } g_ctx;
 
 #define CHECK_ROW(row_, rows_, msg_)                                                         \
@@ -164,6 +165,12 @@ void model_bf16_launch(const sta::AttnProblem& pr, const AttnParams& p, long lon
     check_head(p, t, D, total_rows);
     model_own_rows<ROWS>(p, t, pr.raster && !pr.dense, p.S, "query");
     const ChunkWalk w = pr.dense ? sta::make_walk<64, true>(t, p.S) : sta::make_walk<64, false>(t, p.S);
+    if (p.n_cand > 0) {
+      // every chunk of the whole-volume walk has an entry in the candidate
+      // table, and the candidate windows' rows are written like lse's
+      CHECK(w.n_chunks <= p.cand_chunks, "candidate table covers the walk");
+      CHECK(p.cand_stride >= total_rows, "each candidate's rows have a slot of their own");
+    }
     for (int it = 0; it < w.n_chunks; ++it)
       model_chunk(p, w, it, pr.raster && !pr.dense, plane, p.pad, p.S, k_row_bytes, table_len, "key");
   }
@@ -314,6 +321,21 @@ int launch_kv_tiles(int*, int*, int heads, const Geometry& g, const uint16_t (*o
 int launch_attention(const AttnProblem& pr, void*) {
   if (pr.qk_fp8 && !(pr.dtype == STA_BF16 && pr.head_dim == 128)) return STA_ERR_UNSUPPORTED;
   if (pr.head_dim != 64 && pr.head_dim != 128) return STA_ERR_UNSUPPORTED;
+  if (pr.n_cand > 0) {
+    // one-pass window recall: the launcher's rules (bf16 log-sum-exp only,
+    // whole 64-key chunks, tile-major or plane chunks, a table that fits)
+    if (pr.dtype != STA_BF16 || pr.dense || !pr.lse_only) return STA_ERR_UNSUPPORTED;
+    AttnParams p;
+    sta::fill_params(pr, 64, &p);
+    bool full = !pr.g.padded;
+    for (int h = 0; h < pr.heads; ++h) full = full && (pr.omega[h][2] * pr.g.tau) % 64 == 0;
+    if (!full || (pr.raster && p.plane_cpt == 0) || p.cand_chunks > sta::kMaxRecallTable)
+      return STA_ERR_UNSUPPORTED;
+    CHECK(pr.n_cand <= sta::kMaxRecallCand, "candidates fit the kernel");
+    ++g_ctx.recall_passes;
+    model_bf16_forward<sta::kRecallRows>(pr);
+    return 0;
+  }
   if (pr.dtype == STA_F32) {
     CHECK(!(pr.g.padded && !pr.dense), "float32 attention never reaches a padded grid");
     if (pr.head_dim == 64) model_f32_forward<64>(pr); else model_f32_forward<128>(pr);
@@ -524,7 +546,8 @@ int main() {
              raster ? "raster" : "tile-major", outside, p.S, worst, pr.g.S_pad);
     }
   }
-  printf("host model: %lld launches modelled (%lld forwards with a split last round), %lld checks, all in bounds\n",
-         g_ctx.launches, g_ctx.tail_launches, g_ctx.checks);
+  printf("host model: %lld launches modelled (%lld forwards with a split last round, %lld one-pass "
+         "recalls), %lld checks, all in bounds\n",
+         g_ctx.launches, g_ctx.tail_launches, g_ctx.recall_passes, g_ctx.checks);
   return 0;
 }

@@ -310,6 +310,11 @@ def test_window_recall_rejects_bad_arguments(lib):
     assert call(d=32) == -2
     assert call(ws=FAKE * 2000 + 64) == -1                              # workspace overlaps k
     assert "overlap" in binding.last_error()
+    # the workspace holds n_candidates + 1 slots of B * heads * S floats: two
+    # slots that end where k starts leave the third overlapping k
+    slot = 1 * 2 * 30 * 48 * 80 * 4
+    assert call(ws=FAKE * 2000 - 2 * slot) == -1
+    assert "overlap" in binding.last_error()
 
 
 def test_float32_attention_on_a_padded_grid_is_refused(lib):

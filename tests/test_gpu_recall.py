@@ -40,7 +40,7 @@ def test_recall_matches_oracle(case, order):
     q, k = to_gpu(inp.q, dtype), to_gpu(inp.k, dtype)
     scale = default_scale(d)
     S = int(np.prod(volume))
-    ws = torch.empty((2, w.B, heads, S), dtype=torch.float32, device="cuda")
+    ws = torch.empty((len(cands) + 1, w.B, heads, S), dtype=torch.float32, device="cuda")
     if order == "raster":
         got = binding.sta_window_recall(q, k, tile, cands, scale, workspace=ws)
     else:
@@ -51,9 +51,9 @@ def test_recall_matches_oracle(case, order):
     err = np.abs(got.cpu().numpy().astype(np.float64) - ref).max()
     print(f"[parity] {name} {order} recall max_abs {err:.3e} ref {ref.ravel()[:4]}", flush=True)
     assert err <= RECALL_MAX_ABS
-    # The workspace keeps the two row log-sum-exps of the last pass: all keys,
-    # and the last candidate window. Each row against the oracle.
-    lse_ref = [oracle.sta_lse(inp.q, inp.k, tile, [win] * heads, scale) for win in (volume, cands[-1])]
+    # The workspace keeps the row log-sum-exps over all keys (slot 0) and over
+    # each candidate window (slot c + 1). Each row against the oracle.
+    lse_ref = [oracle.sta_lse(inp.q, inp.k, tile, [win] * heads, scale) for win in [volume] + cands]
     for slot, r in enumerate(lse_ref):
         r = r[..., None]
         if order == "tile_major":

@@ -38,8 +38,10 @@ def test_host_model_under_sanitizers(tmp_path):
     assert "all in bounds" in run.stdout
     # the 30x48x80 workloads' 7200 whole-tile items leave a partly filled last
     # round, which the launcher runs as 64-row items: that path is modelled
-    tails = re.search(r"\((\d+) forwards with a split last round\)", run.stdout)
+    tails = re.search(r"\((\d+) forwards with a split last round, (\d+) one-pass recalls\)", run.stdout)
     assert tails and int(tails.group(1)) > 0, run.stdout[-500:]
+    # window recall runs as one pass wherever the kernels allow: modelled too
+    assert int(tails.group(2)) > 0, run.stdout[-500:]
     # the float32 kernels' unpadded row mapping leaves a raster slice on a
     # padded grid (which is why the library refuses that case)
     assert "raster order: 324 query rows map past the 210 rows" in run.stdout
