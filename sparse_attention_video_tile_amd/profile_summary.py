@@ -93,7 +93,7 @@ def role(name: str) -> str:
         return "STA backward, D = rowsum(dO * O)"
     if "attn_bf16_kernel" in name:
         a = _targs(name)
-        # <D, WAVES, RB, BN, DENSE, RASTER, LSE_ONLY, PAD, PLANE, FULL, QK8>
+        # <D, WAVES, RB, BN, DENSE, RASTER, LSE_ONLY, PAD, PLANE, FULL, QK8, RECALL>
         dense, raster = a[4] == "true", a[5] == "true"
         lse_only = len(a) > 6 and a[6] == "true"
         pad = len(a) > 7 and a[7] == "true"
@@ -107,6 +107,8 @@ def role(name: str) -> str:
             what += ", padded grid"
         if qk8:
             what += ", fp8 q and k"
+        if len(a) > 11 and a[11] == "true":
+            what += ", one pass over all candidate windows"
         if small:
             what += ", 64-row items"
         return what
