@@ -321,10 +321,10 @@ int sta_backward_noalloc(const void* q, const void* k, const void* v, const void
  * output; with bf16 inputs this mode sums the probabilities in float32
  * without rounding them to bfloat16, as nothing multiplies them), then a
  * deterministic double-precision reduction per (b, h). With bf16 (or fp8)
- * inputs, whole 64-key chunks per tile, no padding and at most 8 candidates,
- * one pass over all keys (the whole volume as the window) also sums each
- * candidate window's share, since every chunk lies in one key tile; else a
- * full-attention pass and one pass per candidate.
+ * inputs, whole 64-key chunks per tile and no padding, one pass over all
+ * keys (the whole volume as the window) per group of up to 8 candidates also
+ * sums each candidate window's share, since every chunk lies in one key
+ * tile; else a full-attention pass and one pass per candidate.
  *   q, k:        device [B][heads][S][head_dim], token order `order`, read.
  *   recall:      device float [B][heads][n_candidates], written.
  *   workspace:   device float [n_candidates + 1][B][heads][S], caller-owned;

@@ -554,10 +554,11 @@ int recall_common(const void* q, const void* k, float* recall, float* workspace,
     return fail(STA_ERR_INVALID_ARG, "recall or workspace overlaps an input or each other");
   float* lse_full = workspace;
   const size_t slot = (size_t)BH * win.g.S;
-  // One pass when the kernels allow it: STA with the whole volume as every
-  // head's window (full attention) that also sums, per candidate, the
-  // probabilities of the keys the candidate's window holds.
-  if (n_candidates <= sta::kMaxRecallCand && !win.g.padded) {
+  // One pass per group of up to kMaxRecallCand candidates when the kernels
+  // allow it: STA with the whole volume as every head's window (full
+  // attention) that also sums, per candidate, the probabilities of the keys
+  // the candidate's window holds. Every pass writes the same full lse.
+  if (!win.g.padded) {
     static thread_local sta::AttnProblem one;
     one.q = q; one.k = k; one.v = k; one.out = nullptr; one.lse = lse_full;
     one.B = B; one.heads = heads; one.head_dim = head_dim; one.dtype = dtype; one.scale = scale;
@@ -568,17 +569,21 @@ int recall_common(const void* q, const void* k, float* recall, float* workspace,
       one.omega[h][1] = (uint16_t)win.g.nh;
       one.omega[h][2] = (uint16_t)win.g.nw;
     }
-    one.n_cand = n_candidates;
-    one.lse_cand = workspace + slot;
     one.cand_stride = (long long)slot;
-    for (int c = 0; c < n_candidates; ++c) {
-      one.cand_omega[c][0] = (uint16_t)(candidates[3 * c] / win.g.ct);
-      one.cand_omega[c][1] = (uint16_t)(candidates[3 * c + 1] / win.g.ch);
-      one.cand_omega[c][2] = (uint16_t)(candidates[3 * c + 2] / win.g.cw);
+    bool done = true;
+    for (int c0 = 0; c0 < n_candidates && done; c0 += sta::kMaxRecallCand) {
+      one.n_cand = n_candidates - c0 < sta::kMaxRecallCand ? n_candidates - c0 : sta::kMaxRecallCand;
+      one.lse_cand = workspace + (c0 + 1) * slot;
+      for (int c = 0; c < one.n_cand; ++c) {
+        one.cand_omega[c][0] = (uint16_t)(candidates[3 * (c0 + c)] / win.g.ct);
+        one.cand_omega[c][1] = (uint16_t)(candidates[3 * (c0 + c) + 1] / win.g.ch);
+        one.cand_omega[c][2] = (uint16_t)(candidates[3 * (c0 + c) + 2] / win.g.cw);
+      }
+      rc = sta::launch_attention(one, stream);
+      if (rc > 0) return launched(rc);
+      done = rc == 0;   // no one-pass kernel for this problem: the first group falls back
     }
-    rc = sta::launch_attention(one, stream);
-    if (rc > 0) return launched(rc);
-    if (rc == 0) {
+    if (done) {
       for (int c = 0; c < n_candidates; ++c) {
         rc = sta::launch_recall_reduce(lse_full, workspace + (c + 1) * slot, recall, (int)BH, win.g.S,
                                        n_candidates, c, stream);

@@ -23,6 +23,9 @@ RECALL_FULL_SIZE_ABS = 2.5e-4
 
 CASES = [
     ("tiles_6x8x8", (12, 16, 24), (6, 8, 8), [(6, 8, 8), (6, 16, 8), (12, 16, 24)], 2, 128, "bf16"),
+    # more candidates than one pass takes: two groups
+    ("tiles_6x8x8_ten_candidates", (12, 16, 24), (6, 8, 8),
+     [(t, h, w) for t in (6, 12) for h in (8, 16) for w in (8, 16, 24)][:10], 1, 128, "bf16"),
     ("tile64_d64", (12, 16, 16), (4, 4, 4), [(4, 4, 4), (8, 8, 8), (12, 12, 12), (4, 16, 8)], 2, 64, "bf16"),
     ("tile48_ragged", (9, 8, 12), (3, 4, 4), [(3, 4, 4), (6, 4, 8)], 1, 128, "bf16"),
     ("f32_tiny", (12, 16, 16), (4, 4, 4), [(4, 4, 4), (12, 12, 12)], 2, 64, "f32"),
@@ -94,7 +97,8 @@ def test_recall_full_size_invariants():
     assert np.abs(r - rt).max() <= 1e-4
 
 
-FP8_CASES = [CASES[0], CASES[2], ("padded_tile96", (7, 12, 20), (3, 4, 8), [(3, 4, 8), (6, 8, 16)], 2, 128, "bf16")]
+FP8_CASES = [c for c in CASES if c[0] in ("tiles_6x8x8", "tile48_ragged")] + [
+    ("padded_tile96", (7, 12, 20), (3, 4, 8), [(3, 4, 8), (6, 8, 16)], 2, 128, "bf16")]
 
 
 # recall on a padded grid is defined for raster order only (the API refuses
