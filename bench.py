@@ -70,7 +70,8 @@ def gpu_inputs(w, torch):
 def recorded_traffic(workload: str, path_name: str):
     """HBM-side bytes per attention launch from the committed counter record
     (profiles/), or None when there is none for this workload and path or the
-    kernel sources have changed since the counters were taken."""
+    kernel sources' code (comments aside) has changed since the counters were
+    taken."""
     from sparse_attention_video_tile_amd.profile_summary import source_sha256
     path = os.path.join(ROOT, "profiles", f"attn_bf16_{path_name}_{workload}_traffic.json")
     if not os.path.exists(path):

@@ -7,7 +7,14 @@
 // memory the window is omega_t * omega_h runs, each run omega_w consecutive
 // tiles = omega_w * tau consecutive tokens. The kernel walks those runs in
 // chunks of BN keys, so no block is ever masked except for a ragged last chunk
-// of a run whose length is not a multiple of BN.
+// of a run whose length is not a multiple of BN, or the padding positions of
+// a volume the tile does not divide; such keys start their scores at -inf.
+//
+// Modes: log-sum-exp only (no V, no output; window recall), and one-pass
+// recall, which runs the whole volume as the window (full attention) and
+// also sums, per candidate window, the probabilities of the key tiles the
+// candidate holds. Whole-tile work items leave a partly filled last round on
+// each XCD; the host runs it as 64-row items in a second launch.
 //
 // bf16 kernel. Each wavefront owns RB blocks of 16 query rows. It computes
 // S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (K from LDS as the A operand, the

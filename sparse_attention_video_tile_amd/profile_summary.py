@@ -60,10 +60,39 @@ def pmc_cmd(counter: str) -> str:
     return f"rocprofv3 --pmc {counter} --kernel-trace -d <outdir> -o run -f csv -- python3 bench.py {PMC_ARGS}"
 
 
-def source_sha256(root: str = ROOT) -> str:
+def strip_comments(text: str) -> str:
+    """C/C++ source without its comments and blank lines, trailing spaces cut:
+    what the compiler sees, so that an edit of a comment leaves it unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    lines = (ln.rstrip() for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln) + "\n"
+
+
+def source_sha256(root: str = ROOT, read=None) -> str:
+    """Hash of the kernel sources' code (comments removed). A counter record
+    whose hash differs was taken from other kernels."""
+    read = read or (lambda f: open(os.path.join(root, f), encoding="utf-8").read())
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(root, f), "rb").read())
+        h.update(strip_comments(read(f)).encode())
     return h.hexdigest()
 
 
