@@ -255,11 +255,13 @@ __device__ __forceinline__ RowMap<C, RB> map_rows(const AttnParams& p, const Tas
 // Bit k set iff key k (0..63) of chunk `it` is a token of the volume: all
 // ones unless the problem is padded (PAD, a kernel variant of its own so that
 // unpadded launches carry no masking code) and the chunk's run reaches past
-// the volume. One key per lane (64-key chunks), then a wave ballot.
+// the volume. From the precomputed masks when tau is a multiple of 64, else
+// one key per lane (64-key chunks), then a wave ballot.
 template <bool PAD>
 __device__ __forceinline__ unsigned long long chunk_real_keys(const AttnParams& p, const ChunkWalk& w,
                                                                int it, int lane) {
   if (!PAD) return ~0ull;
+  if (p.pad_cpt > 0 && w.bn == 64) return chunk_pad_mask(p, w.kv, w.chunks_per_run, it);
   const int run = it / w.chunks_per_run;
   if (!run_padded(p, w.kv, run)) return ~0ull;
   const int e = (it - run * w.chunks_per_run) * w.bn + lane;

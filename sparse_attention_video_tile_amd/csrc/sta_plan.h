@@ -23,6 +23,10 @@ constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kXcds = 8;  // MI355X dispatches workgroups round-robin over 8 XCDs
 
 // Parameters shared by both kernels.
+// 64-key chunks per tile up to which padded grids use precomputed token masks
+// (tau <= 1024).
+constexpr int kMaxPadChunks = 16;
+
 struct AttnParams {
   const void* q;
   const void* k;
@@ -52,6 +56,14 @@ struct AttnParams {
   // one tile (64 divides c_h * c_w, c_w divides 64, tau a multiple of 64):
   // chunks per tile and per plane. 0 when that does not hold.
   int plane_cpt, plane_cpp;
+  // Padded grids with tau a multiple of 64 (each 64-key chunk inside one
+  // tile): bit k of pad_mask[a][c] says whether key 64c + k of a tile lies
+  // inside the extent of the tiles the volume's end cuts along axis a (the
+  // last tile along t, h or w). A chunk's token mask is the AND of the masks
+  // of the axes along which its key tile is cut. pad_cpt = tau / 64 then,
+  // else 0.
+  int pad_cpt;
+  unsigned long long pad_mask[3][kMaxPadChunks];
   uint16_t omega[STA_MAX_HEADS][3];
   uint8_t head_order[STA_MAX_HEADS];  // logical head slot -> head (heaviest windows first)
   // Window recall in one pass (see AttnProblem); cand_chunks: entries of the
@@ -80,6 +92,27 @@ inline void set_plane_chunks(AttnParams* p) {
   } else {
     p->plane_cpt = p->plane_cpp = 0;
   }
+}
+
+// Host side: pad_cpt / pad_mask of a sparse problem (needs the volume, the
+// tile and the tile grid).
+inline void set_pad_masks(AttnParams* p) {
+  p->pad_cpt = 0;
+  if (!p->pad || p->tau % 64 != 0 || p->tau / 64 > kMaxPadChunks) return;
+  const int ext[3] = {p->T - (p->nt - 1) * p->ct, p->H - (p->nh - 1) * p->ch,
+                      p->W - (p->nw - 1) * p->cw};
+  const int plane = p->ch * p->cw;
+  for (int c = 0; c < p->tau / 64; ++c) {
+    unsigned long long m[3] = {0ull, 0ull, 0ull};
+    for (int k = 0; k < 64; ++k) {
+      const int local = 64 * c + k;
+      const int at[3] = {local / plane, (local % plane) / p->cw, local % p->cw};
+      for (int a = 0; a < 3; ++a)
+        if (at[a] < ext[a]) m[a] |= 1ull << k;
+    }
+    for (int a = 0; a < 3; ++a) p->pad_mask[a][c] = m[a];
+  }
+  p->pad_cpt = p->tau / 64;
 }
 
 inline void plan_tasks(AttnParams* p, long long tasks, int heads, bool dense) {
@@ -169,6 +202,22 @@ STA_HD bool run_key_real(const AttnParams& p, const KvRuns& kv, int r, int e) {
   const int it = r / kv.oh, ih = r - (r / kv.oh) * kv.oh;
   const int tw = e / p.tau;
   return tile_row_real(p, kv.st + it, kv.sh + ih, kv.sw + tw, e - tw * p.tau);
+}
+
+// Token mask of 64-key chunk `it` of walk w from the tables (pad_cpt > 0):
+// bit k for key 64 * (it - run * chunks_per_run) + k of its run. Everything
+// here is uniform over the wave, so it takes no vector work.
+STA_HD unsigned long long chunk_pad_mask(const AttnParams& p, const KvRuns& kv, int chunks_per_run,
+                                         int it) {
+  const int run = it / chunks_per_run;
+  const int rt = run / kv.oh, rh = run - rt * kv.oh;
+  const int j = it - run * chunks_per_run;
+  const int tw = j / p.pad_cpt, c = j - tw * p.pad_cpt;
+  unsigned long long m = ~0ull;
+  if ((kv.st + rt + 1) * p.ct > p.T) m &= p.pad_mask[0][c];
+  if ((kv.sh + rh + 1) * p.ch > p.H) m &= p.pad_mask[1][c];
+  if ((kv.sw + tw + 1) * p.cw > p.W) m &= p.pad_mask[2][c];
+  return m;
 }
 
 // Raster token index of row `local` (tile-major order inside the tile) of
@@ -328,6 +377,7 @@ inline void fill_params(const AttnProblem& pr, int rows_per_item, AttnParams* p)
     p->T = p->H = p->W = p->ct = p->ch = p->cw = 1;
     p->pad = 0;
     p->plane_cpt = p->plane_cpp = 0;
+    p->pad_cpt = 0;
   } else {
     p->n_units = pr.g.n_tiles;
     p->unit_rows = pr.g.tau;
@@ -337,6 +387,7 @@ inline void fill_params(const AttnProblem& pr, int rows_per_item, AttnParams* p)
     p->ct = pr.g.ct; p->ch = pr.g.ch; p->cw = pr.g.cw;
     p->pad = pr.g.padded;
     set_plane_chunks(p);
+    set_pad_masks(p);
     for (int h = 0; h < pr.heads; ++h)
       for (int a = 0; a < 3; ++a) p->omega[h][a] = pr.omega[h][a];
   }
@@ -380,6 +431,7 @@ inline void fill_bwd_params(const BwdProblem& pr, int rows_per_item, AttnParams*
   p->pad = a.g.padded;
   p->ct = a.g.ct; p->ch = a.g.ch; p->cw = a.g.cw;
   set_plane_chunks(p);
+  set_pad_masks(p);
   for (int h = 0; h < a.heads; ++h)
     for (int x = 0; x < 3; ++x) p->omega[h][x] = a.omega[h][x];
   p->row_blocks = (p->unit_rows + rows_per_item - 1) / rows_per_item;

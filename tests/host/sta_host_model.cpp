@@ -40,6 +40,7 @@ struct Ctx {
   long long launches = 0;
   long long tail_launches = 0;   // forward launches whose last round ran as 64-row items
   long long recall_passes = 0;   // one-pass window recall launches
+  long long pad_masks = 0;       // padded chunks whose precomputed token mask was checked
 } g_ctx;
 
 #define CHECK_ROW(row_, rows_, msg_)                                                         \
@@ -76,6 +77,16 @@ void model_chunk(const AttnParams& p, const ChunkWalk& w, int it, bool raster, b
                  long long rows, int row_bytes, int table_len, const char* what) {
   const int run = it / w.chunks_per_run;
   CHECK(run >= 0 && run < (w.dense ? 1 : w.kv.runs), "chunk index inside the walk");
+  if (pad && p.pad_cpt > 0 && w.bn == 64) {
+    // the kernels take the token mask of such a chunk from the plan's tables
+    // (chunk_pad_mask): it must equal the per-key definition
+    const unsigned long long m = sta::chunk_pad_mask(p, w.kv, w.chunks_per_run, it);
+    const int j = it - run * w.chunks_per_run;
+    for (int k = 0; k < 64; ++k)
+      CHECK(((m >> k) & 1ull) == (key_real(p, w, run, j * 64 + k, pad) ? 1ull : 0ull),
+            "precomputed chunk token mask");
+    ++g_ctx.pad_masks;
+  }
   if (plane) {
     const int row0 = w.at_plane(p, it);
     for (int key = 0; key < 64; ++key) {
@@ -547,7 +558,7 @@ int main() {
     }
   }
   printf("host model: %lld launches modelled (%lld forwards with a split last round, %lld one-pass "
-         "recalls), %lld checks, all in bounds\n",
-         g_ctx.launches, g_ctx.tail_launches, g_ctx.recall_passes, g_ctx.checks);
+         "recalls), %lld padded chunk masks from tables, %lld checks, all in bounds\n",
+         g_ctx.launches, g_ctx.tail_launches, g_ctx.recall_passes, g_ctx.pad_masks, g_ctx.checks);
   return 0;
 }

@@ -42,6 +42,10 @@ def test_host_model_under_sanitizers(tmp_path):
     assert tails and int(tails.group(1)) > 0, run.stdout[-500:]
     # window recall runs as one pass wherever the kernels allow: modelled too
     assert int(tails.group(2)) > 0, run.stdout[-500:]
+    # padded grids with tau a multiple of 64 take each chunk's token mask from
+    # precomputed tables: checked against the per-key rule on every such chunk
+    masks = re.search(r"(\d+) padded chunk masks from tables", run.stdout)
+    assert masks and int(masks.group(1)) > 0, run.stdout[-500:]
     # the float32 kernels' unpadded row mapping leaves a raster slice on a
     # padded grid (which is why the library refuses that case)
     assert "raster order: 324 query rows map past the 210 rows" in run.stdout
