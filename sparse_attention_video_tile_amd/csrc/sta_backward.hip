@@ -567,6 +567,10 @@ bwd_dkdv_pair_kernel(const AttnParams p, const BwdParams b) {
       walk.at(it, &row0, &nvalid);
       wait_vm_all();
       __syncthreads();
+      // the next chunk's loads go out as soon as its buffers are free
+      // (measured: 4 % faster on the whole backward than after the first
+      // products, 2.5 % than after the mid-chunk barrier)
+      if (it + 1 < walk.n_chunks) dma(it + 1, qnxt, onxt, lnxt, dnxt);
       const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
       // query rows that are not tokens score -inf, so their P is 0 (and so
       // is wave S's dS, which multiplies P)
@@ -575,7 +579,6 @@ bwd_dkdv_pair_kernel(const AttnParams p, const BwdParams b) {
       mma_rows<C, RB, !FULL>(s, qcur, koff, kf, km);    // S[q][key] = Q K^T
       sched_phase<RB, C::kKT * C::kDK, 1, 3, 0>();
       __builtin_amdgcn_sched_barrier(0);
-      if (it + 1 < walk.n_chunks) dma(it + 1, qnxt, onxt, lnxt, dnxt);
       f32x4 lq[C::kKT];
 #pragma unroll
       for (int kt = 0; kt < C::kKT; ++kt) lq[kt] = *reinterpret_cast<const f32x4*>(lcur + 16 * kt + 4 * g);
@@ -615,11 +618,11 @@ bwd_dkdv_pair_kernel(const AttnParams p, const BwdParams b) {
       walk.at(it, &row0, &nvalid);
       wait_vm_all();
       __syncthreads();
+      if (it + 1 < walk.n_chunks) dma(it + 1, qnxt, onxt, lnxt, dnxt);
       f32x4 dp[RB][C::kKT];
       mma_rows<C, RB>(dp, ocur, koff, vf);   // dP[q][key] = dO V^T
       sched_phase<RB, C::kKT * C::kDK, 1, 3, 0>();
       __builtin_amdgcn_sched_barrier(0);
-      if (it + 1 < walk.n_chunks) dma(it + 1, qnxt, onxt, lnxt, dnxt);
       f32x4 dq_[C::kKT];
 #pragma unroll
       for (int kt = 0; kt < C::kKT; ++kt) dq_[kt] = *reinterpret_cast<const f32x4*>(dcur + 16 * kt + 4 * g);
