@@ -746,94 +746,148 @@ attn_bf16_kernel(const AttnParams p) {
 // f32 kernel
 // ---------------------------------------------------------------------------
 
+// A work item is 64 query rows, one per lane, held by every wave of the
+// workgroup. The window's keys are cut into 32-key chunks (per run, the last
+// one ragged) and wave w takes chunks w, w + KS, w + 2 KS, ...: it stages
+// each in its own LDS buffers (no workgroup barrier in the loop) and keeps
+// its own running max, row sum and output. At the end the waves' partial
+// results go through LDS: each is weighted by 2^(m_w - M) against the rows'
+// common max M, and wave w sums and stores dimensions w * D / KS ...
 template <int D, bool RASTER>
-__global__ void __launch_bounds__(kF32Threads) attn_f32_kernel(const AttnParams p) {
-  __shared__ float4 ks[kF32BN * D / 4];
-  __shared__ float4 vs[kF32BN * D / 4];
+__global__ void __launch_bounds__(f32_key_splits(D) * 64) attn_f32_kernel(const AttnParams p) {
+  constexpr int KS = f32_key_splits(D);
+  constexpr int D4 = D / 4;
+  constexpr int kStage = KS * 2 * kF32BN * D4;   // float4: K and V chunk of every wave
+  constexpr int kMerge = KS * D * kF32Rows / 4;  // float4: every wave's weighted output
+  __shared__ float4 lds[kStage > kMerge ? kStage : kMerge];
+  __shared__ float mrow[KS][kF32Rows];
+  __shared__ float lrow[KS][kF32Rows];
   const int task = logical_task(p);
   if (task >= p.n_tasks) return;
-  const Task t = decode_task<kF32Threads>(p, task, D);
+  const Task t = decode_task<kF32Rows>(p, task, D);
   const float* qg = static_cast<const float*>(p.q) + t.head_base;
   const float4* kg = reinterpret_cast<const float4*>(static_cast<const float*>(p.k) + t.head_base);
   const float4* vg = reinterpret_cast<const float4*>(static_cast<const float*>(p.v) + t.head_base);
   float* og = p.out ? static_cast<float*>(p.out) + t.head_base : nullptr;
 
-  const int tid = threadIdx.x;
-  const bool row_ok = tid < t.valid_rows;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool row_ok = lane < t.valid_rows;
   float q[D], o[D];
-  const int my_row = row_ok ? tid : 0;
+  const int my_row = row_ok ? lane : 0;
   const int q_tok = RASTER ? tile_row_raster(p, t.qt, t.qh, t.qw, t.local0 + my_row) : t.row0 + my_row;
   const float* qrow = qg + (long long)q_tok * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    q[d] = row_ok ? qrow[d] : 0.f;
+    q[d] = qrow[d];
     o[d] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
 
-  for (int run = 0; run < t.kv.runs; ++run) {
-    const int kv0 = t.kv.run_start(run);
-    const int kv0_raster = RASTER ? t.kv.run_start_raster(run, p.H, p.W, p.ct, p.ch, p.cw) : 0;
-    for (int c0 = 0; c0 < t.kv.run_len; c0 += kF32BN) {
-      const int nvalid = min(kF32BN, t.kv.run_len - c0);
-      __syncthreads();
-      for (int i = tid; i < kF32BN * D / 4; i += kF32Threads) {
-        const int key = i / (D / 4);
-        float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+  float4* ks = lds + wave * (2 * kF32BN * D4);
+  float4* vs = ks + kF32BN * D4;
+  const int cpr = (t.kv.run_len + kF32BN - 1) / kF32BN;   // chunks per run
+  const int n_chunks = t.kv.runs * cpr;
+  for (int c = wave; c < n_chunks; c += KS) {
+    const int run = c / cpr;
+    const int c0 = (c - run * cpr) * kF32BN;
+    const int nvalid = min(kF32BN, t.kv.run_len - c0);
+    const int kv0 = RASTER ? t.kv.run_start_raster(run, p.H, p.W, p.ct, p.ch, p.cw) : t.kv.run_start(run);
+    // This wave's buffers only: its LDS operations run in order, so the
+    // reads below see these writes and the next chunk's writes follow them.
+    // Loads go out in groups (of eight float4 per operand for d = 64, all
+    // of the chunk; of four for d = 128, within the registers), each group
+    // before its writes.
+    constexpr int kPer = kF32BN * D4 / 64;   // float4 of K (and of V) per lane
+    constexpr int kGroup = D <= 64 ? (kPer < 8 ? kPer : 8) : 4;
+#pragma unroll
+    for (int r0 = 0; r0 < kPer; r0 += kGroup) {
+      float4 kx[kGroup], vx[kGroup];
+#pragma unroll
+      for (int r = 0; r < kGroup; ++r) {
+        const int i = lane + 64 * (r0 + r);
+        const int key = i / D4;
+        kx[r] = vx[r] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (key < nvalid) {
-          const int tok = RASTER ? kv0_raster + run_offset_raster(p, c0 + key) : kv0 + c0 + key;
-          const long long off = (long long)tok * (D / 4) + (i - key * (D / 4));
-          kx = kg[off];
-          vx = vg[off];
+          const int tok = kv0 + (RASTER ? run_offset_raster(p, c0 + key) : c0 + key);
+          const long long off = (long long)tok * D4 + (i - key * D4);
+          kx[r] = kg[off];
+          vx[r] = vg[off];
         }
-        ks[i] = kx;
-        vs[i] = vx;
       }
-      __syncthreads();
-      float s[kF32BN];
-      float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < kF32BN; ++j) {
-        float acc = 0.f;
-#pragma unroll
-        for (int d4 = 0; d4 < D / 4; ++d4) {
-          const float4 kk = ks[j * (D / 4) + d4];
-          acc = fmaf(q[4 * d4], kk.x, acc);
-          acc = fmaf(q[4 * d4 + 1], kk.y, acc);
-          acc = fmaf(q[4 * d4 + 2], kk.z, acc);
-          acc = fmaf(q[4 * d4 + 3], kk.w, acc);
-        }
-        s[j] = j < nvalid ? acc * p.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, s[j]);
+      for (int r = 0; r < kGroup; ++r) {
+        ks[lane + 64 * (r0 + r)] = kx[r];
+        vs[lane + 64 * (r0 + r)] = vx[r];
       }
-      const float m_new = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      m = m_new;
-      l *= alpha;
+    }
+    float s[kF32BN];
+    float mx = -INFINITY;
+#pragma unroll 8
+    for (int j = 0; j < kF32BN; ++j) {
+      float acc = 0.f;
 #pragma unroll
-      for (int d = 0; d < D; ++d) o[d] *= alpha;
+      for (int d4 = 0; d4 < D4; ++d4) {
+        const float4 kk = ks[j * D4 + d4];
+        acc = fmaf(q[4 * d4], kk.x, acc);
+        acc = fmaf(q[4 * d4 + 1], kk.y, acc);
+        acc = fmaf(q[4 * d4 + 2], kk.z, acc);
+        acc = fmaf(q[4 * d4 + 3], kk.w, acc);
+      }
+      s[j] = j < nvalid ? acc * p.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    const float m_new = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    l *= alpha;
 #pragma unroll
-      for (int j = 0; j < kF32BN; ++j) {
-        const float e = __builtin_amdgcn_exp2f(s[j] - m_new);
-        l += e;
+    for (int d = 0; d < D; ++d) o[d] *= alpha;
+#pragma unroll 8
+    for (int j = 0; j < kF32BN; ++j) {
+      const float e = __builtin_amdgcn_exp2f(s[j] - m_new);
+      l += e;
 #pragma unroll
-        for (int d4 = 0; d4 < D / 4; ++d4) {
-          const float4 vv = vs[j * (D / 4) + d4];
-          o[4 * d4] = fmaf(e, vv.x, o[4 * d4]);
-          o[4 * d4 + 1] = fmaf(e, vv.y, o[4 * d4 + 1]);
-          o[4 * d4 + 2] = fmaf(e, vv.z, o[4 * d4 + 2]);
-          o[4 * d4 + 3] = fmaf(e, vv.w, o[4 * d4 + 3]);
-        }
+      for (int d4 = 0; d4 < D4; ++d4) {
+        const float4 vv = vs[j * D4 + d4];
+        o[4 * d4] = fmaf(e, vv.x, o[4 * d4]);
+        o[4 * d4 + 1] = fmaf(e, vv.y, o[4 * d4 + 1]);
+        o[4 * d4 + 2] = fmaf(e, vv.z, o[4 * d4 + 2]);
+        o[4 * d4 + 3] = fmaf(e, vv.w, o[4 * d4 + 3]);
       }
     }
   }
+
+  // Merge. A wave that took no chunk has m = -inf and weight 0; the rows'
+  // common max is finite (every window holds at least one key).
+  mrow[wave][lane] = m;
+  lrow[wave][lane] = l;
+  __syncthreads();   // every wave is done with its chunk buffers, and m, l are visible
+  float mmax = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < KS; ++w) mmax = fmaxf(mmax, mrow[w][lane]);
+  const float a = __builtin_amdgcn_exp2f(m - mmax);
+  float* ob = reinterpret_cast<float*>(lds);   // [KS][D][64]: dimension-major, lanes contiguous
+#pragma unroll
+  for (int d = 0; d < D; ++d) ob[(wave * D + d) * kF32Rows + lane] = o[d] * a;
+  float lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < KS; ++w) lsum += lrow[w][lane] * __builtin_amdgcn_exp2f(mrow[w][lane] - mmax);
+  __syncthreads();
   if (row_ok) {
-    const float inv = 1.0f / l;
-    if (p.lse) p.lse[t.head_base / D + q_tok] = (m + __log2f(l)) * kLn2;
+    const float inv = 1.0f / lsum;
+    if (p.lse && wave == 0) p.lse[t.head_base / D + q_tok] = (mmax + __log2f(lsum)) * kLn2;
     if (og) {
       float* dst = og + (long long)q_tok * D;
+      constexpr int kDims = D / KS;
 #pragma unroll
-      for (int d = 0; d < D; ++d) dst[d] = o[d] * inv;
+      for (int dd = 0; dd < kDims; ++dd) {
+        const int d = wave * kDims + dd;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < KS; ++w) acc += ob[(w * D + d) * kF32Rows + lane];
+        dst[d] = acc * inv;
+      }
     }
   }
 }
@@ -1026,12 +1080,13 @@ int cu_per_xcd() {
 template <int D>
 int launch_f32(const AttnProblem& pr, hipStream_t stream) {
   AttnParams p;
-  fill_params(pr, kF32Threads, &p);
+  fill_params(pr, kF32Rows, &p);
   const unsigned grid = (unsigned)p.per_xcd * kXcds;
+  constexpr int kThreads = f32_key_splits(D) * 64;
   if (pr.raster && !pr.dense)
-    hipLaunchKernelGGL((attn_f32_kernel<D, true>), dim3(grid), dim3(kF32Threads), 0, stream, p);
+    hipLaunchKernelGGL((attn_f32_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_f32_kernel<D, false>), dim3(grid), dim3(kF32Threads), 0, stream, p);
+    hipLaunchKernelGGL((attn_f32_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
   return (int)hipGetLastError();
 }
 

@@ -465,8 +465,12 @@ constexpr int kRecallRows = 128;
 inline int fwd_bf16_rows(int unit_rows) {
   return unit_rows % kFwdBigRows == 0 ? kFwdBigRows : unit_rows <= 64 ? 64 : 128;
 }
-constexpr int kF32Threads = 128;   // float32 forward: one thread per query row
-constexpr int kF32BN = 32;         // float32 forward: keys per chunk
+// float32 forward: 64 query rows an item, one per lane; every wave of the
+// workgroup holds the same rows and takes every kF32Splits-th 32-key chunk of
+// the window, and the waves' partial results are merged at the end.
+constexpr int kF32Rows = 64;
+constexpr int kF32BN = 32;         // keys per chunk
+STA_HD constexpr int f32_key_splits(int D) { return D <= 64 ? 8 : 4; }
 constexpr int kF32Waves = 4;       // float32 backward: one wave per own row
 // bf16 backward, key side: 4 pairs of waves sharing 48 key rows when such
 // items tile tau, else pairs sharing 32 key rows (tiles of at least 128

@@ -219,43 +219,55 @@ void model_bf16_forward(const sta::AttnProblem& pr) {
   }
 }
 
-// The float32 forward (attn_f32_kernel): one thread per query row, 32-key
-// chunks staged in LDS arrays of kF32BN * D / 4 float4.
+// The float32 forward (attn_f32_kernel): 64 query rows an item, one per
+// lane of every wave; wave w stages chunks w, w + KS, ... of 32 keys in its
+// own K and V buffers of one LDS array, which the merge then reuses as
+// [KS][D][64] floats.
 template <int D>
 void model_f32_forward(const sta::AttnProblem& pr) {
+  constexpr int KS = sta::f32_key_splits(D);
+  constexpr int D4 = D / 4;
+  constexpr int kStage = KS * 2 * sta::kF32BN * D4;
+  constexpr int kMerge = KS * D * sta::kF32Rows / 4;
+  constexpr int kLds = kStage > kMerge ? kStage : kMerge;   // float4
   AttnParams p;
-  sta::fill_params(pr, sta::kF32Threads, &p);
+  sta::fill_params(pr, sta::kF32Rows, &p);
   const long long total_rows = (long long)pr.B * pr.heads * p.S;
   const bool raster = pr.raster && !pr.dense;
   const long long grid = (long long)p.per_xcd * sta::kXcds;
   for (long long bid = 0; bid < grid; ++bid) {
     const int task = sta::task_of_block(p, (int)bid);
     if (task >= p.n_tasks) continue;
-    const Task t = sta::decode_task<sta::kF32Threads>(p, task, D);
+    const Task t = sta::decode_task<sta::kF32Rows>(p, task, D);
     check_head(p, t, D, total_rows);
-    for (int tid = 0; tid < sta::kF32Threads; ++tid) {
-      const bool row_ok = tid < t.valid_rows;
-      const int my_row = row_ok ? tid : 0;
+    for (int lane = 0; lane < 64; ++lane) {
+      const bool row_ok = lane < t.valid_rows;
+      const int my_row = row_ok ? lane : 0;
       const long long q_tok = raster ? sta::tile_row_raster(p, t.qt, t.qh, t.qw, t.local0 + my_row)
                                      : (long long)t.row0 + my_row;
       CHECK_ROW(q_tok, p.S, row_ok ? "f32 query (read and written)" : "f32 query (read)");
+      for (int w = 0; w < KS; ++w)
+        for (int d = 0; d < D; ++d) CHECK((w * D + d) * sta::kF32Rows + lane < 4 * kLds, "f32 merge index");
     }
-    for (int run = 0; run < t.kv.runs; ++run) {
-      const int kv0 = t.kv.run_start(run);
-      const int kv0r = raster ? t.kv.run_start_raster(run, p.H, p.W, p.ct, p.ch, p.cw) : 0;
-      for (int c0 = 0; c0 < t.kv.run_len; c0 += sta::kF32BN) {
+    const int cpr = (t.kv.run_len + sta::kF32BN - 1) / sta::kF32BN;
+    const int n_chunks = t.kv.runs * cpr;
+    for (int wave = 0; wave < KS; ++wave)
+      for (int c = wave; c < n_chunks; c += KS) {
+        const int run = c / cpr;
+        const int c0 = (c - run * cpr) * sta::kF32BN;
+        CHECK(c0 < t.kv.run_len, "f32 chunk inside its run");
         const int nvalid = sta::imin(sta::kF32BN, t.kv.run_len - c0);
-        for (int i = 0; i < sta::kF32BN * D / 4; ++i) {
-          const int key = i / (D / 4);
-          CHECK(i < sta::kF32BN * D / 4, "f32 LDS index");
+        const long long kv0 = raster ? t.kv.run_start_raster(run, p.H, p.W, p.ct, p.ch, p.cw)
+                                     : t.kv.run_start(run);
+        for (int i = 0; i < sta::kF32BN * D4; ++i) {
+          const int key = i / D4;
+          CHECK(wave * (2 * sta::kF32BN * D4) + sta::kF32BN * D4 + i < kLds, "f32 LDS staging index");
           if (key < nvalid) {
-            const long long tok = raster ? (long long)kv0r + sta::run_offset_raster(p, c0 + key)
-                                         : (long long)kv0 + c0 + key;
+            const long long tok = kv0 + (raster ? sta::run_offset_raster(p, c0 + key) : c0 + key);
             CHECK_ROW(tok, p.S, "f32 key");
           }
         }
       }
-    }
   }
   ++g_ctx.launches;
 }
@@ -539,13 +551,13 @@ int main() {
     for (int raster = 0; raster < 2; ++raster) {
       pr.raster = raster;
       AttnParams p;
-      sta::fill_params(pr, sta::kF32Threads, &p);
+      sta::fill_params(pr, sta::kF32Rows, &p);
       long long worst = -1, outside = 0;
       const long long grid = (long long)p.per_xcd * sta::kXcds;
       for (long long bid = 0; bid < grid; ++bid) {
         const int task = sta::task_of_block(p, (int)bid);
         if (task >= p.n_tasks) continue;
-        const Task t = sta::decode_task<sta::kF32Threads>(p, task, 64);
+        const Task t = sta::decode_task<sta::kF32Rows>(p, task, 64);
         for (int tid = 0; tid < t.valid_rows; ++tid) {
           const long long tok = raster ? sta::tile_row_raster(p, t.qt, t.qh, t.qw, t.local0 + tid)
                                        : (long long)t.row0 + tid;
