@@ -746,25 +746,30 @@ attn_bf16_kernel(const AttnParams p) {
 // f32 kernel
 // ---------------------------------------------------------------------------
 
-// A work item is 64 query rows, one per lane, held by every wave of the
-// workgroup. The window's keys are cut into 32-key chunks (per run, the last
-// one ragged) and wave w takes chunks w, w + KS, w + 2 KS, ...: it stages
-// each in its own LDS buffers (no workgroup barrier in the loop) and keeps
-// its own running max, row sum and output. At the end the waves' partial
-// results go through LDS: each is weighted by 2^(m_w - M) against the rows'
-// common max M, and wave w sums and stores dimensions w * D / KS ...
+// A work item is 32 query rows held by every wave of the workgroup: lane l
+// keeps dimensions D/2 * (l / 32) .. of row l % 32 (a score is the sum of
+// the two halves' dot products, exchanged by a permlane swap). The window's
+// keys are cut into 32-key chunks (per run, the last one ragged) and wave w
+// takes chunks w, w + KS, w + 2 KS, ...: it stages each in its own LDS
+// buffers (no workgroup barrier in the loop) and keeps its own running max,
+// row sum and output. At the end the waves' partial results go through LDS:
+// each is weighted by 2^(m_w - M) against the rows' common max M, and wave w
+// sums and stores dimensions w * D / KS ...
 template <int D, bool RASTER>
 __global__ void __launch_bounds__(f32_key_splits(D) * 64) attn_f32_kernel(const AttnParams p) {
   constexpr int KS = f32_key_splits(D);
   constexpr int D4 = D / 4;
+  constexpr int DH = D / 2;                       // dimensions per lane
+  constexpr int H4 = D4 / 2;
+  constexpr int R = kF32Rows;
   constexpr int kStage = KS * 2 * kF32BN * D4;   // float4: K and V chunk of every wave
-  constexpr int kMerge = KS * D * kF32Rows / 4;  // float4: every wave's weighted output
+  constexpr int kMerge = KS * D * R / 4;         // float4: every wave's weighted output
   __shared__ float4 lds[kStage > kMerge ? kStage : kMerge];
-  __shared__ float mrow[KS][kF32Rows];
-  __shared__ float lrow[KS][kF32Rows];
+  __shared__ float mrow[KS][R];
+  __shared__ float lrow[KS][R];
   const int task = logical_task(p);
   if (task >= p.n_tasks) return;
-  const Task t = decode_task<kF32Rows>(p, task, D);
+  const Task t = decode_task<R>(p, task, D);
   const float* qg = static_cast<const float*>(p.q) + t.head_base;
   const float4* kg = reinterpret_cast<const float4*>(static_cast<const float*>(p.k) + t.head_base);
   const float4* vg = reinterpret_cast<const float4*>(static_cast<const float*>(p.v) + t.head_base);
@@ -772,13 +777,15 @@ __global__ void __launch_bounds__(f32_key_splits(D) * 64) attn_f32_kernel(const 
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool row_ok = lane < t.valid_rows;
-  float q[D], o[D];
-  const int my_row = row_ok ? lane : 0;
+  const int row = lane & (R - 1);
+  const int half = lane / R;
+  const bool row_ok = row < t.valid_rows;
+  float q[DH], o[DH];
+  const int my_row = row_ok ? row : 0;
   const int q_tok = RASTER ? tile_row_raster(p, t.qt, t.qh, t.qw, t.local0 + my_row) : t.row0 + my_row;
-  const float* qrow = qg + (long long)q_tok * D;
+  const float* qrow = qg + (long long)q_tok * D + half * DH;
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
+  for (int d = 0; d < DH; ++d) {
     q[d] = qrow[d];
     o[d] = 0.f;
   }
@@ -821,19 +828,22 @@ __global__ void __launch_bounds__(f32_key_splits(D) * 64) attn_f32_kernel(const 
         vs[lane + 64 * (r0 + r)] = vx[r];
       }
     }
+    const float4* kh = ks + half * H4;
+    const float4* vh = vs + half * H4;
     float s[kF32BN];
     float mx = -INFINITY;
 #pragma unroll 8
     for (int j = 0; j < kF32BN; ++j) {
       float acc = 0.f;
 #pragma unroll
-      for (int d4 = 0; d4 < D4; ++d4) {
-        const float4 kk = ks[j * D4 + d4];
+      for (int d4 = 0; d4 < H4; ++d4) {
+        const float4 kk = kh[j * D4 + d4];
         acc = fmaf(q[4 * d4], kk.x, acc);
         acc = fmaf(q[4 * d4 + 1], kk.y, acc);
         acc = fmaf(q[4 * d4 + 2], kk.z, acc);
         acc = fmaf(q[4 * d4 + 3], kk.w, acc);
       }
+      acc = pair32(acc, false);   // + the other half of the row (the same sum on both lanes)
       s[j] = j < nvalid ? acc * p.scale_log2 : -INFINITY;
       mx = fmaxf(mx, s[j]);
     }
@@ -842,14 +852,14 @@ __global__ void __launch_bounds__(f32_key_splits(D) * 64) attn_f32_kernel(const 
     m = m_new;
     l *= alpha;
 #pragma unroll
-    for (int d = 0; d < D; ++d) o[d] *= alpha;
+    for (int d = 0; d < DH; ++d) o[d] *= alpha;
 #pragma unroll 8
     for (int j = 0; j < kF32BN; ++j) {
       const float e = __builtin_amdgcn_exp2f(s[j] - m_new);
       l += e;
 #pragma unroll
-      for (int d4 = 0; d4 < D4; ++d4) {
-        const float4 vv = vs[j * D4 + d4];
+      for (int d4 = 0; d4 < H4; ++d4) {
+        const float4 vv = vh[j * D4 + d4];
         o[4 * d4] = fmaf(e, vv.x, o[4 * d4]);
         o[4 * d4 + 1] = fmaf(e, vv.y, o[4 * d4 + 1]);
         o[4 * d4 + 2] = fmaf(e, vv.z, o[4 * d4 + 2]);
@@ -859,33 +869,36 @@ __global__ void __launch_bounds__(f32_key_splits(D) * 64) attn_f32_kernel(const 
   }
 
   // Merge. A wave that took no chunk has m = -inf and weight 0; the rows'
-  // common max is finite (every window holds at least one key).
-  mrow[wave][lane] = m;
-  lrow[wave][lane] = l;
+  // common max is finite (every window holds at least one key). Both lanes
+  // of a row hold the same m and l.
+  if (half == 0) {
+    mrow[wave][row] = m;
+    lrow[wave][row] = l;
+  }
   __syncthreads();   // every wave is done with its chunk buffers, and m, l are visible
   float mmax = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < KS; ++w) mmax = fmaxf(mmax, mrow[w][lane]);
+  for (int w = 0; w < KS; ++w) mmax = fmaxf(mmax, mrow[w][row]);
   const float a = __builtin_amdgcn_exp2f(m - mmax);
-  float* ob = reinterpret_cast<float*>(lds);   // [KS][D][64]: dimension-major, lanes contiguous
+  float* ob = reinterpret_cast<float*>(lds);   // [KS][D][R]: dimension-major, rows contiguous
 #pragma unroll
-  for (int d = 0; d < D; ++d) ob[(wave * D + d) * kF32Rows + lane] = o[d] * a;
+  for (int d = 0; d < DH; ++d) ob[(wave * D + half * DH + d) * R + row] = o[d] * a;
   float lsum = 0.f;
 #pragma unroll
-  for (int w = 0; w < KS; ++w) lsum += lrow[w][lane] * __builtin_amdgcn_exp2f(mrow[w][lane] - mmax);
+  for (int w = 0; w < KS; ++w) lsum += lrow[w][row] * __builtin_amdgcn_exp2f(mrow[w][row] - mmax);
   __syncthreads();
   if (row_ok) {
     const float inv = 1.0f / lsum;
-    if (p.lse && wave == 0) p.lse[t.head_base / D + q_tok] = (mmax + __log2f(lsum)) * kLn2;
+    if (p.lse && wave == 0 && half == 0) p.lse[t.head_base / D + q_tok] = (mmax + __log2f(lsum)) * kLn2;
     if (og) {
       float* dst = og + (long long)q_tok * D;
-      constexpr int kDims = D / KS;
+      constexpr int kDims = D / KS / 2;   // per lane
 #pragma unroll
       for (int dd = 0; dd < kDims; ++dd) {
-        const int d = wave * kDims + dd;
+        const int d = (2 * wave + half) * kDims + dd;
         float acc = 0.f;
 #pragma unroll
-        for (int w = 0; w < KS; ++w) acc += ob[(w * D + d) * kF32Rows + lane];
+        for (int w = 0; w < KS; ++w) acc += ob[(w * D + d) * R + row];
         dst[d] = acc * inv;
       }
     }

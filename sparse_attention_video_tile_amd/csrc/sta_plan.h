@@ -465,10 +465,11 @@ constexpr int kRecallRows = 128;
 inline int fwd_bf16_rows(int unit_rows) {
   return unit_rows % kFwdBigRows == 0 ? kFwdBigRows : unit_rows <= 64 ? 64 : 128;
 }
-// float32 forward: 64 query rows an item, one per lane; every wave of the
-// workgroup holds the same rows and takes every kF32Splits-th 32-key chunk of
-// the window, and the waves' partial results are merged at the end.
-constexpr int kF32Rows = 64;
+// float32 forward: 32 query rows an item, two lanes a row (half the head
+// dimension each); every wave of the workgroup holds the same rows and takes
+// every f32_key_splits(D)-th 32-key chunk of the window, and the waves'
+// partial results are merged at the end.
+constexpr int kF32Rows = 32;
 constexpr int kF32BN = 32;         // keys per chunk
 STA_HD constexpr int f32_key_splits(int D) { return D <= 64 ? 8 : 4; }
 constexpr int kF32Waves = 4;       // float32 backward: one wave per own row

@@ -219,10 +219,10 @@ void model_bf16_forward(const sta::AttnProblem& pr) {
   }
 }
 
-// The float32 forward (attn_f32_kernel): 64 query rows an item, one per
-// lane of every wave; wave w stages chunks w, w + KS, ... of 32 keys in its
-// own K and V buffers of one LDS array, which the merge then reuses as
-// [KS][D][64] floats.
+// The float32 forward (attn_f32_kernel): 32 query rows an item, lane l of
+// every wave on row l % 32 (half the dimensions each); wave w stages chunks
+// w, w + KS, ... of 32 keys in its own K and V buffers of one LDS array, which
+// the merge then reuses as [KS][D][32] floats.
 template <int D>
 void model_f32_forward(const sta::AttnProblem& pr) {
   constexpr int KS = sta::f32_key_splits(D);
@@ -241,13 +241,23 @@ void model_f32_forward(const sta::AttnProblem& pr) {
     const Task t = sta::decode_task<sta::kF32Rows>(p, task, D);
     check_head(p, t, D, total_rows);
     for (int lane = 0; lane < 64; ++lane) {
-      const bool row_ok = lane < t.valid_rows;
-      const int my_row = row_ok ? lane : 0;
+      const int row = lane % sta::kF32Rows, half = lane / sta::kF32Rows;
+      const bool row_ok = row < t.valid_rows;
+      const int my_row = row_ok ? row : 0;
       const long long q_tok = raster ? sta::tile_row_raster(p, t.qt, t.qh, t.qw, t.local0 + my_row)
                                      : (long long)t.row0 + my_row;
       CHECK_ROW(q_tok, p.S, row_ok ? "f32 query (read and written)" : "f32 query (read)");
       for (int w = 0; w < KS; ++w)
-        for (int d = 0; d < D; ++d) CHECK((w * D + d) * sta::kF32Rows + lane < 4 * kLds, "f32 merge index");
+        for (int d = 0; d < D / 2; ++d)
+          CHECK((w * D + half * (D / 2) + d) * sta::kF32Rows + row < 4 * kLds, "f32 merge index");
+      for (int wave = 0; wave < KS; ++wave)
+        for (int dd = 0; dd < D / KS / 2; ++dd) {
+          const int d = (2 * wave + half) * (D / KS / 2) + dd;
+          CHECK(d < D, "f32 stored dimension");
+          for (int w = 0; w < KS; ++w) CHECK((w * D + d) * sta::kF32Rows + row < 4 * kLds, "f32 merge read");
+        }
+      for (int j = 0; j < sta::kF32BN; ++j)
+        for (int d4 = 0; d4 < D4 / 2; ++d4) CHECK(half * (D4 / 2) + j * D4 + d4 < sta::kF32BN * D4, "f32 operand read");
     }
     const int cpr = (t.kv.run_len + sta::kF32BN - 1) / sta::kF32BN;
     const int n_chunks = t.kv.runs * cpr;
