@@ -454,7 +454,7 @@ def main(argv=None):
             "launch_ms": attn_ms,
             "launch_note": "one step's attention launches, HIP events around them: whole-tile work "
                            "items, then (when they leave the last round mostly idle) that round "
-                           "as 64-row items in a second launch",
+                           "as 64-row items (keys split over two wave groups) in a second launch",
         },
         "cpu_baseline": cpu,
         "dense": dense,

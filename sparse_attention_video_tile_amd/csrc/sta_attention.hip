@@ -14,7 +14,8 @@
 // recall, which runs the whole volume as the window (full attention) and
 // also sums, per candidate window, the probabilities of the key tiles the
 // candidate holds. Whole-tile work items leave a partly filled last round on
-// each XCD; the host runs it as 64-row items in a second launch.
+// each XCD; the host runs it as 64-row items in a second launch, whose two
+// wave groups split each item's key chunks between them (KSPLIT).
 //
 // bf16 kernel. Each wavefront owns RB blocks of 16 query rows. It computes
 // S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (K from LDS as the A operand, the
@@ -30,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cfloat>
 
 #include "sta_attn_common.h"
 
@@ -455,17 +457,27 @@ attn_bf16_kernel(const AttnParams p) {
   // 64-key chunks of one key tile each, so membership is per chunk).
   static_assert(!RECALL || (LSE_ONLY && FULL && !DENSE && BN == 64 && (!RASTER || PLANE)),
                 "one-pass recall: whole chunks, no raster offset table");
-  using C = Bf16Cfg<D, WAVES, RB, BN, QK8>;
+  // KSPLIT, the 8-wave configuration of 16-row blocks (the items a split
+  // last round runs as): waves 0-3 and waves 4-7 hold the same 64 query
+  // rows and take the even and the odd key chunks of the walk, each group
+  // with its own K/V buffers and softmax state; the two states are merged
+  // through LDS at the end. A work item then takes half as many chunk steps.
+  constexpr bool KSPLIT = WAVES == 8 && RB == 1;
+  constexpr int kGroups = KSPLIT ? 2 : 1;
+  constexpr int GW = WAVES / kGroups;   // waves of a group; the rows are GW * 16 * RB
+  constexpr int kThreadsAll = WAVES * 64;
+  static_assert(!KSPLIT || !RECALL, "one-pass recall does not split its keys");
+  using C = Bf16Cfg<D, GW, RB, BN, QK8>;
   using KG = typename C::KGeom;
   // K and V buffers of two chunks. They are separate objects and the loop
   // selects them statically, so the compiler can tell the chunk being read
   // apart from the one the LDS DMA is filling and does not wait for the
   // prefetch before reading.
   // (Log-sum-exp only: no V, so no V buffers; more workgroups fit a CU.)
-  __shared__ __attribute__((aligned(1024))) char kb0[KG::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char vb0[LSE_ONLY ? 16 : C::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char kb1[KG::kChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char vb1[LSE_ONLY ? 16 : C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char kb0[kGroups * KG::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char vb0[LSE_ONLY ? 16 : kGroups * C::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char kb1[kGroups * KG::kChunkBytes];
+  __shared__ __attribute__((aligned(1024))) char vb1[LSE_ONLY ? 16 : kGroups * C::kChunkBytes];
   // Raster offsets of one window run (RASTER only), sized at launch.
   extern __shared__ int rtab[];
 
@@ -479,19 +491,23 @@ attn_bf16_kernel(const AttnParams p) {
   bf16_t* og = static_cast<bf16_t*>(p.out) + t.head_base;
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // wave: this wave's place among the waves that share its key chunks (the
+  // row block it owns, its share of each chunk's loads); grp: its key group.
+  const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = KSPLIT ? wave_id % GW : wave_id;
+  const int grp = KSPLIT ? wave_id / GW : 0;
   const int l16 = lane & 15;
   const int g = lane >> 4;
   const ChunkWalk walk = make_walk<BN, DENSE>(t, p.S);
   // Plane chunks: raster rows by arithmetic (no table); else the table.
   constexpr bool plane = RASTER && PLANE && BN == 64;
-  int lane_row[(C::kBlocks + WAVES - 1) / WAVES];
-  int lane_row_k[(KG::kBlocks + WAVES - 1) / WAVES];   // fp8 K rows (QK8 only)
+  int lane_row[(C::kBlocks + GW - 1) / GW];
+  int lane_row_k[(KG::kBlocks + GW - 1) / GW];   // fp8 K rows (QK8 only)
   if constexpr (plane) {
-    plane_lane_rows<C, WAVES>(p, wave, lane, lane_row);
-    if constexpr (QK8) plane_lane_rows<KG, WAVES>(p, wave, lane, lane_row_k);
+    plane_lane_rows<C, GW>(p, wave, lane, lane_row);
+    if constexpr (QK8) plane_lane_rows<KG, GW>(p, wave, lane, lane_row_k);
   } else if (RASTER) {
-    for (int e = threadIdx.x; e < walk.run_len; e += C::kThreads) rtab[e] = run_offset_raster(p, e);
+    for (int e = threadIdx.x; e < walk.run_len; e += kThreadsAll) rtab[e] = run_offset_raster(p, e);
     __syncthreads();
   }
   // RECALL: bit c of cand_tab[it] says whether candidate window c of this
@@ -512,7 +528,7 @@ attn_bf16_kernel(const AttnParams p) {
     // its key tile's three axis masks.
     unsigned char* axis_tab = cand_tab + ((p.cand_chunks + 3) & ~3);
     const int na = p.nt + p.nh + p.nw;
-    for (int e = threadIdx.x; e < na; e += C::kThreads) {
+    for (int e = threadIdx.x; e < na; e += kThreadsAll) {
       const int a = e < p.nt ? 0 : e < p.nt + p.nh ? 1 : 2;
       const int i = e - (a == 0 ? 0 : a == 1 ? p.nt : p.nt + p.nh);
       const int n = a == 0 ? p.nt : a == 1 ? p.nh : p.nw;
@@ -526,7 +542,7 @@ attn_bf16_kernel(const AttnParams p) {
     }
     __syncthreads();
     const int cpt = p.tau / BN;   // chunks per key tile
-    for (int e = threadIdx.x; e < walk.n_chunks && e < p.cand_chunks; e += C::kThreads) {
+    for (int e = threadIdx.x; e < walk.n_chunks && e < p.cand_chunks; e += kThreadsAll) {
       const int run = e / walk.chunks_per_run, j = e - run * walk.chunks_per_run;
       const int kt = t.kv.st + run / t.kv.oh, kh = t.kv.sh + run % t.kv.oh;
       const int kw = t.kv.sw + j / cpt;
@@ -545,30 +561,35 @@ attn_bf16_kernel(const AttnParams p) {
     if constexpr (plane) {
       const int row0 = walk.at_plane(p, it);
       if constexpr (QK8)
-        load_rows_plane<KG, WAVES>(kg, row0, lane_row_k, kdst, wave, lane);
+        load_rows_plane<KG, GW>(kg, row0, lane_row_k, kdst, wave, lane);
       else
-        load_rows_plane<C, WAVES>(kg, row0, lane_row, kdst, wave, lane);
-      if (!LSE_ONLY) load_rows_plane<C, WAVES>(vg, row0, lane_row, vdst, wave, lane);
+        load_rows_plane<C, GW>(kg, row0, lane_row, kdst, wave, lane);
+      if (!LSE_ONLY) load_rows_plane<C, GW>(vg, row0, lane_row, vdst, wave, lane);
     } else if (RASTER) {
       int base, c0, nv;
       walk.at_raster(p, it, &base, &c0, &nv);
       const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
-      load_rows<KG, WAVES>(kg, base, nv, kdst, wave, lane, rtab + c0, real);
-      if (!LSE_ONLY) load_rows<C, WAVES>(vg, base, nv, vdst, wave, lane, rtab + c0, real);
+      load_rows<KG, GW>(kg, base, nv, kdst, wave, lane, rtab + c0, real);
+      if (!LSE_ONLY) load_rows<C, GW>(vg, base, nv, vdst, wave, lane, rtab + c0, real);
     } else if constexpr (PAD) {
       int row0, kb, nv;
       walk.at_tile(it, p.tau, &row0, &kb, &nv);
       const unsigned long long real = chunk_real_keys<PAD>(p, walk, it, lane);
-      load_rows<KG, WAVES>(kg, row0, nv, kdst, wave, lane, nullptr, real, kb);
-      if (!LSE_ONLY) load_rows<C, WAVES>(vg, row0, nv, vdst, wave, lane, nullptr, real, kb);
+      load_rows<KG, GW>(kg, row0, nv, kdst, wave, lane, nullptr, real, kb);
+      if (!LSE_ONLY) load_rows<C, GW>(vg, row0, nv, vdst, wave, lane, nullptr, real, kb);
     } else {
       int row0, nv;
       walk.at(it, &row0, &nv);
-      load_rows<KG, WAVES>(kg, row0, nv, kdst, wave, lane);
-      if (!LSE_ONLY) load_rows<C, WAVES>(vg, row0, nv, vdst, wave, lane);
+      load_rows<KG, GW>(kg, row0, nv, kdst, wave, lane);
+      if (!LSE_ONLY) load_rows<C, GW>(vg, row0, nv, vdst, wave, lane);
     }
   };
-  dma(0, kb0, vb0);
+  // This group's two K/V buffers.
+  char* const k0 = kb0 + grp * KG::kChunkBytes;
+  char* const k1 = kb1 + grp * KG::kChunkBytes;
+  char* const v0 = LSE_ONLY ? vb0 : vb0 + grp * C::kChunkBytes;
+  char* const v1 = LSE_ONLY ? vb1 : vb1 + grp * C::kChunkBytes;
+  if (!KSPLIT || grp < walk.n_chunks) dma(grp, k0, v0);
   WaveState<C, RB> w;
   load_q_init<C, RB>(w, qg, map_rows<C, RB, RASTER>(p, t, wave, l16), l16, g);
 
@@ -585,7 +606,7 @@ attn_bf16_kernel(const AttnParams p) {
   auto chunk_step = [&](auto first, const char* kcur, const char* vcur, char* knxt, char* vnxt, int it)
                         __attribute__((always_inline)) {
     if constexpr (kSingleBuffer) {
-      kcur = kb0; vcur = vb0; knxt = nullptr; vnxt = nullptr;
+      kcur = k0; vcur = v0; knxt = nullptr; vnxt = nullptr;
     }
     int row0, nvalid;
     walk.at(it, &row0, &nvalid);
@@ -639,7 +660,7 @@ attn_bf16_kernel(const AttnParams p) {
       // fp8: one MFMA per tile and row block, twice as long as a bf16 one.
       sched_qk_softmax<RB, C::kKT, C::kDK, (plane ? 1 : 2) * (QK8 ? 2 : 1), QK8 ? 2 : 1>();
       __builtin_amdgcn_sched_barrier(0);
-      if (!kSingleBuffer && it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
+      if (!kSingleBuffer && it + kGroups < walk.n_chunks) dma(it + kGroups, knxt, vnxt);
       bool grow = false;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) grow |= !(lc[rb] <= 256.0f);   // also an infinite sum
@@ -693,8 +714,20 @@ attn_bf16_kernel(const AttnParams p) {
       // The next chunk's loads go out after QK^T, so their LDS writes land
       // during the softmax (few LDS reads) rather than beside the K reads
       // (measured: 2 % faster than issuing right after the barrier).
-      if (!kSingleBuffer && it + 1 < walk.n_chunks) dma(it + 1, knxt, vnxt);
-      softmax_chunk<C, RB, LSE_ONLY>(w, nvalid, real, p.scale_log2, g);
+      if (!kSingleBuffer && it + kGroups < walk.n_chunks) dma(it + kGroups, knxt, vnxt);
+      if constexpr (KSPLIT) {
+        // The odd group's first chunk (chunk 1) can be all padding on a
+        // padded grid: its rows' max stays -inf. A finite stand-in keeps
+        // the exponentials of masked keys at 0 instead of NaN; a later real
+        // score then exceeds it and takes the rescale branch (factor 0).
+        softmax_max<C, RB>(w, w.s, nvalid, real, p.scale_log2, g);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if (w.m[rb] == -INFINITY) w.m[rb] = -FLT_MAX;
+        softmax_exp<C, RB, LSE_ONLY>(w, w.s, p.scale_log2);
+      } else {
+        softmax_chunk<C, RB, LSE_ONLY>(w, nvalid, real, p.scale_log2, g);
+      }
       if constexpr (RECALL) {
         // the work item's first chunk: the row sums were 0 before it
         float x[RB];
@@ -712,31 +745,91 @@ attn_bf16_kernel(const AttnParams p) {
     }
     if constexpr (kSingleBuffer) {
       __syncthreads();   // every wave is done with this chunk's K and V
-      if (it + 1 < walk.n_chunks) dma(it + 1, kb0, vb0);
+      if (it + kGroups < walk.n_chunks) dma(it + kGroups, k0, v0);
     }
   };
   // The first chunk sets the reference max: the max-first order (with the
   // masks of its keys that are not tokens), which the sum test would
   // otherwise send down its rare branch every time. A work item's first
   // chunk always holds a token (its window's first tile starts at one).
-  chunk_step(FirstChunk<true>{}, kb0, vb0, kb1, vb1, 0);
-  for (int it = 1; it < walk.n_chunks; it += 2) {
-    chunk_step(FirstChunk<false>{}, kb1, vb1, kb0, vb0, it);
-    if (it + 1 < walk.n_chunks) chunk_step(FirstChunk<false>{}, kb0, vb0, kb1, vb1, it + 1);
+  // Step s runs chunk s * kGroups + grp of the walk. KSPLIT: a group whose
+  // chunk is past the walk's end (the odd group of an odd chunk count) only
+  // keeps the step's barriers.
+  const int steps = (walk.n_chunks + kGroups - 1) / kGroups;
+  auto step = [&](auto first, char* kcur, char* vcur, char* knxt, char* vnxt, int s)
+                  __attribute__((always_inline)) {
+    const int it = s * kGroups + grp;
+    if (!KSPLIT || it < walk.n_chunks) {
+      chunk_step(first, kcur, vcur, knxt, vnxt, it);
+    } else {
+      __syncthreads();
+      if constexpr (kSingleBuffer) __syncthreads();
+    }
+  };
+  step(FirstChunk<true>{}, k0, v0, k1, v1, 0);
+  for (int s = 1; s < steps; s += 2) {
+    step(FirstChunk<false>{}, k1, v1, k0, v0, s);
+    if (s + 1 < steps) step(FirstChunk<false>{}, k0, v0, k1, v1, s + 1);
   }
-  // The row map is built again rather than kept in registers across the loop.
-  const RowMap<C, RB> rm_out = map_rows<C, RB, RASTER>(p, t, wave, l16);
-  store_out<C, RB>(w, LSE_ONLY ? nullptr : og, p.lse ? p.lse + t.head_base / D : nullptr, rm_out, g);
-  if constexpr (RECALL) {
-    // each candidate's row log-sum-exp: ln 2 * (m + log2 of its row sum)
-#pragma unroll
-    for (int c = 0; c < kMaxRecallCand; ++c) {
-      if (c >= p.n_cand) break;   // uniform
-      float* dst = p.lse_cand + c * p.cand_stride + t.head_base / D;
+  if constexpr (KSPLIT) {
+    // Merge: the odd group's reference max, lane sums and output go through
+    // the K and V buffers to the even group's wave of the same rows, each
+    // side weighted by 2^(m - M) against the larger max M (the odd group's
+    // m is -inf, its weight 0, when it ran no chunk).
+    static_assert(LSE_ONLY || GW * RB * C::kDB * 4 * 64 * 4 <= (int)sizeof(vb0), "merge output fits the V buffers");
+    static_assert(GW * 2 * RB * 64 * 4 <= (int)sizeof(kb0), "merge state fits the K buffers");
+    __syncthreads();   // both groups are done with their chunk buffers
+    float* xs = reinterpret_cast<float*>(kb0);   // [GW][2 RB][64]: m, lane sum
+    float* xo = reinterpret_cast<float*>(vb0);   // [GW][RB * kDB * 4][64]
+    if (grp == 1) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const float l = row_sum4(lc_c[c][rb]);
-        if (rm_out.ok[rb] && g == 0) dst[rm_out.tok[rb]] = (w.m[rb] + __log2f(l)) * kLn2;
+        xs[(wave * 2 * RB + 2 * rb) * 64 + lane] = w.m[rb];
+        xs[(wave * 2 * RB + 2 * rb + 1) * 64 + lane] = w.lsum[rb];
+        if constexpr (!LSE_ONLY) {
+#pragma unroll
+          for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xo[((wave * RB + rb) * C::kDB * 4 + 4 * db + e) * 64 + lane] = w.o[rb][db][e];
+        }
+      }
+    }
+    __syncthreads();
+    if (grp == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float m1 = xs[(wave * 2 * RB + 2 * rb) * 64 + lane];
+        const float l1 = xs[(wave * 2 * RB + 2 * rb + 1) * 64 + lane];
+        const float mm = fmaxf(w.m[rb], m1);
+        const float a0 = __builtin_amdgcn_exp2f(w.m[rb] - mm);
+        const float a1 = __builtin_amdgcn_exp2f(m1 - mm);
+        w.m[rb] = mm;
+        w.lsum[rb] = w.lsum[rb] * a0 + l1 * a1;
+        if constexpr (!LSE_ONLY) {
+#pragma unroll
+          for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              w.o[rb][db][e] = w.o[rb][db][e] * a0 + xo[((wave * RB + rb) * C::kDB * 4 + 4 * db + e) * 64 + lane] * a1;
+        }
+      }
+    }
+  }
+  if (!KSPLIT || grp == 0) {
+    // The row map is built again rather than kept in registers across the loop.
+    const RowMap<C, RB> rm_out = map_rows<C, RB, RASTER>(p, t, wave, l16);
+    store_out<C, RB>(w, LSE_ONLY ? nullptr : og, p.lse ? p.lse + t.head_base / D : nullptr, rm_out, g);
+    if constexpr (RECALL) {
+      // each candidate's row log-sum-exp: ln 2 * (m + log2 of its row sum)
+#pragma unroll
+      for (int c = 0; c < kMaxRecallCand; ++c) {
+        if (c >= p.n_cand) break;   // uniform
+        float* dst = p.lse_cand + c * p.cand_stride + t.head_base / D;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const float l = row_sum4(lc_c[c][rb]);
+          if (rm_out.ok[rb] && g == 0) dst[rm_out.tok[rb]] = (w.m[rb] + __log2f(l)) * kLn2;
+        }
       }
     }
   }
@@ -925,7 +1018,8 @@ unsigned raster_table_bytes(const AttnProblem& pr) {
 template <int D, int WAVES, int RB, int BN, bool FULL, bool QK8>
 bool launch_recall_pass(const AttnProblem& pr, const AttnParams& p, unsigned grid, hipStream_t stream) {
   using C = Bf16Cfg<D, WAVES, RB, BN>;
-  if constexpr (!FULL || BN != 64 || Bf16Cfg<D, WAVES, RB, BN>::kRows != kRecallRows) {
+  if constexpr (!FULL || BN != 64 || Bf16Cfg<D, WAVES, RB, BN>::kRows != kRecallRows ||
+                (WAVES == 8 && RB == 1)) {
     return false;   // only the recall shape (dispatch_bf16) has these kernels
   } else {
     const bool plane = p.plane_cpt > 0;
@@ -1125,8 +1219,10 @@ int dispatch_bf16(const AttnProblem& pr, hipStream_t stream) {
     const int rc = launch_bf16_planned<D, STA_CFG_WAVES, STA_CFG_RB, STA_CFG_BN, QK8>(
         pr, p, (unsigned)main_per_xcd * kXcds, stream);
     if (rc || !tail) return rc;
-    static_assert(Bf16Cfg<D, 4, 1, 64>::kRows == kFwdTailRows, "tail shape");
-    return launch_bf16_planned<D, 4, 1, 64, QK8>(pr, tp, (unsigned)tp.per_xcd * kXcds, stream);
+    // 8 waves of 16 rows: two groups of 4 waves on the same 64 rows, each
+    // taking half of the key chunks (the KSPLIT configuration of the kernel)
+    static_assert(4 * 16 == kFwdTailRows, "tail shape");
+    return launch_bf16_planned<D, 8, 1, 64, QK8>(pr, tp, (unsigned)tp.per_xcd * kXcds, stream);
   }
   if (rows == 64) return launch_bf16<D, 4, 1, 64, QK8>(pr, stream);
   return launch_bf16<D, 4, 2, 64, QK8>(pr, stream);

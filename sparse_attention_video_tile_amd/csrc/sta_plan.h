@@ -456,7 +456,8 @@ inline void fill_bwd_params(const BwdProblem& pr, int rows_per_item, AttnParams*
 #define STA_CFG_BN 64
 #endif
 constexpr int kFwdBigRows = STA_CFG_WAVES * 16 * STA_CFG_RB;
-// Rows of the items a split last round runs as (4 waves of 16 rows).
+// Rows of the items a split last round runs as (two groups of 4 waves of 16
+// rows, each group taking half of the key chunks).
 constexpr int kFwdTailRows = 64;
 // Rows of the items of a one-pass window recall (4 waves of 32 rows).
 constexpr int kRecallRows = 128;

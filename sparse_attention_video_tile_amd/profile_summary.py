@@ -128,6 +128,7 @@ def role(name: str) -> str:
         pad = len(a) > 7 and a[7] == "true"
         qk8 = len(a) > 10 and a[10] == "true"
         small = a[1] == "4" and a[2] == "1"   # 4 waves of 16 rows: 64-row items
+        ksplit = a[1] == "8" and a[2] == "1"  # two groups of 4 waves on 64 rows (a split last round)
         what = "dense comparator" if dense else (
             "STA forward, raster order (fused path)" if raster else "STA forward, tile-major (three-call path)")
         if lse_only:
@@ -140,6 +141,8 @@ def role(name: str) -> str:
             what += ", one pass over all candidate windows"
         if small:
             what += ", 64-row items"
+        if ksplit:
+            what += ", 64-row items, keys split over two wave groups"
         return what
     if "attn_f32_kernel" in name:
         return "STA forward, float32"
@@ -163,7 +166,7 @@ def is_headline(name: str) -> bool:
 def is_headline_tail(name: str) -> bool:
     """The second launch of a headline step: the last round's items as 64-row
     items (absent when the work items fill every round)."""
-    return role(name) == "STA forward, raster order (fused path), 64-row items"
+    return role(name).startswith("STA forward, raster order (fused path), 64-row items")
 
 
 def step_dispatches(ids_names):
@@ -410,7 +413,7 @@ def main(argv=None) -> int:
                 "commands": [pmc_cmd("FETCH_SIZE"), pmc_cmd("WRITE_SIZE")],
             }
     # the tile-major path's step: add its 64-row tail launch, if it has one
-    tails = [n for n in kernels if role(n) == "STA forward, tile-major (three-call path), 64-row items"]
+    tails = [n for n in kernels if role(n).startswith("STA forward, tile-major (three-call path), 64-row items")]
     if "three_call" in records and tails:
         f, w, _ = summarize(lambda x: x == tails[0])
         rec = records["three_call"]

@@ -148,9 +148,13 @@ void check_head(const AttnParams& p, const Task& t, int D, long long total_rows)
 
 // The bf16 forward (attn_bf16_kernel) and its dense form: every workgroup of
 // the grid of one launch planned in p; each task it runs is marked in seen.
+// groups = 2: the key-split configuration (the last round's 64-row items):
+// two groups of waves on the same rows, group g taking chunks g, g + 2, ...
+// at steps 0, 1, ..., each with its own double-buffered K and V, all of it
+// (with the raster table) within the 160 KB of LDS a workgroup can hold.
 template <int ROWS>
 void model_bf16_launch(const sta::AttnProblem& pr, const AttnParams& p, long long grid,
-                       std::vector<char>& seen) {
+                       std::vector<char>& seen, int groups = 1) {
   const int D = pr.head_dim;
   const long long total_rows = (long long)pr.B * pr.heads * p.S;
   const bool full = [&] {
@@ -182,8 +186,23 @@ void model_bf16_launch(const sta::AttnProblem& pr, const AttnParams& p, long lon
       CHECK(w.n_chunks <= p.cand_chunks, "candidate table covers the walk");
       CHECK(p.cand_stride >= total_rows, "each candidate's rows have a slot of their own");
     }
-    for (int it = 0; it < w.n_chunks; ++it)
-      model_chunk(p, w, it, pr.raster && !pr.dense, plane, p.pad, p.S, k_row_bytes, table_len, "key");
+    const int steps = (w.n_chunks + groups - 1) / groups;
+    int loaded = 0;
+    for (int st = 0; st < steps; ++st)
+      for (int grp = 0; grp < groups; ++grp) {
+        const int it = st * groups + grp;
+        if (it >= w.n_chunks) continue;   // the group only keeps the step's barriers
+        model_chunk(p, w, it, pr.raster && !pr.dense, plane, p.pad, p.S, k_row_bytes, table_len, "key");
+        ++loaded;
+      }
+    CHECK(loaded == w.n_chunks, "every chunk of the walk runs exactly once");
+  }
+  if (groups > 1) {
+    const long long v_bytes = pr.lse_only ? 16 : 64LL * 2 * D;
+    const long long stat = 2LL * groups * (64LL * k_row_bytes + v_bytes);
+    const bool table = pr.raster && !pr.dense && !plane;
+    CHECK(stat + (table ? 4LL * table_len : 0) <= 163840, "key-split LDS within 160 KB");
+    CHECK(pr.lse_only || 4LL * (ROWS / 16) * (D / 4) * 64 <= groups * 64LL * 2 * D, "merge output fits the V buffers");
   }
   ++g_ctx.launches;
 }
@@ -210,7 +229,7 @@ void model_bf16_forward(const sta::AttnProblem& pr) {
   }
   ++g_ctx.tail_launches;
   std::vector<char> tseen(tp.n_tasks, 0);
-  model_bf16_launch<sta::kFwdTailRows>(pr, tp, (long long)tp.per_xcd * sta::kXcds, tseen);
+  model_bf16_launch<sta::kFwdTailRows>(pr, tp, (long long)tp.per_xcd * sta::kXcds, tseen, 2);
   for (int i = 0; i < p.n_tasks; ++i) {
     int parts = 0;
     for (int b = 0; b < tp.tail_split; ++b) parts += tseen[(size_t)i * tp.tail_split + b];
@@ -536,6 +555,9 @@ int main() {
       {"padded_tile384", 2, 2, 128, 10, 20, 30, {6, 8, 8}, {6, 16, 16, 12, 24, 24}, STA_BF16},
       {"padded_tile192_items", 2, 2, 128, 11, 9, 13, {4, 4, 12}, {8, 8, 12, 12, 12, 24}, STA_BF16},
       {"padded_tile384_items", 2, 1, 128, 13, 17, 19, {6, 8, 8}, {18, 24, 24}, STA_BF16},
+      // the tile grid of the 30x48x80 workloads, padded (a one-plane last
+      // t-tile), at 24 heads: the last round runs as key-split 64-row items
+      {"padded_25x47x79_w6x24x24", 1, 24, 128, 25, 47, 79, {6, 8, 8}, same(24, 6, 24, 24), STA_BF16},
       {"ragged_tile48", 2, 2, 128, 9, 8, 12, {3, 4, 4}, {3, 4, 4, 6, 4, 8}, STA_BF16},
       {"image_2d_tile8x8", 1, 2, 128, 1, 32, 48, {1, 8, 8}, {1, 24, 24, 1, 32, 48}, STA_BF16},
       {"even_windows", 1, 2, 64, 8, 16, 16, {2, 4, 4}, {4, 8, 8, 8, 8, 4}, STA_BF16},

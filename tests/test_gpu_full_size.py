@@ -5,7 +5,9 @@ every row of one whole head of the (18,24,24) workload and of the mixed
 workload's heaviest head that is not the whole volume, and the last four
 tiles of every head (a process pool of the oracle over the host's cores);
 whole-volume STA is also compared element by element with the dense kernel,
-and the raster-order kernel with the reorder + tile-major path."""
+and the raster-order kernel with the reorder + tile-major path; and a padded
+grid of the same tile grid, whose last round runs with every odd key chunk
+padding only."""
 
 import time
 
@@ -132,6 +134,39 @@ def test_full_size_last_tiles_of_every_head():
         assert_close(got[0, h, rows], ref[(0, h)][rows], w.dtype, f"{w.name} head {h} last tiles")
 
 
+@pytest.mark.timeout(300)   # input draws, then 96 query tiles of the oracle on the host
+def test_padded_full_size_last_tiles_of_every_head():
+    """A padded grid at full size: 25x47x79 with (6,8,8) tiles is the 5x6x10
+    tile grid of the named workloads, its last t-tile holding one plane of
+    tokens. At 24 heads the last round again runs as 64-row items whose two
+    wave groups take the even and the odd key chunks; with window (6,24,24)
+    the last tiles' windows lie in that one-plane t-tile, so every odd chunk
+    (and the odd group's first) holds padding only. Every row of the last four
+    tiles of every head against the oracle, and the raster kernel against the
+    reorder + tile-major path bit for bit."""
+    w = workloads.small_case((25, 47, 79), (6, 8, 8), [(6, 24, 24)] * 24, seed=11,
+                             name="padded_25x47x79_w6x24x24")
+    print(f"[case] full size {w.name}: last four tiles of every head", flush=True)
+    inp = workloads.make_inputs(w)
+    q, k, v = (to_gpu(x, w.dtype) for x in (inp.q, inp.k, inp.v))
+    out = binding.sliding_tile_attention(q, k, v, w.tile, inp.windows, fused=True)
+    alt = binding.sliding_tile_attention(q, k, v, w.tile, inp.windows, fused=False)
+    torch.cuda.synchronize()
+    assert torch.equal(out, alt)
+    got = out.float().cpu().numpy().reshape(w.B, w.heads, -1, w.head_dim)
+    assert np.isfinite(got).all()
+    n = oracle.tile_grid(w.volume, w.tile)
+    n_tiles = n[0] * n[1] * n[2]
+    last = list(range(n_tiles - 4, n_tiles))
+    jobs = pool.tile_jobs(w.volume, w.tile, [(0, h) for h in range(w.heads)], tiles=last)
+    ref, wall, workers = pool.sta_attention_pool(inp.q, inp.k, inp.v, w.tile, inp.windows,
+                                                 default_scale(w.head_dim), jobs)
+    print(f"[oracle] {len(jobs)} tiles: {wall:.1f} s on {workers} workers", flush=True)
+    rows = np.concatenate([oracle.tile_tokens(w.volume, w.tile, t) for t in last])
+    for h in range(w.heads):
+        assert_close(got[0, h, rows], ref[(0, h)][rows], w.dtype, f"{w.name} head {h} last tiles")
+
+
 @pytest.mark.parametrize("w", [workloads.STA_18_24_24, workloads.MIXED_HEADS], ids=lambda w: w.name)
 def test_full_size_raster_equals_three_call_path(w):
     print(f"[case] full size {w.name}: raster kernel vs reorder path", flush=True)
@@ -170,10 +205,16 @@ def test_more_than_2_31_elements_per_tensor():
         ref = oracle.sta_attention_rows(qh, kh, vh, tile, win, scale, 0, 0, rows)
         got = out[b, h].float().cpu().numpy().reshape(-1, d)[rows]
         assert_close(got, ref, "bf16", f"large b={b} h={h}")
-    # the tile-major path on the last (batch, head) alone gives the same rows
+    # the tile-major path on the last (batch, head) alone gives the same rows,
+    # up to rounding: that one-slice problem runs its partly filled last round
+    # with each item's key chunks split over two wave groups (a different
+    # summation order), which the 57 600 items here, filling every round, do not
     last = [x[B - 1:B, heads - 1:heads].contiguous() for x in (q, k, v)]
     ref_last = binding.sliding_tile_attention(*last, tile, [win], fused=False)
     torch.cuda.synchronize()
-    assert torch.equal(ref_last[0, 0], out[B - 1, heads - 1])
+    a = ref_last[0, 0].float().cpu().numpy().reshape(-1, d)
+    b = out[B - 1, heads - 1].float().cpu().numpy().reshape(-1, d)
+    assert_close(a, b.astype(np.float64), "bf16", "large: last slice alone vs in the batch")
+    assert (a == b).mean() > 0.5
     del q, k, v, out
     torch.cuda.empty_cache()
