@@ -62,7 +62,7 @@ extern "C" {
 typedef enum {
   STA_OK = 0,
   STA_ERR_INVALID_ARG = -1, /* NULL pointer, bad size, tile/window mismatch, overlap */
-  STA_ERR_UNSUPPORTED = -2, /* a valid request this build has no kernel for */
+  STA_ERR_UNSUPPORTED = -2, /* a valid request that no compiled kernel serves */
   STA_ERR_HIP = -3          /* the HIP runtime reported an error at launch */
 } sta_status;
 
