@@ -23,8 +23,9 @@
 // transposed (ds_read_b64_tr_b16); every lane then holds values of one own
 // row, and the recomputed P and dS are rounded to bf16 as MFMA operands.
 //
-// f32 kernels (float32 problems): one wavefront per own row, the head
-// dimension split over the lanes, dot products reduced across the wave.
+// f32 kernels (float32 problems): 32 own rows an item, two lanes a row, the
+// walk's 32-row chunks dealt to the waves of the workgroup, whose partial
+// gradients add up through LDS at the end.
 #include <hip/hip_runtime.h>
 
 #include "sta_attn_common.h"
@@ -652,117 +653,251 @@ bwd_dkdv_pair_kernel(const AttnParams p, const BwdParams b) {
 }
 
 // ---------------------------------------------------------------------------
-// f32 kernels: one wavefront per own row
+// f32 kernels: 32 own rows an item, two lanes a row, the walk split over waves
 // ---------------------------------------------------------------------------
+// As the float32 forward: lane l keeps dimensions D/2 * (l / 32) .. of own
+// row l % 32 (a dot product is the sum of the two halves, exchanged by a
+// permlane swap); the walk's 32-row chunks are dealt to the KS waves of the
+// workgroup in turn (wave w takes chunks w, w + KS, ...), each staged in the
+// wave's own LDS buffers with no workgroup barrier; no softmax state is
+// carried (P comes from lse), so the waves' partial gradients simply add up
+// through LDS at the end, in a fixed order.
 
-__device__ __forceinline__ float wave_sum(float x) {
+// Rows of chunk c of the walk (32 rows of run c / cpr) into this wave's two
+// buffers: a and b rows (K and V, or Q and dO) as float4, zero past the run.
+template <int D, bool RASTER>
+__device__ __forceinline__ void f32_stage_chunk(const AttnParams& p, const KvRuns& kv, int run, int c0,
+                                                int nvalid, const float4* ga, const float4* gb,
+                                                float4* la, float4* lb, int lane) {
+  constexpr int D4 = D / 4;
+  constexpr int kPer = kF32BN * D4 / 64;   // float4 of each operand per lane
+  constexpr int kGroup = D <= 64 ? (kPer < 8 ? kPer : 8) : 4;
+  const int row0 = RASTER ? kv.run_start_raster(run, p.H, p.W, p.ct, p.ch, p.cw) : kv.run_start(run);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-  return x;
+  for (int r0 = 0; r0 < kPer; r0 += kGroup) {
+    float4 xa[kGroup], xb[kGroup];
+#pragma unroll
+    for (int r = 0; r < kGroup; ++r) {
+      const int i = lane + 64 * (r0 + r);
+      const int key = i / D4;
+      xa[r] = xb[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (key < nvalid) {
+        const int tok = row0 + (RASTER ? run_offset_raster(p, c0 + key) : c0 + key);
+        const long long off = (long long)tok * D4 + (i - key * D4);
+        xa[r] = ga[off];
+        xb[r] = gb[off];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kGroup; ++r) {
+      la[lane + 64 * (r0 + r)] = xa[r];
+      lb[lane + 64 * (r0 + r)] = xb[r];
+    }
+  }
 }
 
-// Own-row token of wave `wave` in the work item (or -1 when it has none).
+// Token of chunk row `key` (< nvalid) of run `run` of the walk.
 template <bool RASTER>
-__device__ __forceinline__ int own_token(const AttnParams& p, const Task& t, int wave) {
-  if (wave >= t.valid_rows) return -1;
-  return RASTER ? tile_row_raster(p, t.qt, t.qh, t.qw, t.local0 + wave) : t.row0 + wave;
-}
-
-// Token of key (or query) `e` of run `run` of the walk.
-template <bool RASTER>
-__device__ __forceinline__ int walk_token(const AttnParams& p, const KvRuns& kv, int run, int e) {
+__device__ __forceinline__ int f32_walk_token(const AttnParams& p, const KvRuns& kv, int run, int e) {
   return RASTER ? kv.run_start_raster(run, p.H, p.W, p.ct, p.ch, p.cw) + run_offset_raster(p, e)
                 : kv.run_start(run) + e;
 }
 
+// Half-row dot product: this lane's DH dimensions against row j of a staged
+// chunk (its half), summed with the partner lane's half.
+template <int D>
+__device__ __forceinline__ float f32_row_dot(const float (&x)[D / 2], const float4* rows, int j) {
+  constexpr int D4 = D / 4;
+  float acc = 0.f;
+#pragma unroll
+  for (int d4 = 0; d4 < D4 / 2; ++d4) {
+    const float4 y = rows[j * D4 + d4];
+    acc = fmaf(x[4 * d4], y.x, acc);
+    acc = fmaf(x[4 * d4 + 1], y.y, acc);
+    acc = fmaf(x[4 * d4 + 2], y.z, acc);
+    acc = fmaf(x[4 * d4 + 3], y.w, acc);
+  }
+  return pair32(acc, false);
+}
+
+template <int D>
+__device__ __forceinline__ void f32_row_axpy(float (&acc)[D / 2], float a, const float4* rows, int j) {
+  constexpr int D4 = D / 4;
+#pragma unroll
+  for (int d4 = 0; d4 < D4 / 2; ++d4) {
+    const float4 y = rows[j * D4 + d4];
+    acc[4 * d4] = fmaf(a, y.x, acc[4 * d4]);
+    acc[4 * d4 + 1] = fmaf(a, y.y, acc[4 * d4 + 1]);
+    acc[4 * d4 + 2] = fmaf(a, y.z, acc[4 * d4 + 2]);
+    acc[4 * d4 + 3] = fmaf(a, y.w, acc[4 * d4 + 3]);
+  }
+}
+
+// Own-row token of lane row `row` (row 0 of the item when the row does not
+// exist: read, never written).
+template <bool RASTER>
+__device__ __forceinline__ int f32_own_token(const AttnParams& p, const Task& t, int row) {
+  const int r = row < t.valid_rows ? row : 0;
+  return RASTER ? tile_row_raster(p, t.qt, t.qh, t.qw, t.local0 + r) : t.row0 + r;
+}
+
+// dQ: own rows are queries, the walk is the window's keys.
 template <int D, bool RASTER>
-__global__ void __launch_bounds__(kF32Waves * 64) bwd_f32_dq_kernel(const AttnParams p, const BwdParams b) {
-  constexpr int E = D / 64;
+__global__ void __launch_bounds__(f32_key_splits(D) * 64) bwd_f32_dq_kernel(const AttnParams p, const BwdParams b) {
+  constexpr int KS = f32_key_splits(D);
+  constexpr int D4 = D / 4;
+  constexpr int DH = D / 2;
+  constexpr int R = kF32Rows;
+  constexpr int kStage = KS * 2 * kF32BN * D4;
+  constexpr int kMerge = KS * D * R / 4;
+  __shared__ float4 lds[kStage > kMerge ? kStage : kMerge];
   const int task = logical_task(p);
   if (task >= p.n_tasks) return;
-  const Task t = decode_task<kF32Waves>(p, task, D);
-  const int lane = threadIdx.x & 63;
-  const int tok = own_token<RASTER>(p, t, threadIdx.x >> 6);
-  if (tok < 0) return;
+  const Task t = decode_task<R>(p, task, D);
   const long long rowbase = t.head_base / D;
   const float* qg = static_cast<const float*>(p.q) + t.head_base;
-  const float* kg = static_cast<const float*>(p.k) + t.head_base;
-  const float* vg = static_cast<const float*>(p.v) + t.head_base;
+  const float4* kg = reinterpret_cast<const float4*>(static_cast<const float*>(p.k) + t.head_base);
+  const float4* vg = reinterpret_cast<const float4*>(static_cast<const float*>(p.v) + t.head_base);
   const float* dog = static_cast<const float*>(b.dout) + t.head_base;
-  float q[E], d_o[E], acc[E];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane & (R - 1);
+  const int half = lane / R;
+  const int tok = f32_own_token<RASTER>(p, t, row);
+  float q[DH], d_o[DH], acc[DH];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    q[e] = qg[(long long)tok * D + lane + 64 * e];
-    d_o[e] = dog[(long long)tok * D + lane + 64 * e];
-    acc[e] = 0.f;
+  for (int d = 0; d < DH; ++d) {
+    q[d] = qg[(long long)tok * D + half * DH + d];
+    d_o[d] = dog[(long long)tok * D + half * DH + d];
+    acc[d] = 0.f;
   }
   const float lse2 = b.lse[rowbase + tok] * kLog2e;
   const float dl = b.delta[rowbase + tok];
-  for (int run = 0; run < t.kv.runs; ++run)
-    for (int e = 0; e < t.kv.run_len; ++e) {
-      const long long kr = (long long)walk_token<RASTER>(p, t.kv, run, e) * D;
-      float sq = 0.f, sp = 0.f;
-#pragma unroll
-      for (int x = 0; x < E; ++x) {
-        sq = fmaf(q[x], kg[kr + lane + 64 * x], sq);
-        sp = fmaf(d_o[x], vg[kr + lane + 64 * x], sp);
-      }
-      const float pr = __builtin_amdgcn_exp2f(fmaf(wave_sum(sq), p.scale_log2, -lse2));
-      const float ds = pr * (wave_sum(sp) - dl);
-#pragma unroll
-      for (int x = 0; x < E; ++x) acc[x] = fmaf(ds, kg[kr + lane + 64 * x], acc[x]);
+  float4* ks = lds + wave * (2 * kF32BN * D4);
+  float4* vs = ks + kF32BN * D4;
+  const int cpr = (t.kv.run_len + kF32BN - 1) / kF32BN;
+  const int n_chunks = t.kv.runs * cpr;
+  for (int c = wave; c < n_chunks; c += KS) {
+    const int run = c / cpr;
+    const int c0 = (c - run * cpr) * kF32BN;
+    const int nvalid = min(kF32BN, t.kv.run_len - c0);
+    f32_stage_chunk<D, RASTER>(p, t.kv, run, c0, nvalid, kg, vg, ks, vs, lane);
+    const float4* kh = ks + half * (D4 / 2);
+    const float4* vh = vs + half * (D4 / 2);
+#pragma unroll 1
+    for (int j = 0; j < kF32BN; ++j) {
+      const float sq = f32_row_dot<D>(q, kh, j);
+      const float sp = f32_row_dot<D>(d_o, vh, j);
+      const float pr = j < nvalid ? __builtin_amdgcn_exp2f(fmaf(sq, p.scale_log2, -lse2)) : 0.f;
+      f32_row_axpy<D>(acc, pr * (sp - dl), kh, j);
     }
-  float* dqg = static_cast<float*>(b.dq) + t.head_base;
+  }
+  __syncthreads();   // every wave is done with its chunk buffers
+  float* ob = reinterpret_cast<float*>(lds);   // [KS][D][R]
 #pragma unroll
-  for (int e = 0; e < E; ++e) dqg[(long long)tok * D + lane + 64 * e] = acc[e] * b.scale;
+  for (int d = 0; d < DH; ++d) ob[(wave * D + half * DH + d) * R + row] = acc[d];
+  __syncthreads();
+  if (row < t.valid_rows) {
+    float* dst = static_cast<float*>(b.dq) + t.head_base + (long long)tok * D;
+    constexpr int kDims = D / KS / 2;
+#pragma unroll
+    for (int dd = 0; dd < kDims; ++dd) {
+      const int d = (2 * wave + half) * kDims + dd;
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < KS; ++w) x += ob[(w * D + d) * R + row];
+      dst[d] = x * b.scale;
+    }
+  }
 }
 
+// dK, dV: own rows are keys, the walk is the query rows of the query tiles
+// whose window holds the key tile.
 template <int D, bool RASTER>
-__global__ void __launch_bounds__(kF32Waves * 64) bwd_f32_dkdv_kernel(const AttnParams p, const BwdParams b) {
-  constexpr int E = D / 64;
+__global__ void __launch_bounds__(f32_key_splits(D) * 64) bwd_f32_dkdv_kernel(const AttnParams p, const BwdParams b) {
+  constexpr int KS = f32_key_splits(D);
+  constexpr int D4 = D / 4;
+  constexpr int DH = D / 2;
+  constexpr int R = kF32Rows;
+  constexpr int kStage = KS * 2 * kF32BN * D4;
+  constexpr int kMerge = KS * 2 * D * R / 4;   // dK and dV
+  __shared__ float4 lds[kStage > kMerge ? kStage : kMerge];
+  __shared__ float lsb[KS][kF32BN];   // the chunk's lse (base 2) and D
+  __shared__ float dsb[KS][kF32BN];
   const int task = logical_task(p);
   if (task >= p.n_tasks) return;
-  const Task t = decode_task<kF32Waves, true>(p, task, D);
-  const int lane = threadIdx.x & 63;
-  const int tok = own_token<RASTER>(p, t, threadIdx.x >> 6);
-  if (tok < 0) return;
+  const Task t = decode_task<R, true>(p, task, D);
   const long long rowbase = t.head_base / D;
-  const float* qg = static_cast<const float*>(p.q) + t.head_base;
+  const float4* qg = reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + t.head_base);
   const float* kg = static_cast<const float*>(p.k) + t.head_base;
   const float* vg = static_cast<const float*>(p.v) + t.head_base;
-  const float* dog = static_cast<const float*>(b.dout) + t.head_base;
-  float k[E], v[E], dk[E], dv[E];
+  const float4* dog = reinterpret_cast<const float4*>(static_cast<const float*>(b.dout) + t.head_base);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane & (R - 1);
+  const int half = lane / R;
+  const int tok = f32_own_token<RASTER>(p, t, row);
+  float k[DH], v[DH], dk[DH], dv[DH];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    k[e] = kg[(long long)tok * D + lane + 64 * e];
-    v[e] = vg[(long long)tok * D + lane + 64 * e];
-    dk[e] = dv[e] = 0.f;
+  for (int d = 0; d < DH; ++d) {
+    k[d] = kg[(long long)tok * D + half * DH + d];
+    v[d] = vg[(long long)tok * D + half * DH + d];
+    dk[d] = dv[d] = 0.f;
   }
-  for (int run = 0; run < t.kv.runs; ++run)
-    for (int e = 0; e < t.kv.run_len; ++e) {
-      const int qtok = walk_token<RASTER>(p, t.kv, run, e);
-      const long long qr = (long long)qtok * D;
-      float sq = 0.f, sp = 0.f;
-#pragma unroll
-      for (int x = 0; x < E; ++x) {
-        sq = fmaf(qg[qr + lane + 64 * x], k[x], sq);
-        sp = fmaf(dog[qr + lane + 64 * x], v[x], sp);
+  float4* qs = lds + wave * (2 * kF32BN * D4);
+  float4* os = qs + kF32BN * D4;
+  const int cpr = (t.kv.run_len + kF32BN - 1) / kF32BN;
+  const int n_chunks = t.kv.runs * cpr;
+  for (int c = wave; c < n_chunks; c += KS) {
+    const int run = c / cpr;
+    const int c0 = (c - run * cpr) * kF32BN;
+    const int nvalid = min(kF32BN, t.kv.run_len - c0);
+    f32_stage_chunk<D, RASTER>(p, t.kv, run, c0, nvalid, qg, dog, qs, os, lane);
+    if (lane < kF32BN) {
+      float l2 = 0.f, dd = 0.f;
+      if (lane < nvalid) {
+        const int qt = f32_walk_token<RASTER>(p, t.kv, run, c0 + lane);
+        l2 = b.lse[rowbase + qt] * kLog2e;
+        dd = b.delta[rowbase + qt];
       }
-      const float pr = __builtin_amdgcn_exp2f(
-          fmaf(wave_sum(sq), p.scale_log2, -b.lse[rowbase + qtok] * kLog2e));
-      const float ds = pr * (wave_sum(sp) - b.delta[rowbase + qtok]);
-#pragma unroll
-      for (int x = 0; x < E; ++x) {
-        dk[x] = fmaf(ds, qg[qr + lane + 64 * x], dk[x]);
-        dv[x] = fmaf(pr, dog[qr + lane + 64 * x], dv[x]);
-      }
+      lsb[wave][lane] = l2;
+      dsb[wave][lane] = dd;
     }
-  float* dkg = static_cast<float*>(b.dk) + t.head_base;
-  float* dvg = static_cast<float*>(b.dv) + t.head_base;
+    const float4* qh = qs + half * (D4 / 2);
+    const float4* oh = os + half * (D4 / 2);
+#pragma unroll 1
+    for (int j = 0; j < kF32BN; ++j) {
+      const float sq = f32_row_dot<D>(k, qh, j);
+      const float sp = f32_row_dot<D>(v, oh, j);
+      const float pr = j < nvalid ? __builtin_amdgcn_exp2f(fmaf(sq, p.scale_log2, -lsb[wave][j])) : 0.f;
+      f32_row_axpy<D>(dv, pr, oh, j);
+      f32_row_axpy<D>(dk, pr * (sp - dsb[wave][j]), qh, j);
+    }
+  }
+  __syncthreads();   // every wave is done with its chunk buffers
+  float* ob = reinterpret_cast<float*>(lds);   // [KS][2][D][R]: dK, then dV
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    dkg[(long long)tok * D + lane + 64 * e] = dk[e] * b.scale;
-    dvg[(long long)tok * D + lane + 64 * e] = dv[e];
+  for (int d = 0; d < DH; ++d) {
+    ob[((wave * 2 + 0) * D + half * DH + d) * R + row] = dk[d];
+    ob[((wave * 2 + 1) * D + half * DH + d) * R + row] = dv[d];
+  }
+  __syncthreads();
+  if (row < t.valid_rows) {
+    float* dkd = static_cast<float*>(b.dk) + t.head_base + (long long)tok * D;
+    float* dvd = static_cast<float*>(b.dv) + t.head_base + (long long)tok * D;
+    constexpr int kDims = D / KS / 2;
+#pragma unroll
+    for (int dd = 0; dd < kDims; ++dd) {
+      const int d = (2 * wave + half) * kDims + dd;
+      float xk = 0.f, xv = 0.f;
+#pragma unroll
+      for (int w = 0; w < KS; ++w) {
+        xk += ob[((w * 2 + 0) * D + d) * R + row];
+        xv += ob[((w * 2 + 1) * D + d) * R + row];
+      }
+      dkd[d] = xk * b.scale;
+      dvd[d] = xv;
+    }
   }
 }
 
@@ -880,14 +1015,15 @@ template <int D>
 int launch_f32_bwd(const BwdProblem& pr, hipStream_t stream) {
   AttnParams p;
   BwdParams b;
-  fill_bwd_params(pr, kF32Waves, &p, &b);
+  fill_bwd_params(pr, kF32Rows, &p, &b);
   const unsigned grid = (unsigned)p.per_xcd * kXcds;
+  constexpr int kThreads = f32_key_splits(D) * 64;
   if (pr.attn.raster) {
-    hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D, true>), dim3(grid), dim3(kF32Waves * 64), 0, stream, p, b);
-    hipLaunchKernelGGL((bwd_f32_dq_kernel<D, true>), dim3(grid), dim3(kF32Waves * 64), 0, stream, p, b);
+    hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p, b);
+    hipLaunchKernelGGL((bwd_f32_dq_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p, b);
   } else {
-    hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D, false>), dim3(grid), dim3(kF32Waves * 64), 0, stream, p, b);
-    hipLaunchKernelGGL((bwd_f32_dq_kernel<D, false>), dim3(grid), dim3(kF32Waves * 64), 0, stream, p, b);
+    hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p, b);
+    hipLaunchKernelGGL((bwd_f32_dq_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p, b);
   }
   return (int)hipGetLastError();
 }

@@ -473,7 +473,6 @@ inline int fwd_bf16_rows(int unit_rows) {
 constexpr int kF32Rows = 32;
 constexpr int kF32BN = 32;         // keys per chunk
 STA_HD constexpr int f32_key_splits(int D) { return D <= 64 ? 8 : 4; }
-constexpr int kF32Waves = 4;       // float32 backward: one wave per own row
 // bf16 backward, key side: 4 pairs of waves sharing 48 key rows when such
 // items tile tau, else pairs sharing 32 key rows (tiles of at least 128
 // tokens), else 4 waves of 16; query side: 4 waves of 32 query rows, else of

@@ -301,6 +301,67 @@ void model_f32_forward(const sta::AttnProblem& pr) {
   ++g_ctx.launches;
 }
 
+// The float32 backward (bwd_f32_dkdv_kernel, bwd_f32_dq_kernel): 32 own
+// rows an item, lane l of every wave on row l % 32; wave w stages chunks w,
+// w + KS, ... of 32 streamed rows (and, on the key side, their lse and D);
+// the merge reuses the staging array as [KS][D][32] (query side) or
+// [KS][2][D][32] (key side) floats.
+template <int D>
+void model_f32_backward(const sta::BwdProblem& pb) {
+  const sta::AttnProblem& a = pb.attn;
+  constexpr int KS = sta::f32_key_splits(D);
+  constexpr int D4 = D / 4;
+  constexpr int R = sta::kF32Rows;
+  constexpr int kStage = KS * 2 * sta::kF32BN * D4;
+  const long long total_rows = (long long)a.B * a.heads * (a.raster ? a.g.S : a.g.S_pad);
+  for (int side = 0; side < 2; ++side) {
+    const bool keys = side == 0;
+    const int kMerge = KS * (keys ? 2 : 1) * D * R / 4;
+    const int kLds = kStage > kMerge ? kStage : kMerge;
+    AttnParams p;
+    sta::BwdParams b;
+    sta::fill_bwd_params(pb, R, &p, &b);
+    const long long grid = (long long)p.per_xcd * sta::kXcds;
+    for (long long bid = 0; bid < grid; ++bid) {
+      const int task = sta::task_of_block(p, (int)bid);
+      if (task >= p.n_tasks) continue;
+      const Task t = keys ? sta::decode_task<R, true>(p, task, D) : sta::decode_task<R>(p, task, D);
+      check_head(p, t, D, total_rows);
+      for (int lane = 0; lane < 64; ++lane) {
+        const int row = lane % R, half = lane / R;
+        const int r = row < t.valid_rows ? row : 0;
+        const long long tok = a.raster ? sta::tile_row_raster(p, t.qt, t.qh, t.qw, t.local0 + r)
+                                       : (long long)t.row0 + r;
+        CHECK_ROW(tok, p.S, keys ? "f32 own key" : "f32 own query");
+        for (int w = 0; w < KS; ++w)
+          for (int m = 0; m < (keys ? 2 : 1); ++m)
+            for (int d = 0; d < D / 2; ++d)
+              CHECK(((w * (keys ? 2 : 1) + m) * D + half * (D / 2) + d) * R + row < 4 * kLds, "f32 backward merge index");
+        for (int dd = 0; dd < D / KS / 2; ++dd) CHECK((2 * (KS - 1) + half) * (D / KS / 2) + dd < D, "f32 stored dimension");
+      }
+      const int cpr = (t.kv.run_len + sta::kF32BN - 1) / sta::kF32BN;
+      const int n_chunks = t.kv.runs * cpr;
+      for (int wave = 0; wave < KS; ++wave)
+        for (int c = wave; c < n_chunks; c += KS) {
+          const int run = c / cpr;
+          const int c0 = (c - run * cpr) * sta::kF32BN;
+          CHECK(c0 < t.kv.run_len, "f32 chunk inside its run");
+          const int nvalid = sta::imin(sta::kF32BN, t.kv.run_len - c0);
+          const long long row0 = a.raster ? t.kv.run_start_raster(run, p.H, p.W, p.ct, p.ch, p.cw)
+                                          : t.kv.run_start(run);
+          for (int i = 0; i < sta::kF32BN * D4; ++i) {
+            CHECK(wave * (2 * sta::kF32BN * D4) + sta::kF32BN * D4 + i < kLds, "f32 backward staging index");
+            const int key = i / D4;
+            if (key < nvalid)
+              CHECK_ROW(row0 + (a.raster ? sta::run_offset_raster(p, c0 + key) : c0 + key), p.S,
+                        keys ? "f32 streamed query (q, dO, lse, D)" : "f32 streamed key (k, v)");
+          }
+        }
+    }
+    ++g_ctx.launches;
+  }
+}
+
 // The backward's two passes: key side (own key rows, walking the query tiles
 // whose window holds the key tile) and query side (own query rows, walking the
 // window), with their work-item shapes.
@@ -406,7 +467,7 @@ int launch_backward(const BwdProblem& pb, void*) {
   CHECK(pb.delta != nullptr, "the D workspace is set");
   if (a.dtype == STA_F32) {
     CHECK(!a.g.padded, "float32 backward never reaches a padded grid");
-    ++g_ctx.launches;
+    if (a.head_dim == 64) model_f32_backward<64>(pb); else model_f32_backward<128>(pb);
     return 0;
   }
   const int kr = bwd_key_rows(a.g.tau), qr = bwd_query_rows(a.g.tau);
