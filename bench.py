@@ -23,7 +23,8 @@ Printed as one JSON line. Besides the contract fields it carries
   fp8_qk        sta_forward_fp8 (e4m3 q and k, bf16 v) at the same shape, against
                 the mixed peak of its two products (QK^T at the fp8 MFMA peak,
                 PV at the bf16 one);
-  other_workloads  the fused kernel on the other named workloads.
+  other_workloads  the fused kernel on the other named workloads (and, on the
+                small float32 one, sta_backward).
 """
 
 from __future__ import annotations
@@ -257,7 +258,22 @@ def other_workloads(main_w, args, torch, binding, workloads, q, k, v, out, strea
                        "algorithmic_tflop": flops / 1e12,
                        "windows": sorted({tuple(x) for x in windows.tolist()})}
         if not same:
-            del a, b, c, o
+            # the small workloads also time their backward (five-product count)
+            dout = torch.randn(a.shape, device="cuda", dtype=torch.float32).to(a.dtype)
+            o, lse = binding.sta_forward_lse(a, b, c, w.tile, windows)
+            delta = torch.empty_like(lse)
+            binding.sta_backward(a, b, c, o, dout, lse, w.tile, windows, delta=delta)  # warm-up
+            torch.cuda.synchronize()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            for _ in range(args.config_reps):
+                binding.sta_backward(a, b, c, o, dout, lse, w.tile, windows, delta=delta)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            bms = e0.elapsed_time(e1) / args.config_reps
+            res[w.name].update({"backward_ms": bms,
+                                "backward_frac_of_peak": 2.5 * flops / (bms * 1e-3) / 1e12 / peak})
+            del a, b, c, o, dout, lse, delta
     return res
 
 
