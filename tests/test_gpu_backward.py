@@ -176,6 +176,7 @@ def sample_tokens(volume, tile, rng, tiles):
     return np.concatenate(out)
 
 
+@pytest.mark.timeout(400)   # input draws, the backward, then the oracle's rows on the host
 @pytest.mark.parametrize("wl", [workloads.STA_18_24_24, workloads.MIXED_HEADS], ids=lambda w: w.name)
 def test_backward_full_size_sampled_rows(wl):
     """At 30x48x80 (24 heads, d=128, bf16), in the raster launch configuration:
@@ -207,6 +208,15 @@ def test_backward_full_size_sampled_rows(wl):
         rows = sample_tokens(wl.volume, wl.tile, rng, [0, n_tiles - 1, interior, edge])
         gq = oracle.sta_backward_query_rows(inp.q, inp.k, inp.v, dout, wl.tile, window, scale, 0, h, rows)
         assert_grad_close(dq[0, h, rows], gq, "bf16", f"{wl.name} head {h} {window} dq")
+    if wl is workloads.STA_18_24_24:
+        # every row of the last four query tiles of every head (the query
+        # side's work items of each XCD's last, partly filled round)
+        rows = np.concatenate([oracle.tile_tokens(wl.volume, wl.tile, t) for t in range(n_tiles - 4, n_tiles)])
+        print(f"[case] backward full size {wl.name}: dq of the last four tiles of every head", flush=True)
+        for h in range(wl.heads):
+            window = tuple(int(x) for x in inp.windows[h])
+            gq = oracle.sta_backward_query_rows(inp.q, inp.k, inp.v, dout, wl.tile, window, scale, 0, h, rows)
+            assert_grad_close(dq[0, h, rows], gq, "bf16", f"{wl.name} head {h} dq, last tiles")
     for h in sorted(set(key_heads)):
         window = tuple(int(x) for x in inp.windows[h])
         rows = sample_tokens(wl.volume, wl.tile, rng, [0, interior])
